@@ -1,0 +1,41 @@
+"""The seeded input generator: published SplitMix64 outputs, moments of the
+N(0,1) stand-in, and the workload recipes' structure."""
+import numpy as np
+
+import synthetic
+
+
+def test_splitmix64_reference_outputs():
+    # SplitMix64 seeded with 0 (state advanced by the golden gamma before each output):
+    # the first outputs of the published reference generator.
+    got = synthetic.bits(0, np.arange(2))
+    assert [hex(int(v)) for v in got] == ["0xe220a8397b1dcdaf", "0x6e789e6aa1b965f4"]
+
+
+def test_normal_standin_moments():
+    z = synthetic.normal(synthetic.stream_key(0, synthetic.TAG_X), np.arange(1 << 20))
+    assert z.dtype == np.float32
+    assert abs(z.mean()) < 0.005 and abs(z.std() - 1.0) < 0.005
+    assert np.abs(z).max() <= 2 * np.sqrt(3) + 1e-6
+
+
+def test_weight_recipes():
+    W = synthetic.weights(0, synthetic.TAG_W, 0, 64, 256)
+    assert W.shape == (64, 256) and abs(W.std() - 0.02) < 0.001
+    # any subset of rows regenerates identically
+    assert np.array_equal(synthetic.weights(0, synthetic.TAG_W, 0, 64, 256, rows=[5, 63]), W[[5, 63]])
+    Wo = synthetic.weights_with_outliers(0, 256, 4096)
+    frac = (np.abs(Wo) > 0.02 * 2 * np.sqrt(3) + 1e-6).mean()
+    assert 0.0002 < frac < 0.002
+    mu = synthetic.column_means(0, 8192)
+    assert mu.min() >= -0.01 and mu.max() < 0.01 and abs(mu.mean()) < 0.001
+    x = synthetic.activations_with_outlier_channels(0, 4, 8192)
+    ch = synthetic.outlier_channels(0, 8192)
+    assert len(set(ch.tolist())) == 4 and np.abs(x[:, ch]).max() > 10
+
+
+def test_router_recipes():
+    z = synthetic.router_logits_skewed(0, 64, 384)
+    b = synthetic.zipf_bias(384)
+    assert b[0] == 0 and np.all(np.diff(b) < 0)
+    assert z.shape == (64, 384) and z.dtype == np.float32
