@@ -1,0 +1,205 @@
+/*
+ * w4a8.h -- C ABI of the MI355X (gfx950) W4A8 linear-layer library, libw4a8.so.
+ *
+ * The method (page keys as in the design notes):
+ *   [p1] "Kimi 2.7 MoE: from 4-bit storage to INT8 compute" (hotelren.com/news/5173946)
+ *   [p2] "Kimi 2.7 MoE, 4-bit storage to INT8, dissected"   (pptc.cn/news/121597)
+ *   [p3] "LLM quantization primer"                            (hotelren.com/news/5982361)
+ *   [p4] "MoE deployment: active parameters are not the storage bill" (feinterview.poetries.top)
+ *
+ * Weights W[N][K] (row n = output feature n, the nn.Linear out x in layout) are
+ * quantized in groups of 128 consecutive K entries per output feature, each
+ * group with an fp16 scale and an fp16 zero point ([p2 §2.1, §2.2, §2.3]):
+ *     scale = (max - min) / 15, zp = round(-min / scale),
+ *     q = clamp(round(w / scale) + zp, 0, 15),   w ~ (q - zp) * scale,
+ * where [min, max] is the group's range widened to contain 0, rounding is to
+ * nearest-even, and q is computed with the fp16-rounded scale.  Two codes share
+ * a byte, the first (lower k) in the low nibble ([p2 §2.2]).
+ *
+ * Activations x[M][K] are quantized per token to symmetric INT8 at run time
+ * ([p1 §3.1, §5.3]; [p3 §2.1]): s_m = max_k |x[m][k]| / 127,
+ * qa = clamp(rint(x / s_m), -127, 127); a row with s_m == 0 gets codes 0.
+ *
+ * The product is an INT8 x INT8 matmul with int32 accumulation per group,
+ * followed by a floating-point epilogue ([p2 §3.2, §5.4]; [p1 §4.3]):
+ *     isum[g][m][n] = sum_{k in g} qa[m][k] * (q[n][k] - zp[g][n])
+ *     out[m][n]     = s_m * sum_g scale[g][n] * isum[g][m][n]      (fp32)
+ *
+ * Layouts (all row-major, C-contiguous):
+ *     W        fp32  [N][K]
+ *     packed   u8    [N][K/2]      byte (n, j) = q[n][2j] | q[n][2j+1] << 4
+ *     scale    u16   [K/128][N]    fp16 bit patterns
+ *     zp       u16   [K/128][N]    fp16 bit patterns of integers 0..15
+ *     qa       i8    [M][K],  a_scale fp32 [M]
+ *     out      fp32  [M][N]
+ * MoE weights stack E experts: packed [E][N][K/2], scale/zp [E][K/128][N].
+ *
+ * Conventions for every entry point:
+ *   - Return codes only; nothing throws or aborts across the ABI.  Arguments
+ *     are validated on the host before anything is launched; a rejected call
+ *     launches nothing and writes nothing.  w4a8_last_error() then describes
+ *     the problem (thread-local text, valid until the next call on the thread).
+ *   - group must be 128 (W4A8_EUNSUPPORTED otherwise; there is no fallback).
+ *     K must be a multiple of 128 (W4A8_EINVAL; pad K at conversion time).
+ *   - Device pointers (marked "device") must be device memory owned by the
+ *     caller; the library allocates nothing and keeps no pointer after the
+ *     call returns.  Device calls are asynchronous on `stream` (NULL = the
+ *     default stream); a fault inside a kernel surfaces at the caller's next
+ *     synchronisation.  A failed launch returns W4A8_EHIP.
+ *   - Packed weights, qa and out must be 16-byte aligned (W4A8_EINVAL).
+ *   - Results are deterministic: identical inputs give identical output bytes
+ *     (no floating-point atomics anywhere).
+ *   - Non-finite activations give unspecified codes (no error is raised on the
+ *     device); the host packer rejects non-finite weights.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_EINVAL = 1,        /* bad pointer, size, alignment or value */
+    W4A8_EUNSUPPORTED = 2,  /* valid request this library does not implement (e.g. group != 128) */
+    W4A8_EHIP = 3           /* a HIP runtime call or kernel launch failed */
+} w4a8_status;
+
+#define W4A8_ABI_VERSION 1
+#define W4A8_GROUP 128
+
+int w4a8_abi_version(void);
+const char *w4a8_status_str(int status);
+const char *w4a8_last_error(void);
+
+/* ------------------------------------------------------------------ packing */
+
+/* Host, synchronous.  Quantizes W[N][K] (host fp32) into packed codes and fp16
+ * scale/zero point per group, exactly as stated at the top of this file
+ * ([p2 §2.1, §2.2]).  All pointers are host memory owned by the caller.
+ * A group whose scale rounds to 0 in fp16 stores scale 1.0 and zp 0.
+ * Errors: W4A8_EINVAL for null pointers, N <= 0, K <= 0, K % 128 != 0,
+ * non-finite weights, or a group scale above the largest finite fp16. */
+w4a8_status w4a8_pack_weights(const float *W, int64_t N, int64_t K, int32_t group,
+                              uint8_t *packed, uint16_t *scale, uint16_t *zp);
+
+/* Device, asynchronous.  The same quantization as w4a8_pack_weights, run on the
+ * GPU for W (device fp32 [N][K]) -- for weight sets too large to convert on the
+ * host.  Bit-identical to the host packer.  Device memory only.  Errors as the
+ * host packer for sizes; non-finite weights or fp16 scale overflow cannot be
+ * reported from the device: such groups get scale 0x7C00 (inf) and must be
+ * checked by the caller if the input is untrusted. */
+w4a8_status w4a8_pack_weights_device(const float *W, int64_t N, int64_t K, int32_t group,
+                                     uint8_t *packed, uint16_t *scale, uint16_t *zp,
+                                     hipStream_t stream);
+
+/* Host, synchronous.  Inverse view of a packed weight: q_out[N][K] receives the
+ * 4-bit codes (may be NULL) and w_hat[N][K] the dequantized fp32 values
+ * (q - zp) * scale (may be NULL) [p2 §2.1].  Host memory. */
+w4a8_status w4a8_unpack_weights(const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
+                                int64_t N, int64_t K, int32_t group, uint8_t *q_out, float *w_hat);
+
+/* -------------------------------------------------------- activation quant */
+
+/* Device.  Per-token symmetric INT8 quantization of x (rows of length K, row
+ * stride ldx >= K floats) into qa[M][K] and a_scale[M] ([p1 §5.3]: the scale is
+ * computed in the kernel at forward time; [p3 §2.1]: symmetric INT8 form).
+ * Division and rounding are IEEE fp32 (correctly rounded divide, ties-to-even).
+ * Errors: W4A8_EINVAL for null pointers, M < 0, K <= 0, ldx < K, or qa not
+ * 16-byte aligned, or K % 16 != 0.  M == 0 is a no-op. */
+w4a8_status w4a8_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
+                              int8_t *qa, float *a_scale, hipStream_t stream);
+
+/* --------------------------------------------------------------------- GEMM */
+
+/* Device.  out[M][N] = W4A8 linear layer of the quantized activations with the
+ * packed weights (formula at the top; [p2 §3.2]: INT8 matmul with int32
+ * accumulation, then multiply by the scales; [p1 §4.3 step 2]: the 4-bit codes
+ * are widened to INT8 inside the kernel, never in memory).  Small M takes an
+ * HBM-streaming path, large M an LDS-tiled MFMA path; both give the same
+ * per-group int32 sums.  The fp32 epilogue adds groups in increasing g.
+ * Errors: W4A8_EINVAL (null, M < 0, N <= 0, K <= 0, K % 128, N % 16 != 0,
+ * misalignment), W4A8_EUNSUPPORTED (group != 128).  M == 0 is a no-op. */
+w4a8_status w4a8_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
+                      const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
+                      int64_t N, int32_t group, float *out, hipStream_t stream);
+
+/* Device, test/debug aid.  Same main loop as w4a8_gemm, but instead of the fp32
+ * epilogue it stores every per-group int32 sum: isums[K/128][M][N] ([p2 §5.4]).
+ * `path` selects the main loop: 0 = the one w4a8_gemm would pick for M,
+ * 1 = the small-M streaming loop (M <= 64), 2 = the large-M tiled loop. */
+w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K,
+                                  const uint8_t *packed, const uint16_t *zp, int64_t N,
+                                  int32_t group, int32_t path, int32_t *isums, hipStream_t stream);
+
+/* Same as w4a8_gemm with a forced main loop (`path` as above); for tests and
+ * benchmarks that compare the two loops on one shape. */
+w4a8_status w4a8_gemm_path(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
+                           const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
+                           int64_t N, int32_t group, int32_t path, float *out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- MoE */
+
+/* Device.  Router for T tokens over E experts ([p1 §5.2]: the router stays in
+ * high precision and sends each token to its experts; [p4]: toy top-1 model).
+ *   topk_ids[T][k]  the k largest logits per token, descending, ties -> lower id
+ *   topk_w[T][k]    softmax over the k selected logits (fp32)
+ *   expert_offsets[E+1]  exclusive scan of the per-expert pair counts
+ *   perm[T*k]       pair indices p = t*k + j grouped by ascending expert and,
+ *                   within an expert, ascending p ("slot" s holds pair perm[s])
+ *   slot_of_pair[T*k]  the inverse of perm
+ * logits: device fp32 [T][E].  Requires 1 <= k <= min(E, 8), E <= 1024 and
+ * T * k < 2^31.  With T == 0 only expert_offsets is written (all zeros) and the
+ * other pointers may be NULL.  The bucketing runs in one workgroup, in chunks of pairs taken
+ * in increasing p, which is what makes the order within an expert stable.
+ * Errors: W4A8_EINVAL (null, T < 0, bad E/k). */
+w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk,
+                           int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                           int32_t *perm, int32_t *slot_of_pair, hipStream_t stream);
+
+/* Device.  Expert-grouped W4A8 GEMM.  Slots s in [expert_offsets[e],
+ * expert_offsets[e+1]) belong to expert e; slot s multiplies activation row
+ * row_index[s] (qa/a_scale row; row_index NULL means row s) with expert e's
+ * packed weights, and writes out[s][0..N).  The per-expert slot counts stay on
+ * the device: the kernel reads expert_offsets itself, so no host round trip
+ * is needed between routing and the GEMM.  Experts with few slots take the
+ * streaming loop, experts with many the tiled loop.
+ *   qa [R][K] i8 and a_scale [R] (R = rows of the activation matrix),
+ *   packed [E][N][K/2], scale/zp [E][K/128][N], out [max_slots][N].
+ * The caller guarantees expert_offsets[E] <= max_slots and row_index[s] < R
+ * (the kernel clamps slots to max_slots and skips slots whose row_index is
+ * outside [0, R)).  Errors as w4a8_gemm, plus E <= 0. */
+w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R,
+                                  const int32_t *row_index, const int32_t *expert_offsets,
+                                  int32_t E, int64_t K, const uint8_t *packed,
+                                  const uint16_t *scale, const uint16_t *zp, int64_t N,
+                                  int32_t group, int64_t max_slots, float *out,
+                                  hipStream_t stream);
+
+/* Device.  MoE expert activation then per-row re-quantization to INT8:
+ * h = silu(gate) * up with gate = gu[p][0..I), up = gu[p][I..2I),
+ * silu(v) = v / (1 + exp(-v)) in fp32; then the per-token quantizer above on
+ * each row of h: qh[P][I], h_scale[P].  h_out[P][I] (optional, may be NULL)
+ * receives the fp32 h.  Errors: W4A8_EINVAL (null, P < 0, I <= 0, I % 16). */
+w4a8_status w4a8_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh,
+                                   float *h_scale, float *h_out, hipStream_t stream);
+
+/* Device.  Weighted combine of expert outputs back to tokens:
+ * out[t][c] = sum_{j<k} topk_w[t][j] * y[slot_of_pair[t*k+j]][c] + y_shared[t][c]
+ * (y_shared may be NULL), summed in fp32 in the order j = 0..k-1, then shared.
+ * y [S][H], out [T][H] fp32.  Errors: W4A8_EINVAL (null, T < 0, H <= 0, k <= 0). */
+w4a8_status w4a8_moe_combine(const float *y, const int32_t *slot_of_pair, const float *topk_w,
+                             const float *y_shared, int64_t T, int32_t topk, int64_t H,
+                             float *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

@@ -179,3 +179,105 @@ CONFIGS = {
     "c5_moe_ffn": dict(E=384, topk=8, H=7168, I=2048, T=(64, 4096), shared=1),
 }
 GROUP = 128
+
+
+# ----------------------------------------------------------------------------- device filler
+_DEV_LIB = None
+_DEV_SRC = __import__("os").path.join(__import__("os").path.dirname(__file__), "gen_device.hip")
+DEV_LIB_PATH = _DEV_SRC.replace("gen_device.hip", "libsynth.so")
+
+
+def build_device(verbose: bool = False) -> str:
+    """Compile the GPU filler (gfx950) in-tree."""
+    import subprocess
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", _DEV_SRC, "-o", DEV_LIB_PATH]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for the synthetic filler:\n" + res.stderr)
+    return DEV_LIB_PATH
+
+
+def _dev_lib():
+    global _DEV_LIB
+    if _DEV_LIB is None:
+        import ctypes
+        lib = ctypes.CDLL(DEV_LIB_PATH)
+        lib.synth_fill_weights.restype = ctypes.c_int
+        lib.synth_fill_weights.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_int, ctypes.c_uint64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_void_p]
+        _DEV_LIB = lib
+    return _DEV_LIB
+
+
+def fill_weights_device(out, seed: int, tag: int, sub: int, K: int, row0: int = 0, mode: str = "plain"):
+    """Fill the device fp32 tensor out [rows][K] with rows [row0, row0+rows) of the same weights the
+    numpy recipes give: mode 'plain' (weights), 'outliers' (weights_with_outliers, tag must be TAG_W,
+    sub 0), 'offset' (weights_with_offset)."""
+    import ctypes
+    import torch
+    rows = out.shape[0]
+    assert out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.shape[1] == K
+    m = {"plain": 0, "outliers": 1, "offset": 2}[mode]
+    key = stream_key(seed, tag, sub)
+    key_o = stream_key(seed, TAG_OUTLIER) if m == 1 else (stream_key(seed, TAG_MU) if m == 2 else 0)
+    rc = _dev_lib().synth_fill_weights(ctypes.c_void_p(out.data_ptr()), key, key_o, row0, rows, K,
+                                       float(IH4_UNIT), float(WEIGHT_STD), m, int(OUTLIER_P_BITS),
+                                       float(OUTLIER_W_FACTOR), float(MU_UNIT),
+                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"synthetic filler launch failed ({rc})")
+    return out
+
+
+# ----------------------------------------------------------------------------- host filler (C)
+_HOST_LIB = None
+HOST_SRC = _DEV_SRC.replace("gen_device.hip", "gen_host.c")
+HOST_LIB_PATH = _DEV_SRC.replace("gen_device.hip", "libsynth_host.so")
+
+
+def build_host() -> str:
+    import subprocess
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                           HOST_SRC, "-o", HOST_LIB_PATH])
+    return HOST_LIB_PATH
+
+
+def _host_lib():
+    global _HOST_LIB
+    if _HOST_LIB is None:
+        import ctypes
+        import os
+        if not os.path.exists(HOST_LIB_PATH):
+            build_host()
+        lib = ctypes.CDLL(HOST_LIB_PATH)
+        lib.synth_fill_weights_host.restype = None
+        lib.synth_fill_weights_host.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                                ctypes.c_int, ctypes.c_uint64, ctypes.c_float, ctypes.c_float]
+        _HOST_LIB = lib
+    return _HOST_LIB
+
+
+def fill_weights_host(seed: int, tag: int, sub: int, K: int, row0: int, rows: int, mode: str = "plain"):
+    """Rows [row0, row0+rows) of a weight recipe, from the C filler (fast; same bytes as numpy)."""
+    import ctypes
+    m = {"plain": 0, "outliers": 1, "offset": 2}[mode]
+    key = stream_key(seed, tag, sub)
+    key_o = stream_key(seed, TAG_OUTLIER) if m == 1 else (stream_key(seed, TAG_MU) if m == 2 else 0)
+    out = np.empty((rows, K), np.float32)
+    _host_lib().synth_fill_weights_host(out.ctypes.data_as(ctypes.c_void_p), key, key_o, row0, rows, K,
+                                        float(IH4_UNIT), float(WEIGHT_STD), m, int(OUTLIER_P_BITS),
+                                        float(OUTLIER_W_FACTOR), float(MU_UNIT))
+    return out
+
+
+def weight_rows_host(seed: int, tag: int, sub: int, K: int, rows, mode: str = "plain"):
+    """Arbitrary (sorted or not) rows of a weight recipe via the C filler."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), K), np.float32)
+    for i, r in enumerate(rows):
+        out[i] = fill_weights_host(seed, tag, sub, K, int(r), 1, mode)[0]
+    return out

@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/w4a8.h
+declares, rejects bad arguments before any launch, and its host packer is
+bit-identical to the oracle's quantization + packing."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synthetic
+import w4a8_quantized_gemm_token_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+EINVAL, EUNSUPPORTED = 1, 2
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_function():
+    lib = w4.load()
+    names = header_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in w4a8.h but not exported"
+    assert sorted(w4.EXPORTS) == names
+    assert lib.w4a8_abi_version() == 1
+    assert lib.w4a8_status_str(2) == b"unsupported"
+
+
+P = ctypes.c_void_p
+
+
+def _fake(addr=4096):
+    return ctypes.c_void_p(addr)
+
+
+def test_validation_rejects_before_launch():
+    lib = w4.load()
+    f = _fake()
+    # null pointers
+    assert lib.w4a8_gemm(None, f, 4, 256, f, f, f, 128, 128, f, None) == EINVAL
+    # group size other than 128: unsupported, never a silent fallback
+    assert lib.w4a8_gemm(f, f, 4, 256, f, f, f, 128, 64, f, None) == EUNSUPPORTED
+    assert b"group" in lib.w4a8_last_error()
+    # K not a multiple of 128
+    assert lib.w4a8_gemm(f, f, 4, 200, f, f, f, 128, 128, f, None) == EINVAL
+    # N not a multiple of 16
+    assert lib.w4a8_gemm(f, f, 4, 256, f, f, f, 120, 128, f, None) == EINVAL
+    # misaligned packed pointer
+    assert lib.w4a8_gemm(f, f, 4, 256, _fake(4097), f, f, 128, 128, f, None) == EINVAL
+    assert b"aligned" in lib.w4a8_last_error()
+    # negative M
+    assert lib.w4a8_gemm(f, f, -1, 256, f, f, f, 128, 128, f, None) == EINVAL
+    # bad path
+    assert lib.w4a8_gemm_path(f, f, 4, 256, f, f, f, 128, 128, 7, f, None) == EINVAL
+    # streaming path with too many rows
+    assert lib.w4a8_gemm_path(f, f, 65, 256, f, f, f, 128, 128, 1, f, None) == EINVAL
+    # M == 0 is a no-op that launches nothing
+    assert lib.w4a8_gemm(f, f, 0, 256, f, f, f, 128, 128, f, None) == 0
+    # quantize_act
+    assert lib.w4a8_quantize_act(None, 4, 256, 256, f, f, None) == EINVAL
+    assert lib.w4a8_quantize_act(f, 4, 256, 100, f, f, None) == EINVAL
+    assert lib.w4a8_quantize_act(f, 4, 250, 256, f, f, None) == EINVAL
+    assert lib.w4a8_quantize_act(f, 0, 256, 256, f, f, None) == 0
+    # router
+    assert lib.w4a8_moe_route(f, 4, 8, 9, f, f, f, f, f, None) == EINVAL
+    assert lib.w4a8_moe_route(f, 4, 2000, 8, f, f, f, f, f, None) == EINVAL
+    assert lib.w4a8_moe_route(f, 4, 8, 0, f, f, f, f, f, None) == EINVAL
+    # grouped gemm
+    assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, None, 8, 256, f, f, f, 128, 128, 16, f, None) == EINVAL
+    assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 0, 256, f, f, f, 128, 128, 16, f, None) == EINVAL
+    assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 8, 256, f, f, f, 128, 256, 16, f, None) == EUNSUPPORTED
+    # silu + requant, combine
+    assert lib.w4a8_silu_mul_quantize(f, 4, 100, f, f, None, None) == EINVAL
+    assert lib.w4a8_moe_combine(f, f, f, None, 4, 1, 102, f, None) == EINVAL
+    assert lib.w4a8_moe_combine(f, f, f, None, 4, 0, 128, f, None) == EINVAL
+    # device packer sizes
+    assert lib.w4a8_pack_weights_device(f, 128, 200, 128, f, f, f, None) == EINVAL
+
+
+def test_host_packer_rejects_bad_weights():
+    W = np.zeros((2, 256), np.float32)
+    W[1, 7] = np.nan
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.pack_weights(W)
+    assert e.value.status == EINVAL
+    W[1, 7] = 1e7  # range / 15 exceeds the largest fp16
+    with pytest.raises(w4.W4A8Error):
+        w4.pack_weights(W)
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.pack_weights(np.zeros((2, 256), np.float32), group=64)
+    assert e.value.status == EUNSUPPORTED
+
+
+def _packer_matches_oracle(orc, W):
+    q, s, z = orc.quantize_weights(W)
+    p_ref = orc.pack_nibbles(q)
+    packed, scale, zp = w4.pack_weights(W)
+    assert np.array_equal(packed, p_ref)
+    assert np.array_equal(scale, s)
+    assert np.array_equal(zp, z)
+    q2, w_hat = w4.unpack_weights(packed, scale, zp)
+    assert np.array_equal(q2, q)
+    assert np.allclose(w_hat, orc.dequantize_weights(q, s, z), rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("case", ["c1", "c2_rows", "c3_rows", "c4_rows", "c5_rows", "edge"])
+def test_host_packer_bit_exact_vs_oracle(orc, case):
+    if case == "c1":
+        W = synthetic.weights(0, synthetic.TAG_W, 0, 128, 256)
+    elif case == "c2_rows":
+        W = synthetic.weights_with_outliers(0, 28672, 8192, rows=np.arange(0, 28672, 449))
+    elif case == "c3_rows":
+        W = synthetic.weights_with_offset(0, 8192, 8192, rows=np.arange(0, 8192, 127))
+    elif case == "c4_rows":
+        W = synthetic.weights(0, synthetic.TAG_W, 3, 14336, 4096, rows=np.arange(0, 14336, 211))
+    elif case == "c5_rows":
+        W = synthetic.weights(0, synthetic.TAG_W_DOWN, 17, 7168, 2048, rows=np.arange(0, 7168, 97))
+    else:
+        rng = np.random.default_rng(9)
+        W = (rng.standard_normal((24, 512)) * 0.02).astype(np.float32)
+        W[0] = 0.0                       # all-zero groups -> scale 1, zp 0
+        W[1] = np.abs(W[1]) + 0.01       # one-signed groups
+        W[2] = -np.abs(W[2]) - 0.01
+        W[3] = (np.arange(512) % 16).astype(np.float32)   # integer lattice, exact ties at x.5 absent
+        W[4, :128] = 1e-9                # scale underflows to an fp16 subnormal
+        W[5, :128] = 3e-8                # fp16 subnormal scale
+        W[6] = np.linspace(-1, 1, 512)
+        W[7, ::2] = 0.5                  # ties in w / s
+        W[8] = W[8] * 1000               # large range
+    _packer_matches_oracle(orc, W)

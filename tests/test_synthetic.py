@@ -39,3 +39,16 @@ def test_router_recipes():
     b = synthetic.zipf_bias(384)
     assert b[0] == 0 and np.all(np.diff(b) < 0)
     assert z.shape == (64, 384) and z.dtype == np.float32
+
+
+def test_host_filler_matches_numpy():
+    # plain, outliers and offset recipes: the C filler gives the numpy bytes
+    for mode, ref in [("plain", lambda r: synthetic.weights(3, synthetic.TAG_W, 5, 300, 512, rows=r)),
+                      ("outliers", lambda r: synthetic.weights_with_outliers(3, 300, 512, rows=r)),
+                      ("offset", lambda r: synthetic.weights_with_offset(3, 300, 512, rows=r))]:
+        sub = 5 if mode == "plain" else 0
+        got = synthetic.fill_weights_host(3, synthetic.TAG_W, sub, 512, 17, 40, mode)
+        assert np.array_equal(got.view(np.uint32), ref(np.arange(17, 57)).view(np.uint32)), mode
+    rows = [299, 3, 150]
+    assert np.array_equal(synthetic.weight_rows_host(3, synthetic.TAG_W, 5, 512, rows),
+                          synthetic.weights(3, synthetic.TAG_W, 5, 300, 512, rows=rows))

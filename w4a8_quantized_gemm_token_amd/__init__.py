@@ -1,0 +1,278 @@
+"""Python binding of libw4a8.so, the MI355X (gfx950) W4A8 linear-layer library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels (or, for ``pack_weights``, its host packer).  torch provides device
+memory and the current stream; nothing here computes any part of the method.
+The C names and argument meanings are documented in ``include/w4a8.h``.
+
+Loading fails loudly (ImportError at first use) when the library is missing or
+no GPU is present for a device call -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+GROUP = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a8.so")
+
+# names exported by include/w4a8.h (checked by the test suite against the header)
+EXPORTS = (
+    "w4a8_abi_version", "w4a8_status_str", "w4a8_last_error",
+    "w4a8_pack_weights", "w4a8_pack_weights_device", "w4a8_unpack_weights",
+    "w4a8_quantize_act", "w4a8_gemm", "w4a8_gemm_debug_isums", "w4a8_gemm_path",
+    "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_silu_mul_quantize", "w4a8_moe_combine",
+)
+
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: status {status} ({detail})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libw4a8.so (built in-tree by build.py); raises if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python w4a8_quantized_gemm_token_amd/build.py` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "w4a8_abi_version": (ctypes.c_int, []),
+        "w4a8_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "w4a8_last_error": (ctypes.c_char_p, []),
+        "w4a8_pack_weights": (ctypes.c_int, [p, i64, i64, i32, p, p, p]),
+        "w4a8_pack_weights_device": (ctypes.c_int, [p, i64, i64, i32, p, p, p, p]),
+        "w4a8_unpack_weights": (ctypes.c_int, [p, p, p, i64, i64, i32, p, p]),
+        "w4a8_quantize_act": (ctypes.c_int, [p, i64, i64, i64, p, p, p]),
+        "w4a8_gemm": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, p, p]),
+        "w4a8_gemm_debug_isums": (ctypes.c_int, [p, i64, i64, p, p, i64, i32, i32, p, p]),
+        "w4a8_gemm_path": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, i32, p, p]),
+        "w4a8_moe_route": (ctypes.c_int, [p, i64, i32, i32, p, p, p, p, p, p]),
+        "w4a8_moe_grouped_gemm": (ctypes.c_int, [p, p, i64, p, p, i32, i64, p, p, p, i64, i32, i64, p, p]),
+        "w4a8_silu_mul_quantize": (ctypes.c_int, [p, i64, i64, p, p, p, p]),
+        "w4a8_moe_combine": (ctypes.c_int, [p, p, p, p, i64, i32, i64, p, p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    del sz
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = load()
+        raise W4A8Error(fn, status, lib.w4a8_last_error().decode(errors="replace"))
+
+
+def _call(name: str, *args):
+    _check(name, getattr(load(), name)(*args))
+
+
+# ----------------------------------------------------------------- torch plumbing
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t):
+    if t is None:
+        return None
+    torch = _torch()
+    assert isinstance(t, torch.Tensor) and t.is_cuda, "device tensor expected"
+    assert t.is_contiguous(), "contiguous tensor expected"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_rows_ptr(t):
+    """Device pointer of a 2-D tensor whose rows may be strided (unit stride inside a row)."""
+    torch = _torch()
+    assert isinstance(t, torch.Tensor) and t.is_cuda and t.dim() == 2, "2-D device tensor expected"
+    assert t.stride(1) == 1 or t.shape[1] <= 1, "rows must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _empty(shape, dtype, like):
+    torch = _torch()
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ----------------------------------------------------------------- packing
+def pack_weights(W: np.ndarray, group: int = GROUP):
+    """Host packer: W float32 [N][K] (numpy) -> (packed u8 [N][K/2], scale u16 [G][N], zp u16 [G][N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    G = K // group if group else 0
+    packed = np.empty((N, K // 2), np.uint8)
+    scale = np.empty((max(G, 1), N), np.uint16)
+    zp = np.empty((max(G, 1), N), np.uint16)
+    _call("w4a8_pack_weights", W.ctypes.data_as(ctypes.c_void_p), N, K, group,
+          packed.ctypes.data_as(ctypes.c_void_p), scale.ctypes.data_as(ctypes.c_void_p),
+          zp.ctypes.data_as(ctypes.c_void_p))
+    return packed, scale, zp
+
+
+def unpack_weights(packed: np.ndarray, scale: np.ndarray, zp: np.ndarray, group: int = GROUP):
+    """Host: (codes u8 [N][K], dequantized float32 [N][K])."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N, K2 = packed.shape
+    K = 2 * K2
+    q = np.empty((N, K), np.uint8)
+    w = np.empty((N, K), np.float32)
+    vp = ctypes.c_void_p
+    _call("w4a8_unpack_weights", packed.ctypes.data_as(vp),
+          np.ascontiguousarray(scale, np.uint16).ctypes.data_as(vp),
+          np.ascontiguousarray(zp, np.uint16).ctypes.data_as(vp), N, K, group,
+          q.ctypes.data_as(vp), w.ctypes.data_as(vp))
+    return q, w
+
+
+def pack_weights_device(W, group: int = GROUP, out=None):
+    """Device packer: W float32 [N][K] (device) -> (packed u8, scale i16-bits, zp i16-bits) device
+    tensors.  `out` may pass preallocated (packed, scale, zp) views to fill."""
+    torch = _torch()
+    N, K = W.shape
+    if out is None:
+        out = (_empty((N, K // 2), torch.uint8, W), _empty((K // group, N), torch.int16, W),
+               _empty((K // group, N), torch.int16, W))
+    packed, scale, zp = out
+    _call("w4a8_pack_weights_device", _dev_ptr(W), N, K, group, _dev_ptr(packed), _dev_ptr(scale),
+          _dev_ptr(zp), _stream(W.device))
+    return packed, scale, zp
+
+
+# ----------------------------------------------------------------- layer
+def quantize_act(x):
+    """x float32 [M][K] (device) -> (qa int8 [M][K], a_scale float32 [M])."""
+    torch = _torch()
+    M, K = x.shape
+    qa = _empty((M, K), torch.int8, x)
+    sc = _empty((M,), torch.float32, x)
+    _call("w4a8_quantize_act", _dev_rows_ptr(x), M, K, x.stride(0), _dev_ptr(qa), _dev_ptr(sc),
+          _stream(x.device))
+    return qa, sc
+
+
+def gemm(qa, a_scale, packed, scale, zp, path: int = 0, out=None, group: int = GROUP):
+    """out float32 [M][N] = W4A8 product of the quantized activations and packed weights."""
+    torch = _torch()
+    M, K = qa.shape
+    N = packed.shape[0]
+    if out is None:
+        out = _empty((M, N), torch.float32, qa)
+    _call("w4a8_gemm_path", _dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(packed), _dev_ptr(scale),
+          _dev_ptr(zp), N, group, path, _dev_ptr(out), _stream(qa.device))
+    return out
+
+
+def gemm_debug_isums(qa, packed, zp, path: int = 0, group: int = GROUP):
+    """int32 [K/128][M][N] per-group integer sums (test aid)."""
+    torch = _torch()
+    M, K = qa.shape
+    N = packed.shape[0]
+    isums = _empty((K // group, M, N), torch.int32, qa)
+    _call("w4a8_gemm_debug_isums", _dev_ptr(qa), M, K, _dev_ptr(packed), _dev_ptr(zp), N, group, path,
+          _dev_ptr(isums), _stream(qa.device))
+    return isums
+
+
+def linear(x, packed, scale, zp, path: int = 0):
+    """Quantize x per token and run the W4A8 product: float32 [M][N]."""
+    qa, sc = quantize_act(x)
+    return gemm(qa, sc, packed, scale, zp, path=path)
+
+
+# ----------------------------------------------------------------- MoE
+def moe_route(logits, topk: int):
+    """-> (ids [T][k] i32, w [T][k] f32, offsets [E+1] i32, perm [T*k] i32, slot_of_pair [T*k] i32)."""
+    torch = _torch()
+    T, E = logits.shape
+    ids = _empty((T, topk), torch.int32, logits)
+    w = _empty((T, topk), torch.float32, logits)
+    off = _empty((E + 1,), torch.int32, logits)
+    perm = _empty((T * topk,), torch.int32, logits)
+    sop = _empty((T * topk,), torch.int32, logits)
+    _call("w4a8_moe_route", _dev_ptr(logits), T, E, topk, _dev_ptr(ids), _dev_ptr(w), _dev_ptr(off),
+          _dev_ptr(perm), _dev_ptr(sop), _stream(logits.device))
+    return ids, w, off, perm, sop
+
+
+def moe_grouped_gemm(qa, a_scale, row_index, offsets, packed, scale, zp, max_slots: int, out=None,
+                     group: int = GROUP):
+    """Expert-grouped product: out[s] = W4A8(qa[row_index[s]], expert of slot s).  packed [E][N][K/2]."""
+    torch = _torch()
+    R, K = qa.shape
+    E, N = packed.shape[0], packed.shape[1]
+    if out is None:
+        out = _empty((max_slots, N), torch.float32, qa)
+    _call("w4a8_moe_grouped_gemm", _dev_ptr(qa), _dev_ptr(a_scale), R, _dev_ptr(row_index), _dev_ptr(offsets),
+          E, K, _dev_ptr(packed), _dev_ptr(scale), _dev_ptr(zp), N, group, max_slots, _dev_ptr(out),
+          _stream(qa.device))
+    return out
+
+
+def silu_mul_quantize(gu, want_h: bool = False):
+    """gu float32 [P][2I] -> (qh int8 [P][I], h_scale float32 [P][, h float32 [P][I]])."""
+    torch = _torch()
+    P, twoI = gu.shape
+    I = twoI // 2
+    qh = _empty((P, I), torch.int8, gu)
+    hs = _empty((P,), torch.float32, gu)
+    h = _empty((P, I), torch.float32, gu) if want_h else None
+    _call("w4a8_silu_mul_quantize", _dev_ptr(gu), P, I, _dev_ptr(qh), _dev_ptr(hs), _dev_ptr(h),
+          _stream(gu.device))
+    return (qh, hs, h) if want_h else (qh, hs)
+
+
+def moe_combine(y, slot_of_pair, topk_w, y_shared=None, out=None):
+    torch = _torch()
+    T, k = topk_w.shape
+    H = y.shape[1]
+    if out is None:
+        out = _empty((T, H), torch.float32, y)
+    _call("w4a8_moe_combine", _dev_ptr(y), _dev_ptr(slot_of_pair), _dev_ptr(topk_w), _dev_ptr(y_shared), T, k, H,
+          _dev_ptr(out), _stream(y.device))
+    return out
+
+
+def moe_ffn(x, logits, topk: int, gate_up, down, max_routed: int | None = None):
+    """One MoE FFN layer: route -> quantize x -> gate/up grouped GEMM (routed experts plus a
+    shared expert stored at index E) -> silu*up + INT8 requant -> down grouped GEMM -> combine.
+
+    gate_up = (packed [E+1][2I][H/2], scale, zp); down = (packed [E+1][H][I/2], scale, zp).
+    Returns (out [T][H] float32, intermediates dict)."""
+    torch = _torch()
+    T, H = x.shape
+    E = logits.shape[1]
+    ids, w, off, perm, sop = moe_route(logits, topk)
+    P = T * topk
+    S = P + T
+    # slots [0, P): routed pairs in expert order (row = token of pair perm[s]);
+    # slots [P, P+T): the shared expert, row = token t
+    row_index = torch.cat([torch.div(perm, topk, rounding_mode="floor"),
+                           torch.arange(T, dtype=torch.int32, device=x.device)]).to(torch.int32).contiguous()
+    offsets = torch.cat([off, (off[-1:] + T)]).contiguous()
+    qa, sc = quantize_act(x)
+    gu = moe_grouped_gemm(qa, sc, row_index, offsets, *gate_up, max_slots=S)
+    qh, hs = silu_mul_quantize(gu)
+    y = moe_grouped_gemm(qh, hs, None, offsets, *down, max_slots=S)
+    out = moe_combine(y, sop, w, y_shared=y[P:])
+    return out, dict(ids=ids, w=w, offsets=offsets, perm=perm, slot_of_pair=sop, row_index=row_index,
+                     qa=qa, a_scale=sc, gu=gu, qh=qh, h_scale=hs, y=y)

@@ -1,0 +1,294 @@
+// abi.cpp -- the extern "C" entry points of libw4a8.so: argument validation,
+// error reporting, the host-side weight packer, and dispatch to the kernels.
+//
+// The host packer restates the group quantization of [p2 §2.1, §2.2]
+// (pptc.cn/news/121597, "Kimi 2.7 MoE, 4-bit storage to INT8, dissected"):
+// scale = (max - min)/15 over the group's range widened to contain 0, stored as
+// fp16; zp = round(-min/scale); q = clamp(round(w/scale) + zp, 0, 15) with the
+// stored fp16 scale; two codes per byte, first code in the low nibble.  fp16
+// conversion uses the compiler's _Float16 (IEEE binary16, round to nearest even).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "w4a8_internal.hpp"
+
+namespace w4a8 {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+w4a8_status hip_status(hipError_t err, const char *what) {
+    if (err == hipSuccess) return W4A8_OK;
+    set_error("%s: %s", what, hipGetErrorString(err));
+    return W4A8_EHIP;
+}
+
+}  // namespace w4a8
+
+using namespace w4a8;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define W4A8_REQUIRE(cond, code, ...) \
+    do {                              \
+        if (!(cond)) {                \
+            set_error(__VA_ARGS__);   \
+            return code;              \
+        }                             \
+    } while (0)
+
+w4a8_status check_group(int32_t group, int64_t K) {
+    W4A8_REQUIRE(group == W4A8_GROUP, W4A8_EUNSUPPORTED, "group size %d is not supported (only 128)", (int)group);
+    W4A8_REQUIRE(K > 0 && K % W4A8_GROUP == 0, W4A8_EINVAL, "K=%lld must be a positive multiple of 128",
+                 (long long)K);
+    return W4A8_OK;
+}
+
+uint16_t f32_to_f16_bits(float f) {
+    const _Float16 h = (_Float16)f;
+    uint16_t b;
+    std::memcpy(&b, &h, 2);
+    return b;
+}
+
+float f16_bits_to_f32(uint16_t b) {
+    _Float16 h;
+    std::memcpy(&h, &b, 2);
+    return (float)h;
+}
+
+// Quantize columns [n0, n1); returns false on non-finite input or fp16 overflow.
+bool pack_columns(const float *W, int64_t N, int64_t K, int64_t n0, int64_t n1, uint8_t *packed, uint16_t *scale,
+                  uint16_t *zp) {
+    const int64_t G = K / W4A8_GROUP;
+    uint8_t codes[W4A8_GROUP];
+    for (int64_t n = n0; n < n1; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float *w = W + n * K + g * W4A8_GROUP;
+            float lo = 0.0f, hi = 0.0f;
+            for (int i = 0; i < W4A8_GROUP; ++i) {
+                if (!std::isfinite(w[i])) return false;
+                lo = std::fmin(lo, w[i]);
+                hi = std::fmax(hi, w[i]);
+            }
+            uint16_t sh = f32_to_f16_bits((hi - lo) / 15.0f);
+            if ((sh & 0x7C00u) == 0x7C00u) return false;
+            float s = f16_bits_to_f32(sh);
+            if (s == 0.0f) {
+                sh = 0x3C00u;
+                s = 1.0f;
+            }
+            const int z = (int)std::fmin(std::fmax(std::nearbyint(-lo / s), 0.0f), 15.0f);
+            for (int i = 0; i < W4A8_GROUP; ++i) {
+                const int v = (int)std::nearbyint(w[i] / s) + z;
+                codes[i] = (uint8_t)(v < 0 ? 0 : (v > 15 ? 15 : v));
+            }
+            uint8_t *dst = packed + n * (K / 2) + g * (W4A8_GROUP / 2);
+            for (int j = 0; j < W4A8_GROUP / 2; ++j) dst[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+            scale[g * N + n] = sh;
+            zp[g * N + n] = f32_to_f16_bits((float)z);
+        }
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a8_abi_version(void) { return W4A8_ABI_VERSION; }
+
+const char *w4a8_status_str(int status) {
+    switch (status) {
+    case W4A8_OK: return "ok";
+    case W4A8_EINVAL: return "invalid argument";
+    case W4A8_EUNSUPPORTED: return "unsupported";
+    case W4A8_EHIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *w4a8_last_error(void) { return g_err; }
+
+w4a8_status w4a8_pack_weights(const float *W, int64_t N, int64_t K, int32_t group, uint8_t *packed, uint16_t *scale,
+                              uint16_t *zp) {
+    clear_error();
+    W4A8_REQUIRE(W && packed && scale && zp, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    unsigned hw = std::thread::hardware_concurrency();
+    int64_t nthreads = hw ? hw : 1;
+    if (nthreads > N) nthreads = N;
+    if ((N * K) < (1 << 20)) nthreads = 1;
+    std::vector<char> ok((size_t)nthreads, 1);
+    std::vector<std::thread> pool;
+    const int64_t per = (N + nthreads - 1) / nthreads;
+    for (int64_t t = 0; t < nthreads; ++t) {
+        const int64_t n0 = t * per, n1 = std::min(N, n0 + per);
+        if (n0 >= n1) continue;
+        pool.emplace_back([=, &ok] { ok[t] = pack_columns(W, N, K, n0, n1, packed, scale, zp); });
+    }
+    for (auto &th : pool) th.join();
+    for (char c : ok)
+        W4A8_REQUIRE(c, W4A8_EINVAL, "weights contain non-finite values or a group range too large for an fp16 scale");
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_unpack_weights(const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t K,
+                                int32_t group, uint8_t *q_out, float *w_hat) {
+    clear_error();
+    W4A8_REQUIRE(packed && scale && zp, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t b = packed[n * (K / 2) + k / 2];
+            const uint8_t q = (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+            if (q_out) q_out[n * K + k] = q;
+            if (w_hat) {
+                const int64_t g = k / W4A8_GROUP;
+                const float s = f16_bits_to_f32(scale[g * N + n]);
+                const float z = f16_bits_to_f32(zp[g * N + n]);
+                w_hat[n * K + k] = ((float)q - z) * s;
+            }
+        }
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_pack_weights_device(const float *W, int64_t N, int64_t K, int32_t group, uint8_t *packed,
+                                     uint16_t *scale, uint16_t *zp, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(W && packed && scale && zp, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(((uintptr_t)W & 7u) == 0, W4A8_EINVAL, "W must be 8-byte aligned");
+    return hip_status(launch_pack_weights(W, N, K, packed, scale, zp, stream), "pack_weights_device launch");
+}
+
+w4a8_status w4a8_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa, float *a_scale,
+                              hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(x && qa && a_scale, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(M >= 0 && K > 0 && ldx >= K, W4A8_EINVAL, "bad sizes M=%lld K=%lld ldx=%lld", (long long)M,
+                 (long long)K, (long long)ldx);
+    W4A8_REQUIRE(K % 16 == 0, W4A8_EINVAL, "K=%lld must be a multiple of 16", (long long)K);
+    W4A8_REQUIRE(aligned16(qa), W4A8_EINVAL, "qa must be 16-byte aligned");
+    W4A8_REQUIRE(M < (1ll << 31), W4A8_EINVAL, "M too large");
+    if (M == 0) return W4A8_OK;
+    return hip_status(launch_quantize_act(x, M, K, ldx, qa, a_scale, stream), "quantize_act launch");
+}
+
+static w4a8_status check_gemm(const int8_t *qa, int64_t M, int64_t K, const uint8_t *packed, const uint16_t *scale,
+                              const uint16_t *zp, int64_t N, int32_t group, const void *out) {
+    W4A8_REQUIRE(qa && packed && zp && out, W4A8_EINVAL, "null pointer");
+    (void)scale;
+    W4A8_REQUIRE(M >= 0, W4A8_EINVAL, "M=%lld must be >= 0", (long long)M);
+    W4A8_REQUIRE(N > 0 && N % 16 == 0, W4A8_EINVAL, "N=%lld must be a positive multiple of 16", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(aligned16(qa) && aligned16(packed) && aligned16(out), W4A8_EINVAL,
+                 "qa, packed and out must be 16-byte aligned");
+    return W4A8_OK;
+}
+
+static w4a8_status gemm_common(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                               const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group, int32_t path,
+                               float *out, int32_t *isums, hipStream_t stream) {
+    W4A8_REQUIRE(path >= 0 && path <= 2, W4A8_EINVAL, "path=%d must be 0, 1 or 2", (int)path);
+    if (path == 0) path = (M <= kStreamMaxM) ? 1 : 2;
+    W4A8_REQUIRE(!(path == 1 && M > kStreamMaxM), W4A8_EINVAL, "the streaming loop takes M <= %lld",
+                 (long long)kStreamMaxM);
+    if (M == 0) return W4A8_OK;
+    return hip_status(launch_gemm(qa, a_scale, M, K, packed, scale, zp, N, path, out, isums, stream), "gemm launch");
+}
+
+w4a8_status w4a8_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                      const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group, float *out,
+                      hipStream_t stream) {
+    return w4a8_gemm_path(qa, a_scale, M, K, packed, scale, zp, N, group, 0, out, stream);
+}
+
+w4a8_status w4a8_gemm_path(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                           const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group, int32_t path,
+                           float *out, hipStream_t stream) {
+    clear_error();
+    if (w4a8_status st = check_gemm(qa, M, K, packed, scale, zp, N, group, out)) return st;
+    W4A8_REQUIRE(a_scale && scale, W4A8_EINVAL, "null pointer");
+    return gemm_common(qa, a_scale, M, K, packed, scale, zp, N, group, path, out, nullptr, stream);
+}
+
+w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K, const uint8_t *packed, const uint16_t *zp,
+                                  int64_t N, int32_t group, int32_t path, int32_t *isums, hipStream_t stream) {
+    clear_error();
+    if (w4a8_status st = check_gemm(qa, M, K, packed, nullptr, zp, N, group, isums)) return st;
+    return gemm_common(qa, nullptr, M, K, packed, nullptr, zp, N, group, path, nullptr, isums, stream);
+}
+
+w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t *topk_ids, float *topk_w,
+                           int32_t *expert_offsets, int32_t *perm, int32_t *slot_of_pair, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(expert_offsets && (T == 0 || (logits && topk_ids && topk_w && perm && slot_of_pair)), W4A8_EINVAL,
+                 "null pointer");
+    W4A8_REQUIRE(T >= 0, W4A8_EINVAL, "T=%lld must be >= 0", (long long)T);
+    W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
+    W4A8_REQUIRE(topk >= 1 && topk <= 8 && topk <= E, W4A8_EINVAL, "topk=%d must be in [1, min(E, 8)]", (int)topk);
+    W4A8_REQUIRE(T * topk < (1ll << 31), W4A8_EINVAL, "T*topk too large");
+    return hip_status(
+        launch_moe_route(logits, T, E, topk, topk_ids, topk_w, expert_offsets, perm, slot_of_pair, stream),
+        "moe_route launch");
+}
+
+w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
+                                  const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
+                                  const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group,
+                                  int64_t max_slots, float *out, hipStream_t stream) {
+    clear_error();
+    if (w4a8_status st = check_gemm(qa, R, K, packed, scale, zp, N, group, out)) return st;
+    W4A8_REQUIRE(a_scale && scale && expert_offsets, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
+    W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");
+    if (max_slots == 0 || R == 0) return W4A8_OK;
+    return hip_status(launch_grouped_gemm(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
+                                          max_slots, out, stream),
+                      "grouped_gemm launch");
+}
+
+w4a8_status w4a8_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh, float *h_scale, float *h_out,
+                                   hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(gu && qh && h_scale, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(P >= 0 && I > 0 && I % 16 == 0, W4A8_EINVAL, "bad sizes P=%lld I=%lld (I must be a multiple of 16)",
+                 (long long)P, (long long)I);
+    W4A8_REQUIRE(aligned16(qh), W4A8_EINVAL, "qh must be 16-byte aligned");
+    W4A8_REQUIRE(P < (1ll << 31), W4A8_EINVAL, "P too large");
+    if (P == 0) return W4A8_OK;
+    return hip_status(launch_silu_mul_quantize(gu, P, I, qh, h_scale, h_out, stream), "silu_mul_quantize launch");
+}
+
+w4a8_status w4a8_moe_combine(const float *y, const int32_t *slot_of_pair, const float *topk_w, const float *y_shared,
+                             int64_t T, int32_t topk, int64_t H, float *out, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(y && slot_of_pair && topk_w && out, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(T >= 0 && topk > 0 && H > 0 && H % 4 == 0, W4A8_EINVAL,
+                 "bad sizes T=%lld topk=%d H=%lld (H must be a multiple of 4)", (long long)T, (int)topk, (long long)H);
+    W4A8_REQUIRE(aligned16(y) && aligned16(out) && (!y_shared || aligned16(y_shared)), W4A8_EINVAL,
+                 "y, y_shared and out must be 16-byte aligned");
+    W4A8_REQUIRE(T < (1ll << 31), W4A8_EINVAL, "T too large");
+    return hip_status(launch_moe_combine(y, slot_of_pair, topk_w, y_shared, T, topk, H, out, stream),
+                      "moe_combine launch");
+}
+
+}  // extern "C"

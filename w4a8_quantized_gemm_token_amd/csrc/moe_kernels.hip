@@ -1,0 +1,225 @@
+// moe_kernels.hip -- routing, expert bucketing and the weighted combine.
+//
+// [p1 §5.2] (hotelren.com/news/5173946, "Kimi 2.7 MoE: from 4-bit storage to
+// INT8 compute"): the router is kept in high precision and decides which
+// experts each token visits; [p1 §5.1, §6.3]: unbalanced buckets must not
+// degrade into many small matmuls -- the grouped GEMM therefore consumes the
+// expert-sorted slot list built here straight from device memory.
+// [p4] (feinterview.poetries.top, "MoE deployment: active parameters are not the
+// storage bill"): the toy top-1 router over 8 experts.
+//
+//  * route_topk: one wave per token; each lane keeps E/64 logits in registers,
+//    k rounds of a wave-wide (value, -id) arg-max pick the experts in
+//    descending order (ties -> lower id), then a softmax over the k picks.
+//  * bucket: one workgroup; per-expert counts with LDS integer atomics, an
+//    exclusive scan, then a stable placement: pairs are taken in chunks of 1024
+//    in increasing pair index; inside a wave, lanes with the same expert are
+//    found with ballots over the expert id bits, and per-wave counts in LDS
+//    give each pair its rank among equal experts -- deterministic, no atomics
+//    on positions.
+//  * combine: out[t] = sum_j w[t][j] * y[slot(t, j)] + y_shared[t], float4 wide.
+#include "w4a8_internal.hpp"
+
+using namespace w4a8dev;
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 8;
+constexpr int kPerLane = kMaxE / kWave;  // 16
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+constexpr int kRouteThreads = 256;
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
+                                                                   int32_t E, int32_t k, int32_t *__restrict__ ids,
+                                                                   float *__restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float v[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int e = i * kWave + lane;
+        v[i] = e < E ? logits[t * E + e] : -INFINITY;
+    }
+    bool taken[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) taken[i] = (i * kWave + lane) >= E;
+    float sel_v[kMaxK];
+    int sel_i[kMaxK];
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = i * kWave + lane;
+            if (!taken[i] && (bi == 0x7FFFFFFF || better(v[i], e, bv, bi))) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, kWave);
+            const int oi = __shfl_xor(bi, off, kWave);
+            if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        sel_v[j] = bv;
+        sel_i[j] = bi;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+            if (i * kWave + lane == bi) taken[i] = true;
+    }
+    if (lane == 0) {
+        const float top = sel_v[0];
+        float denom = 0.0f;
+        float ex[kMaxK];
+        for (int j = 0; j < k; ++j) {
+            ex[j] = expf(sel_v[j] - top);
+            denom += ex[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            ids[t * k + j] = sel_i[j];
+            w[t * k + j] = ex[j] / denom;
+        }
+    }
+}
+
+constexpr int kBucketThreads = 1024;
+constexpr int kBucketWaves = kBucketThreads / kWave;
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *__restrict__ ids, int64_t P, int32_t E,
+                                                                int32_t *__restrict__ offsets,
+                                                                int32_t *__restrict__ perm,
+                                                                int32_t *__restrict__ slot_of_pair) {
+    __shared__ int32_t count[kMaxE];
+    __shared__ int32_t base[kMaxE];      // offsets[e] + pairs of e already placed
+    __shared__ int32_t scan[kBucketThreads];
+    __shared__ uint8_t wave_cnt[kBucketWaves][kMaxE];  // <= 64 per wave
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int e = tid; e < E; e += kBucketThreads) count[e] = 0;
+    for (int i = tid; i < kBucketWaves * kMaxE; i += kBucketThreads) (&wave_cnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int64_t p = tid; p < P; p += kBucketThreads) atomicAdd(&count[ids[p]], 1);
+    __syncthreads();
+
+    // exclusive scan of count[0..E) (E <= 1024 = one entry per thread)
+    scan[tid] = tid < E ? count[tid] : 0;
+    __syncthreads();
+    for (int off = 1; off < kBucketThreads; off <<= 1) {
+        const int32_t v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) {
+        const int32_t excl = scan[tid] - count[tid];
+        base[tid] = excl;
+        offsets[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = scan[kBucketThreads - 1];
+    __syncthreads();
+
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int64_t c0 = 0; c0 < P; c0 += kBucketThreads) {
+        const int64_t p = c0 + tid;
+        const bool valid = p < P;
+        const int e = valid ? ids[p] : -1;
+        // lanes of this wave holding the same expert
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t bit = __ballot(valid && ((e >> b) & 1));
+            peers &= ((e >> b) & 1) ? bit : ~bit;
+        }
+        const int rank_in_wave = __popcll(peers & lt_mask);
+        const bool leader = valid && rank_in_wave == 0;
+        if (leader) wave_cnt[wave][e] = (uint8_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int32_t before = base[e];
+            for (int w2 = 0; w2 < wave; ++w2) before += wave_cnt[w2][e];
+            const int32_t slot = before + rank_in_wave;
+            perm[slot] = (int32_t)p;
+            slot_of_pair[p] = slot;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int32_t add = 0;
+            for (int w2 = 0; w2 < kBucketWaves; ++w2) add += wave_cnt[w2][tid];
+            base[tid] += add;
+        }
+        __syncthreads();
+        if (leader) wave_cnt[wave][e] = 0;
+        __syncthreads();
+    }
+}
+
+constexpr int kCombineThreads = 256;
+// grid: (T, ceil(H/4 / 256)); each thread one float4 of one token row
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ y,
+                                                                  const int32_t *__restrict__ slot_of_pair,
+                                                                  const float *__restrict__ topk_w,
+                                                                  const float *__restrict__ y_shared, int32_t k,
+                                                                  int64_t H, float *__restrict__ out) {
+    const int64_t t = blockIdx.x;
+    const int64_t c4 = (int64_t)blockIdx.y * kCombineThreads + threadIdx.x;
+    if (c4 * 4 >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float wj = topk_w[t * k + j];
+        const int64_t s = slot_of_pair[t * k + j];
+        const float4 v = reinterpret_cast<const float4 *>(y + s * H)[c4];
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z);
+        acc.w = fmaf(wj, v.w, acc.w);
+    }
+    if (y_shared) {
+        const float4 v = reinterpret_cast<const float4 *>(y_shared + t * H)[c4];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    reinterpret_cast<float4 *>(out + t * H)[c4] = acc;
+}
+
+}  // namespace
+
+namespace w4a8 {
+
+hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t *ids, float *w,
+                            int32_t *offsets, int32_t *perm, int32_t *slot_of_pair, hipStream_t stream) {
+    if (T > 0) {
+        const int64_t per = kRouteThreads / kWave;
+        hipLaunchKernelGGL(route_topk_kernel, dim3((uint32_t)((T + per - 1) / per)), dim3(kRouteThreads), 0, stream,
+                           logits, T, E, topk, ids, w);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, T * topk, E, offsets, perm,
+                       slot_of_pair);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const float *y, const int32_t *slot_of_pair, const float *topk_w, const float *y_shared,
+                              int64_t T, int32_t topk, int64_t H, float *out, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int64_t c4 = H / 4;
+    const dim3 grid((uint32_t)T, (uint32_t)((c4 + kCombineThreads - 1) / kCombineThreads));
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, stream, y, slot_of_pair, topk_w, y_shared, topk,
+                       H, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

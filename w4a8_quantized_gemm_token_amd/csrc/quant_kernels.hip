@@ -1,0 +1,206 @@
+// quant_kernels.hip -- the quantizers of the W4A8 layer on gfx950.
+//
+//  * quantize_act: per-token dynamic symmetric INT8 ([p1 §5.3]: the scale is
+//    computed in the kernel at forward time; [p3 §2.1]: q = round(x/s),
+//    s = max|x| / 127).  One workgroup per row; the row maximum is a wave64
+//    shuffle reduction followed by a cross-wave LDS step.
+//  * silu_mul_quantize: the MoE expert activation silu(gate) * up followed by the
+//    same per-row quantizer (the INT8 input of the down projection).
+//  * pack_weights: group-wise asymmetric 4-bit weight quantization and nibble
+//    packing ([p2 §2.1, §2.2]), one wave per (output feature, group of 128).
+//
+// Page keys: [p1] hotelren.com/news/5173946 "Kimi 2.7 MoE: from 4-bit storage to
+// INT8 compute"; [p2] pptc.cn/news/121597 "Kimi 2.7 MoE, 4-bit storage to INT8,
+// dissected"; [p3] hotelren.com/news/5982361 "LLM quantization primer".
+//
+// All three are HBM-bound streaming kernels: they read fp32 and write int8.
+#include "w4a8_internal.hpp"
+
+using namespace w4a8dev;
+
+namespace {
+
+constexpr int kActThreads = 256;
+constexpr int kActWaves = kActThreads / kWave;
+
+// Block-wide max of a non-negative float over kActThreads threads.
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < kActWaves; ++i) m = fmaxf(m, red[i]);
+    return m;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)(d & 0xFF) << 24);
+}
+
+// x rows of K floats (stride ldx); each thread owns groups of 4 consecutive
+// columns.  VEC: x rows are 16-byte aligned, so float4 loads are used.
+template <bool VEC>
+__global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const float *__restrict__ x, int64_t K,
+                                                                   int64_t ldx, int8_t *__restrict__ qa,
+                                                                   float *__restrict__ a_scale) {
+    __shared__ float red[kActWaves];
+    const int64_t m = blockIdx.x;
+    const float *row = x + m * ldx;
+    const int64_t K4 = K / 4;
+    float amax = 0.0f;
+    for (int64_t c = threadIdx.x; c < K4; c += kActThreads) {
+        float4 v;
+        if (VEC) v = reinterpret_cast<const float4 *>(row)[c];
+        else v = make_float4(row[4 * c], row[4 * c + 1], row[4 * c + 2], row[4 * c + 3]);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    amax = block_max(amax, red);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) a_scale[m] = s;
+    uint32_t *out = reinterpret_cast<uint32_t *>(qa + m * K);
+    for (int64_t c = threadIdx.x; c < K4; c += kActThreads) {
+        float4 v;
+        if (VEC) v = reinterpret_cast<const float4 *>(row)[c];
+        else v = make_float4(row[4 * c], row[4 * c + 1], row[4 * c + 2], row[4 * c + 3]);
+        out[c] = pack4_i8(quantize_i8(v.x, s), quantize_i8(v.y, s), quantize_i8(v.z, s), quantize_i8(v.w, s));
+    }
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// One workgroup per row p of gu [P][2I]; h lives in registers between the max
+// and the quantization (VPT4 float4 per thread covers I <= 4 * VPT4 * 256).
+template <int VPT4>
+__global__ __launch_bounds__(kActThreads) void silu_mul_quantize_kernel(const float *__restrict__ gu, int64_t I,
+                                                                        int8_t *__restrict__ qh,
+                                                                        float *__restrict__ h_scale,
+                                                                        float *__restrict__ h_out) {
+    __shared__ float red[kActWaves];
+    const int64_t p = blockIdx.x;
+    const float4 *gate = reinterpret_cast<const float4 *>(gu + p * 2 * I);
+    const float4 *up = reinterpret_cast<const float4 *>(gu + p * 2 * I + I);
+    const int64_t I4 = I / 4;
+    float4 h[VPT4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT4; ++i) {
+        const int64_t c = threadIdx.x + (int64_t)i * kActThreads;
+        if (c < I4) {
+            const float4 g = gate[c], u = up[c];
+            h[i] = make_float4(silu_mul(g.x, u.x), silu_mul(g.y, u.y), silu_mul(g.z, u.z), silu_mul(g.w, u.w));
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(h[i].x), fabsf(h[i].y)), fmaxf(fabsf(h[i].z), fabsf(h[i].w))));
+            if (h_out) reinterpret_cast<float4 *>(h_out + p * I)[c] = h[i];
+        }
+    }
+    amax = block_max(amax, red);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) h_scale[p] = s;
+    uint32_t *out = reinterpret_cast<uint32_t *>(qh + p * I);
+#pragma unroll
+    for (int i = 0; i < VPT4; ++i) {
+        const int64_t c = threadIdx.x + (int64_t)i * kActThreads;
+        if (c < I4)
+            out[c] = pack4_i8(quantize_i8(h[i].x, s), quantize_i8(h[i].y, s), quantize_i8(h[i].z, s),
+                              quantize_i8(h[i].w, s));
+    }
+}
+
+// Fallback for long rows: h recomputed in the second pass.
+__global__ __launch_bounds__(kActThreads) void silu_mul_quantize_long_kernel(const float *__restrict__ gu, int64_t I,
+                                                                             int8_t *__restrict__ qh,
+                                                                             float *__restrict__ h_scale,
+                                                                             float *__restrict__ h_out) {
+    __shared__ float red[kActWaves];
+    const int64_t p = blockIdx.x;
+    const float *gate = gu + p * 2 * I;
+    const float *up = gate + I;
+    float amax = 0.0f;
+    for (int64_t c = threadIdx.x; c < I; c += kActThreads) {
+        const float h = silu_mul(gate[c], up[c]);
+        amax = fmaxf(amax, fabsf(h));
+        if (h_out) h_out[p * I + c] = h;
+    }
+    amax = block_max(amax, red);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) h_scale[p] = s;
+    for (int64_t c = threadIdx.x; c < I; c += kActThreads) qh[p * I + c] = (int8_t)quantize_i8(silu_mul(gate[c], up[c]), s);
+}
+
+// One wave per (output feature n, group g); lane l owns weights 2l and 2l+1 of
+// the group, i.e. exactly packed byte l of the group.
+constexpr int kPackThreads = 256;
+__global__ __launch_bounds__(kPackThreads) void pack_weights_kernel(const float *__restrict__ W, int64_t N,
+                                                                    int64_t K, uint8_t *__restrict__ packed,
+                                                                    uint16_t *__restrict__ scale,
+                                                                    uint16_t *__restrict__ zp) {
+    const int64_t G = K / W4A8_GROUP;
+    const int64_t unit = (int64_t)blockIdx.x * (kPackThreads / kWave) + threadIdx.x / kWave;
+    if (unit >= N * G) return;
+    const int64_t n = unit / G, g = unit % G;
+    const int lane = threadIdx.x % kWave;
+    const float2 w = reinterpret_cast<const float2 *>(W + n * K + g * W4A8_GROUP)[lane];
+    // the range always contains 0: zp in [0, 15], (q - zp) in [-15, 15]
+    const float lo = wave_min(fminf(fminf(w.x, w.y), 0.0f));
+    const float hi = wave_max(fmaxf(fmaxf(w.x, w.y), 0.0f));
+    uint16_t sh = float_to_half_bits((hi - lo) / 15.0f);
+    float s = half_bits_to_float(sh);
+    if (s == 0.0f) {
+        sh = 0x3C00;  // 1.0
+        s = 1.0f;
+    }
+    const int z = (int)fminf(fmaxf(__builtin_rintf(-lo / s), 0.0f), 15.0f);
+    const int q0 = min(max((int)__builtin_rintf(w.x / s) + z, 0), 15);
+    const int q1 = min(max((int)__builtin_rintf(w.y / s) + z, 0), 15);
+    packed[n * (K / 2) + g * (W4A8_GROUP / 2) + lane] = (uint8_t)(q0 | (q1 << 4));
+    if (lane == 0) {
+        scale[g * N + n] = sh;
+        zp[g * N + n] = float_to_half_bits((float)z);
+    }
+}
+
+}  // namespace
+
+namespace w4a8 {
+
+hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa, float *a_scale,
+                               hipStream_t stream) {
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
+    if (vec)
+        hipLaunchKernelGGL(quantize_act_kernel<true>, dim3((uint32_t)M), dim3(kActThreads), 0, stream, x, K, ldx, qa,
+                           a_scale);
+    else
+        hipLaunchKernelGGL(quantize_act_kernel<false>, dim3((uint32_t)M), dim3(kActThreads), 0, stream, x, K, ldx,
+                           qa, a_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh, float *h_scale, float *h_out,
+                                    hipStream_t stream) {
+    const int64_t I4 = I / 4;
+    const bool vec = ((uintptr_t)gu % 16 == 0) && (h_out == nullptr || (uintptr_t)h_out % 16 == 0);
+    if (vec && I4 <= kActThreads * 2)
+        hipLaunchKernelGGL(silu_mul_quantize_kernel<2>, dim3((uint32_t)P), dim3(kActThreads), 0, stream, gu, I, qh,
+                           h_scale, h_out);
+    else if (vec && I4 <= kActThreads * 4)
+        hipLaunchKernelGGL(silu_mul_quantize_kernel<4>, dim3((uint32_t)P), dim3(kActThreads), 0, stream, gu, I, qh,
+                           h_scale, h_out);
+    else
+        hipLaunchKernelGGL(silu_mul_quantize_long_kernel, dim3((uint32_t)P), dim3(kActThreads), 0, stream, gu, I, qh,
+                           h_scale, h_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *packed, uint16_t *scale, uint16_t *zp,
+                               hipStream_t stream) {
+    const int64_t units = N * (K / W4A8_GROUP);
+    const int64_t per_block = kPackThreads / kWave;
+    const int64_t blocks = (units + per_block - 1) / per_block;
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((uint32_t)blocks), dim3(kPackThreads), 0, stream, W, N, K, packed,
+                       scale, zp);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

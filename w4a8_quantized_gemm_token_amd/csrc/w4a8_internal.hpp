@@ -1,0 +1,94 @@
+// w4a8_internal.hpp -- shared internals of libw4a8.so (gfx950 only).
+//
+// Error state for the C ABI, launch wrappers (one per kernel family) and small
+// device helpers used by several kernels.  Nothing here is part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w4a8.h"
+
+namespace w4a8 {
+
+// ---------------------------------------------------------------- error state
+void set_error(const char *fmt, ...);
+void clear_error();
+w4a8_status hip_status(hipError_t err, const char *what);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already validated.
+hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa,
+                               float *a_scale, hipStream_t stream);
+hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh,
+                                    float *h_scale, float *h_out, hipStream_t stream);
+hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *packed,
+                               uint16_t *scale, uint16_t *zp, hipStream_t stream);
+
+// Dense GEMM.  path: 1 = streaming (M <= 64), 2 = tiled.  isums != nullptr selects
+// the debug epilogue that stores the per-group int32 sums instead of `out`.
+hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
+                       const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
+                       int64_t N, int path, float *out, int32_t *isums, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R,
+                               const int32_t *row_index, const int32_t *expert_offsets, int32_t E,
+                               int64_t K, const uint8_t *packed, const uint16_t *scale,
+                               const uint16_t *zp, int64_t N, int64_t max_slots, float *out,
+                               hipStream_t stream);
+
+hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t *ids,
+                            float *w, int32_t *offsets, int32_t *perm, int32_t *slot_of_pair,
+                            hipStream_t stream);
+
+hipError_t launch_moe_combine(const float *y, const int32_t *slot_of_pair, const float *topk_w,
+                              const float *y_shared, int64_t T, int32_t topk, int64_t H, float *out,
+                              hipStream_t stream);
+
+// Streaming-path threshold: the dense GEMM uses the streaming loop for M <= this.
+constexpr int64_t kStreamMaxM = 64;
+
+}  // namespace w4a8
+
+// ---------------------------------------------------------------- device helpers
+#ifdef __HIPCC__
+namespace w4a8dev {
+
+constexpr int kWave = 64;
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// fp16 bit pattern <-> fp32 (hardware conversions, round to nearest even, subnormals kept)
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Per-token symmetric INT8 code of v for a row scale s (s == 0 -> 0).
+// IEEE fp32 divide (the library is built with correctly rounded fp32 division),
+// round half to even, clamp to [-127, 127].
+__device__ __forceinline__ int quantize_i8(float v, float s) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+}  // namespace w4a8dev
+#endif
