@@ -60,6 +60,13 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles) {
     return x * q + (x < r ? x : r) + i;
 }
 
+// Largest power of two <= umax that divides the group count G (prefetch ring depth).
+__host__ __device__ inline int ring_depth(int64_t G, int umax) {
+    int u = umax;
+    while (u > 1 && G % u != 0) u >>= 1;
+    return u;
+}
+
 // ------------------------------------------------------------------ streaming loop
 constexpr int kStreamThreads = 64;
 
@@ -83,16 +90,18 @@ __device__ __forceinline__ void stream_unit(const int8_t *__restrict__ qa, const
                                             const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
                                             int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
                                             int32_t *__restrict__ isums, int64_t M_isums) {
+    // Every global load in the group loop is unconditional (rows outside the
+    // unit read row 0 and are zeroed after the load), so the compiler can count
+    // the U groups in flight exactly instead of draining the queue each group.
     const int lane = threadIdx.x & 63;
     const int kq = lane >> 4;
     const int64_t col = n0 + (lane & 15);
-    const int64_t G = K / G128;
+    const int64_t G = K / G128;  // a multiple of U (chosen by the launcher)
 
     const v4u *bptr = reinterpret_cast<const v4u *>(wpk + col * (K / 2) + kq * 16);
     const uint16_t *sptr = wsc + col;
     const uint16_t *zptr = wzp + col;
 
-    // activation rows of this lane (row (l & 15) of each 16-row tile)
     const int8_t *aptr[MT];
     bool avalid[MT];
 #pragma unroll
@@ -120,64 +129,61 @@ __device__ __forceinline__ void stream_unit(const int8_t *__restrict__ qa, const
         sq[u] = sptr[g * N];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            if (avalid[t]) {
-                const v4u *ap = reinterpret_cast<const v4u *>(aptr[t] + g * G128);
-                aq[u][t][0] = ap[0];
-                aq[u][t][1] = ap[1];
-            } else {
-                aq[u][t][0] = v4u{0u, 0u, 0u, 0u};
-                aq[u][t][1] = v4u{0u, 0u, 0u, 0u};
-            }
+            const v4u *ap = reinterpret_cast<const v4u *>(aptr[t] + g * G128);
+            aq[u][t][0] = ap[0];
+            aq[u][t][1] = ap[1];
         }
     };
 
+    // prologue in the same slot order as the loop, so the wait counts at the loop
+    // head agree on both incoming paths
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        if (u < G) load_group(u, u);
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(u, u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     for (int64_t g0 = 0; g0 < G; g0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g = g0 + u;
-            if (g < G) {
-                const v4u b = bq[u];
-                const uint16_t zb = zq[u], sb = sq[u];
-                v4u a[MT][2];
+            // consume slot u in place ...
+            const uint32_t zadd = zp_add_const(zq[u]);
+            uint32_t w[8];
+            unpack8(bq[u].x, zadd, w[0], w[1]);
+            unpack8(bq[u].y, zadd, w[2], w[3]);
+            unpack8(bq[u].z, zadd, w[4], w[5]);
+            unpack8(bq[u].w, zadd, w[6], w[7]);
+            const v4i b0 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+            const v4i b1 = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+            const float sc = half_bits_to_float(sq[u]);
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    a[t][0] = aq[u][t][0];
-                    a[t][1] = aq[u][t][1];
-                }
-                if (g + U < G) load_group(u, g + U);
-
-                const uint32_t zadd = zp_add_const(zb);
-                uint32_t w[8];
-                unpack8(b.x, zadd, w[0], w[1]);
-                unpack8(b.y, zadd, w[2], w[3]);
-                unpack8(b.z, zadd, w[4], w[5]);
-                unpack8(b.w, zadd, w[6], w[7]);
-                const v4i b0 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-                const v4i b1 = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-                const float sc = half_bits_to_float(sb);
+            for (int t = 0; t < MT; ++t) {
+                const v4i zero = {0, 0, 0, 0};
+                const v4i a0 = avalid[t] ? __builtin_bit_cast(v4i, aq[u][t][0]) : zero;
+                const v4i a1 = avalid[t] ? __builtin_bit_cast(v4i, aq[u][t][1]) : zero;
+                v4i d = {0, 0, 0, 0};
+                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, d, 0, 0, 0);
+                if (ISUMS) {
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const v4i a0 = {(int)a[t][0].x, (int)a[t][0].y, (int)a[t][0].z, (int)a[t][0].w};
-                    const v4i a1 = {(int)a[t][1].x, (int)a[t][1].y, (int)a[t][1].z, (int)a[t][1].w};
-                    v4i d = {0, 0, 0, 0};
-                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, d, 0, 0, 0);
-                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, d, 0, 0, 0);
-                    if (ISUMS) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int m = t * 16 + 4 * kq + r;
-                            if (m < rows.rows) isums[(g * M_isums + rows.slot0 + m) * N + col] = d[r];
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(sc, (float)d[r], acc[t][r]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = t * 16 + 4 * kq + r;
+                        if (m < rows.rows) isums[(g * M_isums + rows.slot0 + m) * N + col] = d[r];
                     }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(sc, (float)d[r], acc[t][r]);
                 }
             }
+            // ... then refill it U groups ahead (past the end: the last group again, never
+            // consumed).  The fences keep the ring in program order so that the wait
+            // before each slot's use only covers that slot's loads.
+            const int64_t gn = (g + U < G) ? g + U : G - 1;
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(u, gn);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -194,6 +200,203 @@ __device__ __forceinline__ void stream_unit(const int8_t *__restrict__ qa, const
                 }
             }
     }
+}
+
+// ------------------------------------------------------------------ streaming loop, line-wide
+// The packed weights are read with every load instruction covering whole 128-byte
+// lines: 8 columns x 128 B (two groups), 8 lanes per column.  Lane L of load j
+// reads column 8j + (L & 7), group (L >> 3) & 1 of the two-group window, quarter
+// L >> 4 (16 bytes = 32 codes).  A DPP rotate by 8 within each 16-lane row plus a
+// select turns the two loads into the 16x16x64 MFMA operand layout: X (first
+// group) and Y (second group) hold column L & 15, quarter L >> 4.
+// Zero points are applied on the matrix cores: sum_k a_k (q_k - zp) is the MFMA of
+// the raw codes plus the MFMA of the same activations with a B operand whose
+// bytes are all -zp, so the weights only need their nibbles spread to bytes.
+// SPLIT waves of a workgroup take disjoint halves of the groups; their fp32 sums
+// are added in a fixed order through LDS at the end.
+__device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+}
+
+// nibbles of one packed dword -> 8 codes (k order) as two dwords of bytes
+__device__ __forceinline__ void spread8(uint32_t d, uint32_t &w0, uint32_t &w1) {
+    const uint32_t lo = d & 0x0F0F0F0Fu;
+    const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;
+    w0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    w1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+template <int MT, int U, int SPLIT, bool ISUMS>
+__device__ __forceinline__ void stream2_unit(float *lds_red, const int8_t *__restrict__ qa,
+                                             const float *__restrict__ a_scale,
+                                             const int32_t *__restrict__ row_index, int64_t R, StreamRows rows,
+                                             int64_t K, const uint8_t *__restrict__ wpk,
+                                             const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
+                                             int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
+                                             int32_t *__restrict__ isums, int64_t M_isums) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;     // split index
+    const int kq = lane >> 4;
+    const int64_t col = n0 + (lane & 15);  // MFMA column of this lane
+    const int64_t G = K / G128;
+    const int64_t nwin = G / 2 / SPLIT;    // two-group windows of this wave
+    const int64_t win0 = wave * nwin;
+
+    // weight loads: column n0 + 8j + (lane & 7), byte (lane >> 3 & 1) * 64 + kq * 16 of each window
+    const int lchunk = ((lane >> 3) & 1) * 64 + kq * 16;
+    const v4u *b0p = reinterpret_cast<const v4u *>(wpk + (n0 + (lane & 7)) * (K / 2) + lchunk);
+    const v4u *b1p = reinterpret_cast<const v4u *>(wpk + (n0 + 8 + (lane & 7)) * (K / 2) + lchunk);
+    const uint16_t *sptr = wsc + col;
+    const uint16_t *zptr = wzp + col;
+    const bool hi8 = (lane & 8) != 0;
+
+    // activation rows; rows outside the unit read row 0 and are never stored
+    const int8_t *aptr[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int r = t * 16 + (lane & 15);
+        int64_t row = -1;
+        if (r < rows.rows) row = row_index ? (int64_t)row_index[rows.slot0 + r] : rows.slot0 + r;
+        aptr[t] = qa + ((row >= 0 && row < R) ? row : 0) * K + kq * 32;
+    }
+
+    float acc[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+
+    v4u rb0[U], rb1[U];
+    v4u ra[U][MT][2][2];   // [slot][row tile][group of window][step]
+    uint16_t rs[U][2], rz[U][2];
+
+    auto load_window = [&](int u, int64_t w) {
+        rb0[u] = __builtin_nontemporal_load(b0p + w * 8);
+        rb1[u] = __builtin_nontemporal_load(b1p + w * 8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            rs[u][h] = sptr[(2 * w + h) * N];
+            rz[u][h] = zptr[(2 * w + h) * N];
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const v4u *ap = reinterpret_cast<const v4u *>(aptr[t] + (2 * w + h) * G128);
+                ra[u][t][h][0] = ap[0];
+                ra[u][t][h][1] = ap[1];
+            }
+    };
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_window(u, win0 + u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int64_t w0 = 0; w0 < nwin; w0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t w = win0 + w0 + u;
+            // operand layout: X = first group, Y = second group of the window
+            uint32_t xy[2][4];
+            {
+                const uint32_t r0[4] = {rb0[u].x, rb0[u].y, rb0[u].z, rb0[u].w};
+                const uint32_t r1[4] = {rb1[u].x, rb1[u].y, rb1[u].z, rb1[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t t1 = dpp_ror8(r1[i]);
+                    const uint32_t t0 = dpp_ror8(r0[i]);
+                    xy[0][i] = hi8 ? t1 : r0[i];
+                    xy[1][i] = hi8 ? r1[i] : t0;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t q[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) spread8(xy[h][i], q[2 * i], q[2 * i + 1]);
+                const v4i bq0 = {(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                const v4i bq1 = {(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+                const int zneg = -(int)half_bits_to_float(rz[u][h]);
+                const int z4 = (int)((uint32_t)(zneg & 0xFF) * 0x01010101u);
+                const v4i bz = {z4, z4, z4, z4};
+                const float sc = half_bits_to_float(rs[u][h]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const v4i a0 = __builtin_bit_cast(v4i, ra[u][t][h][0]);
+                    const v4i a1 = __builtin_bit_cast(v4i, ra[u][t][h][1]);
+                    v4i d = {0, 0, 0, 0};
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq1, d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bz, d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bz, d, 0, 0, 0);
+                    if (ISUMS) {
+                        const int64_t g = 2 * w + h;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int m = t * 16 + 4 * kq + r;
+                            if (m < rows.rows) isums[(g * M_isums + rows.slot0 + m) * N + col] = d[r];
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(sc, (float)d[r], acc[t][r]);
+                    }
+                }
+            }
+            // refill the slot U windows ahead (past the end: the last window, never consumed)
+            const int64_t wn = (w0 + u + U < nwin) ? w + U : win0 + nwin - 1;
+            __builtin_amdgcn_sched_barrier(0);
+            load_window(u, wn);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if (!ISUMS) {
+        if (SPLIT > 1) {
+            // fixed-order reduction of the K halves: wave 0 + wave 1
+            if (wave == 1) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) lds_red[(t * 4 + r) * 64 + lane] = acc[t][r];
+            }
+            __syncthreads();
+            if (wave == 1) return;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[t][r] += lds_red[(t * 4 + r) * 64 + lane];
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = t * 16 + 4 * kq + r;
+                if (m < rows.rows) {
+                    const int64_t slot = rows.slot0 + m;
+                    const int64_t row = row_index ? (int64_t)row_index[slot] : slot;
+                    if (row >= 0 && row < R) out[slot * ldo + col] = a_scale[row] * acc[t][r];
+                }
+            }
+    }
+}
+
+// Dense layer through the line-wide loop: a workgroup of SPLIT waves per 16-column tile.
+template <int MT, int U, int SPLIT, bool ISUMS>
+__global__ __launch_bounds__(64 * SPLIT) void gemm_stream2_kernel(const int8_t *__restrict__ qa,
+                                                                  const float *__restrict__ a_scale, int64_t M,
+                                                                  int64_t K, const uint8_t *__restrict__ packed,
+                                                                  const uint16_t *__restrict__ scale,
+                                                                  const uint16_t *__restrict__ zp, int64_t N,
+                                                                  float *__restrict__ out,
+                                                                  int32_t *__restrict__ isums) {
+    __shared__ float red[MT * 4 * 64];
+    const int64_t ntiles = N / 16;
+    const int64_t tile = xcd_tile(blockIdx.x, ntiles);
+    stream2_unit<MT, U, SPLIT, ISUMS>(red, qa, a_scale, nullptr, M, StreamRows{0, (int)M}, K, packed, scale, zp, N,
+                                      tile * 16, out, N, isums, M);
 }
 
 // Dense layer, M <= 16*MT: one wave per 16-column tile.
@@ -241,7 +444,9 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t G = K / G128;
 
-    // ---- loader state
+    // ---- loader state.  Loads are unconditional: rows/columns outside the tile
+    // read row/column 0 and are zeroed when written to LDS, so no branch sits
+    // between a prefetch and its consumer.
     const int lrow = tid >> 1, lpart = tid & 1;
     int64_t arow = -1;
     if (lrow < rows.rows) arow = row_index ? (int64_t)row_index[rows.slot0 + lrow] : rows.slot0 + lrow;
@@ -252,54 +457,7 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
     const v4u *bglob = reinterpret_cast<const v4u *>(wpk + (bvalid ? bcol : 0) * (K / 2) + lpart * 32);
     const uint16_t *zglob = wzp + (bvalid ? bcol : 0);
 
-    v4u ra[4], rb[2];
-    uint16_t rz = 0;
-    auto gload = [&](int64_t g) {
-        if (avalid) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ra[i] = aglob[g * (G128 / 16) + i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ra[i] = v4u{0u, 0u, 0u, 0u};
-        }
-        if (bvalid) {
-            rb[0] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16));
-            rb[1] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16) + 1);
-            rz = zglob[g * N];
-        } else {
-            rb[0] = rb[1] = v4u{0u, 0u, 0u, 0u};
-            rz = 0;
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint8_t *A = lds + buf * 2 * kLdsTile;
-        uint8_t *B = A + kLdsTile;
-        v4u *ad = reinterpret_cast<v4u *>(A + lrow * kLdsStride + lpart * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ad[i] = ra[i];
-        const uint32_t zadd = zp_add_const(rz);
-        uint32_t w[16];
-        const uint32_t d[8] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w, rb[1].x, rb[1].y, rb[1].z, rb[1].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) unpack8(d[i], zadd, w[2 * i], w[2 * i + 1]);
-        if (!bvalid) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) w[i] = 0;
-        }
-        v4u *bd = reinterpret_cast<v4u *>(B + lrow * kLdsStride + lpart * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bd[i] = v4u{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-    };
-
     // ---- compute state
-    float acc[2][2][16];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
     const int frow = lane & 31, fk = (lane >> 5) * 16;
     int64_t scol[2];
     bool svalid[2];
@@ -308,17 +466,61 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
         scol[j] = n0 + wn * 64 + j * 32 + (lane & 31);
         svalid[j] = scol[j] < N;
     }
+    const uint16_t *sglob[2] = {wsc + (svalid[0] ? scol[0] : 0), wsc + (svalid[1] ? scol[1] : 0)};
+
+    v4u ra[4], rb[2];
+    uint16_t rz = 0, rs[2];
+    auto gload = [&](int64_t g) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[i] = aglob[g * (G128 / 16) + i];
+        rb[0] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16));
+        rb[1] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16) + 1);
+        rz = zglob[g * N];
+        rs[0] = sglob[0][g * N];
+        rs[1] = sglob[1][g * N];
+    };
+    auto lstore = [&](int buf) {
+        uint8_t *A = lds + buf * 2 * kLdsTile;
+        uint8_t *B = A + kLdsTile;
+        v4u *ad = reinterpret_cast<v4u *>(A + lrow * kLdsStride + lpart * 64);
+        const v4u zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ad[i] = avalid ? ra[i] : zero;
+        const uint32_t zadd = zp_add_const(rz);
+        uint32_t w[16];
+        const uint32_t d[8] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w, rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) unpack8(d[i], zadd, w[2 * i], w[2 * i + 1]);
+        v4u *bd = reinterpret_cast<v4u *>(B + lrow * kLdsStride + lpart * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v4u v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            bd[i] = bvalid ? v : zero;
+        }
+    };
+
+    float acc[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     gload(0);
     lstore(0);
+    float sc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sc[j] = svalid[j] ? half_bits_to_float(rs[j]) : 0.0f;
     __syncthreads();
 
     for (int64_t g = 0; g < G; ++g) {
         const int buf = (int)(g & 1);
-        if (g + 1 < G) gload(g + 1);
-        float sc[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) sc[j] = svalid[j] ? half_bits_to_float(wsc[g * N + scol[j]]) : 0.0f;
+        // prefetch the next group (past the end: the last group again, never consumed)
+        gload(g + 1 < G ? g + 1 : G - 1);
+        // keep the prefetch at the top: the scheduler would otherwise sink the loads
+        // next to their use in lstore and expose the full memory latency
+        __builtin_amdgcn_sched_barrier(0);
 
         const uint8_t *A = lds + buf * 2 * kLdsTile;
         const uint8_t *B = A + kLdsTile;
@@ -357,7 +559,13 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
                         acc[i][j][r] = fmaf(sc[j], (float)d[i][j][r], acc[i][j][r]);
                     }
                 }
-        if (g + 1 < G) lstore(buf ^ 1);
+        // unconditional: on the last group this rewrites the idle buffer with data
+        // nobody reads, which keeps the prefetch loads from being sunk below the MFMAs;
+        // fenced so that its waits on the prefetch are not hoisted above the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(buf ^ 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sc[j] = svalid[j] ? half_bits_to_float(rs[j]) : 0.0f;
         __syncthreads();
     }
 
@@ -457,6 +665,7 @@ __device__ __forceinline__ int64_t clamp_slots(int64_t v, int64_t max_slots) {
     return v < 0 ? 0 : (v > max_slots ? max_slots : v);
 }
 
+template <int U>
 __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
@@ -469,6 +678,7 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
         return (c > 0 && c <= kSmallRows) ? ntn : 0;
     });
     const int64_t G = K / G128;
+    constexpr int U2 = U < 4 ? U : 4, U4 = U < 2 ? U : 2;
     for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
         const int e = find_expert(pfx, E, u);
         const int64_t tn = u - pfx[e];
@@ -479,11 +689,11 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
         const uint16_t *wz = zp + (int64_t)e * G * N;
         const StreamRows sr{s0, rows};
         if (rows <= 16)
-            stream_unit<1, 4, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+            stream_unit<1, U, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
         else if (rows <= 32)
-            stream_unit<2, 4, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+            stream_unit<2, U2, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
         else
-            stream_unit<4, 2, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+            stream_unit<4, U4, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
     }
 }
 
@@ -514,6 +724,50 @@ __global__ __launch_bounds__(kTileThreads, 2) void grouped_tiled_kernel(
     }
 }
 
+
+#ifndef W4A8_STREAM_U1
+#define W4A8_STREAM_U1 2
+#endif
+
+template <int MT, int U, int SPLIT>
+hipError_t launch_stream2_t(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                            const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
+                            hipStream_t stream) {
+    const dim3 grid((uint32_t)(N / 16)), block(64 * SPLIT);
+    if (isums)
+        hipLaunchKernelGGL((gemm_stream2_kernel<MT, U, SPLIT, true>), grid, block, 0, stream, qa, a_scale, M, K, packed,
+                           scale, zp, N, out, isums);
+    else
+        hipLaunchKernelGGL((gemm_stream2_kernel<MT, U, SPLIT, false>), grid, block, 0, stream, qa, a_scale, M, K,
+                           packed, scale, zp, N, out, isums);
+    return hipGetLastError();
+}
+
+template <int MT, int U>
+hipError_t launch_stream2_s(int split, const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
+                            const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, float *out,
+                            int32_t *isums, hipStream_t stream) {
+    return split == 2 ? launch_stream2_t<MT, U, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
+                      : launch_stream2_t<MT, U, 1>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+}
+
+hipError_t launch_stream2(int mt, int u, int split, const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
+                          const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, float *out,
+                          int32_t *isums, hipStream_t stream) {
+    if (mt == 1) {
+        if (u >= 4 && W4A8_STREAM_U1 >= 4)
+            return launch_stream2_s<1, (W4A8_STREAM_U1 >= 4 ? 4 : 1)>(split, qa, a_scale, M, K, packed, scale, zp, N,
+                                                                        out, isums, stream);
+        if (u >= 2) return launch_stream2_s<1, 2>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        return launch_stream2_s<1, 1>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+    }
+    if (mt == 2) {
+        if (u >= 2) return launch_stream2_s<2, 2>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        return launch_stream2_s<2, 1>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+    }
+    return launch_stream2_s<4, 1>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+}
+
 }  // namespace
 
 namespace w4a8 {
@@ -522,20 +776,39 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
                        const uint16_t *scale, const uint16_t *zp, int64_t N, int path, float *out, int32_t *isums,
                        hipStream_t stream) {
     if (path == 1) {
+        const int64_t G = K / G128;
+        const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        if (G % 2 == 0) {
+            // line-wide loop: two-group windows, K split over two waves when it divides
+            const int split = (G % 4 == 0) ? 2 : 1;
+            const int64_t nwin = G / 2 / split;
+            const int u = ring_depth(nwin, mt == 1 ? W4A8_STREAM_U1 : (mt == 2 ? 2 : 1));
+            return launch_stream2(mt, u, split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        }
         const dim3 grid((uint32_t)(N / 16)), block(kStreamThreads);
-#define W4A8_STREAM(MT, U)                                                                                        \
+        const int umax = M <= 16 ? 8 : (M <= 32 ? 4 : 2);
+        const int U = ring_depth(G, umax);
+#define W4A8_STREAM_U(MT, UU)                                                                                     \
     do {                                                                                                          \
         if (isums)                                                                                                \
-            hipLaunchKernelGGL((gemm_stream_kernel<MT, U, true>), grid, block, 0, stream, qa, a_scale, M, K,      \
+            hipLaunchKernelGGL((gemm_stream_kernel<MT, UU, true>), grid, block, 0, stream, qa, a_scale, M, K,     \
                                packed, scale, zp, N, out, isums);                                                 \
         else                                                                                                      \
-            hipLaunchKernelGGL((gemm_stream_kernel<MT, U, false>), grid, block, 0, stream, qa, a_scale, M, K,     \
+            hipLaunchKernelGGL((gemm_stream_kernel<MT, UU, false>), grid, block, 0, stream, qa, a_scale, M, K,    \
                                packed, scale, zp, N, out, isums);                                                 \
     } while (0)
-        if (M <= 16) W4A8_STREAM(1, 8);
-        else if (M <= 32) W4A8_STREAM(2, 4);
-        else W4A8_STREAM(4, 2);
+#define W4A8_STREAM(MT)                              \
+    do {                                             \
+        if (U == 8) W4A8_STREAM_U(MT, (MT == 1 ? 8 : 1)); \
+        else if (U == 4) W4A8_STREAM_U(MT, (MT <= 2 ? 4 : 1)); \
+        else if (U == 2) W4A8_STREAM_U(MT, 2);       \
+        else W4A8_STREAM_U(MT, 1);                   \
+    } while (0)
+        if (M <= 16) W4A8_STREAM(1);
+        else if (M <= 32) W4A8_STREAM(2);
+        else W4A8_STREAM(4);
 #undef W4A8_STREAM
+#undef W4A8_STREAM_U
     } else {
         const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
         const dim3 grid((uint32_t)tiles), block(kTileThreads);
@@ -556,8 +829,17 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
-    hipLaunchKernelGGL(grouped_stream_kernel, dim3((uint32_t)(cus * 8)), dim3(kStreamThreads), 0, stream, qa, a_scale,
-                       R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+    const int U = ring_depth(K / G128, 4);
+    const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
+    if (U == 4)
+        hipLaunchKernelGGL(grouped_stream_kernel<4>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
+                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+    else if (U == 2)
+        hipLaunchKernelGGL(grouped_stream_kernel<2>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
+                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+    else
+        hipLaunchKernelGGL(grouped_stream_kernel<1>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
+                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(grouped_tiled_kernel, dim3((uint32_t)(cus * 2)), dim3(kTileThreads), 0, stream, qa, a_scale, R,
