@@ -383,6 +383,168 @@ __device__ __forceinline__ void stream2_unit(float *lds_red, const int8_t *__res
     }
 }
 
+// ------------------------------------------------------------------ decode loop, activations in LDS
+// For M <= 16 every wave needs the same activation rows; reading them through the
+// vector memory path costs twice the address-unit time of the weights.  Here one
+// 1024-thread workgroup per CU stages qa[M][K] in LDS once (rows padded by 16 bytes
+// so the 16 rows of an MFMA fragment fall in different banks); its 16 waves then
+// stream full-line weight windows (as in the loop above) and read activation
+// fragments from LDS.  Workgroup b owns a contiguous range of 16-column tiles; wave
+// w takes tile w / SPLIT, K half w % SPLIT of each round, and the two halves are
+// added through LDS at the end of the round (fixed order: half 0 + half 1).
+constexpr int kDecWaves = 16;
+constexpr int kDecThreads = kDecWaves * 64;
+
+__host__ __device__ inline int64_t dec_lds_bytes(int64_t M, int64_t K) { return M * (K + 16); }
+constexpr int64_t kDecLdsMax = 140 * 1024;
+
+template <int U, int SPLIT, bool ISUMS>
+__global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *__restrict__ qa,
+                                                                 const float *__restrict__ a_scale, int64_t M,
+                                                                 int64_t K, const uint8_t *__restrict__ wpk,
+                                                                 const uint16_t *__restrict__ wsc,
+                                                                 const uint16_t *__restrict__ wzp, int64_t N,
+                                                                 int64_t tiles_per_wg, float *__restrict__ out,
+                                                                 int32_t *__restrict__ isums) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    const int64_t lda = K + 16;
+    const int tid = threadIdx.x;
+    // stage qa[M][K] (16-byte pieces)
+    {
+        const int64_t pieces = M * (K / 16);
+        for (int64_t i = tid; i < pieces; i += kDecThreads) {
+            const int64_t r = i / (K / 16), c = i % (K / 16);
+            *reinterpret_cast<v4u *>(dsm + r * lda + c * 16) = reinterpret_cast<const v4u *>(qa + r * K)[c];
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int kq = lane >> 4;
+    const int half = wave % SPLIT;
+    const int64_t G = K / G128;
+    const int64_t nwin = G / 2 / SPLIT;
+    const int64_t win0 = half * nwin;
+    const int64_t ntiles = N / 16;
+    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_wg;
+    const int64_t t1 = (t0 + tiles_per_wg < ntiles) ? t0 + tiles_per_wg : ntiles;
+    constexpr int per_round = kDecWaves / SPLIT;
+    const int arow = (lane & 15) < M ? (lane & 15) : 0;
+    const uint8_t *abase = dsm + arow * lda + kq * 32;
+    const int lchunk = ((lane >> 3) & 1) * 64 + kq * 16;
+    const bool hi8 = (lane & 8) != 0;
+    float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(M, K) + 15) / 16) * 16);
+
+    for (int64_t tb = t0; tb < t1; tb += per_round) {
+        const int64_t tile = tb + wave / SPLIT;
+        const bool active = (wave / SPLIT) < per_round && tile < t1;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (active) {
+            const int64_t n0 = tile * 16;
+            const int64_t col = n0 + (lane & 15);
+            const v4u *b0p = reinterpret_cast<const v4u *>(wpk + (n0 + (lane & 7)) * (K / 2) + lchunk);
+            const v4u *b1p = reinterpret_cast<const v4u *>(wpk + (n0 + 8 + (lane & 7)) * (K / 2) + lchunk);
+            // one 2-byte load per window gives all four per-column constants of the
+            // window: lane row kq fetches scale (kq = 0, 1) or zp (kq = 2, 3) of
+            // group 2w + (kq & 1); ds_bpermute then broadcasts them across rows
+            const uint16_t *szptr = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + col;
+            v4u rb0[U], rb1[U];
+            uint32_t rsz[U];
+            auto load_window = [&](int u, int64_t w) {
+                rb0[u] = __builtin_nontemporal_load(b0p + w * 8);
+                rb1[u] = __builtin_nontemporal_load(b1p + w * 8);
+                rsz[u] = szptr[2 * w * N];
+            };
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_window(u, win0 + u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            for (int64_t w0 = 0; w0 < nwin; w0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t w = win0 + w0 + u;
+                    uint32_t xy[2][4];
+                    {
+                        const uint32_t r0[4] = {rb0[u].x, rb0[u].y, rb0[u].z, rb0[u].w};
+                        const uint32_t r1[4] = {rb1[u].x, rb1[u].y, rb1[u].z, rb1[u].w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t t1v = dpp_ror8(r1[i]);
+                            const uint32_t t0v = dpp_ror8(r0[i]);
+                            xy[0][i] = hi8 ? t1v : r0[i];
+                            xy[1][i] = hi8 ? r1[i] : t0v;
+                        }
+                    }
+                    uint32_t sz[4];  // scale g0, scale g1, zp g0, zp g1 of this lane's column
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sz[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)rsz[u]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int64_t g = 2 * w + h;
+                        const v4i a0 = *reinterpret_cast<const v4i *>(abase + g * G128);
+                        const v4i a1 = *reinterpret_cast<const v4i *>(abase + g * G128 + 16);
+                        uint32_t q[8];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) spread8(xy[h][i], q[2 * i], q[2 * i + 1]);
+                        const v4i bq0 = {(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                        const v4i bq1 = {(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+                        const int zneg = -(int)half_bits_to_float((uint16_t)sz[2 + h]);
+                        const int z4 = (int)((uint32_t)(zneg & 0xFF) * 0x01010101u);
+                        const v4i bz = {z4, z4, z4, z4};
+                        v4i d = {0, 0, 0, 0};
+                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq1, d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bz, d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bz, d, 0, 0, 0);
+                        if (ISUMS) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int m = 4 * kq + r;
+                                if (m < M) isums[(g * M + m) * N + col] = d[r];
+                            }
+                        } else {
+                            const float sc = half_bits_to_float((uint16_t)sz[h]);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, (float)d[r], acc[r]);
+                        }
+                    }
+                    const int64_t wn = (w0 + u + U < nwin) ? w + U : win0 + nwin - 1;
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_window(u, wn);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        if (!ISUMS) {
+            if (SPLIT > 1) {
+                if (active && half == 1) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((wave / SPLIT) * 4 + r) * 64 + lane] = acc[r];
+                }
+                __syncthreads();
+                if (active && half == 1) {
+                    // nothing more for this wave in this round
+                } else if (active) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] += red[((wave / SPLIT) * 4 + r) * 64 + lane];
+                }
+                __syncthreads();
+            }
+            if (active && half == 0) {
+                const int64_t col = tile * 16 + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * kq + r;
+                    if (m < M) out[m * N + col] = a_scale[m] * acc[r];
+                }
+            }
+        }
+    }
+}
+
 // Dense layer through the line-wide loop: a workgroup of SPLIT waves per 16-column tile.
 template <int MT, int U, int SPLIT, bool ISUMS>
 __global__ __launch_bounds__(64 * SPLIT) void gemm_stream2_kernel(const int8_t *__restrict__ qa,
@@ -415,87 +577,101 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(const int8_
 }
 
 // ------------------------------------------------------------------ tiled loop
-constexpr int kTileThreads = 256;
-constexpr int BM = 128, BN = 128;
-constexpr int kLdsStride = G128 + 16;  // padded row: 144 bytes, conflict-free 128-bit reads
-constexpr int kLdsTile = BM * kLdsStride;
+// A workgroup of WM x WN waves computes a (64 WM) x (64 WN) tile; each wave a 64x64
+// sub-tile as 2x2 v_mfma_i32_32x32x32_i8 tiles.  Per group of 128 k the workgroup
+// stages the activation rows (INT8) and the weight columns (unpacked once, to INT8
+// (q - zp)) in LDS, double-buffered, rows padded to 144 bytes so the 128-bit
+// fragment reads of 32 rows are bank-conflict free.  The next group's global loads
+// are issued before the current group's MFMAs and only waited on when they are
+// written to the idle LDS buffer (one barrier per group).
+// Rows/columns outside the matrix read row/column 0: their results are never
+// stored, so no masking is needed anywhere in the loop.
+// Lane l of a 32x32 tile feeds A row (l&31) / B column (l&31) with k bytes
+// ks*32 + (l>>5)*16 + [0,16), and holds accumulator rows 8*(r>>2) + 4*(l>>5) + (r&3),
+// r = 0..15, of column l&31.
+constexpr int kLdsStride = G128 + 16;  // padded row: 144 bytes
 
 struct TileRows {
     int64_t slot0;
-    int rows;  // valid rows in this tile (<= BM)
+    int rows;  // valid rows in this tile
 };
 
-// One workgroup: rows [slot0, slot0 + rows) x columns [n0, n0 + 128), all K.
-// Loader mapping (per group): thread t loads A row t/2, bytes (t&1)*64 + [0,64),
-// and B column t/2, packed bytes (t&1)*32 + [0,32) (= codes (t&1)*64 + [0,64)).
-// Wave w computes rows (w>>1)*64 + [0,64) x columns (w&1)*64 + [0,64) as 2x2
-// 32x32 MFMA tiles; lane l of a 32x32 tile feeds A row (l&31) / B column (l&31)
-// with k bytes ks*32 + (l>>5)*16 + [0,16), and holds accumulator rows
-// 8*(r>>2) + 4*(l>>5) + (r&3), r = 0..15, of column l&31.
-template <bool ISUMS>
-__device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict__ qa,
-                                          const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
-                                          int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
-                                          const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
-                                          int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
-                                          int32_t *__restrict__ isums, int64_t M_isums) {
+template <int WM, int WN>
+struct TileShape {
+    static constexpr int BM = 64 * WM, BN = 64 * WN, THREADS = 64 * WM * WN;
+    static constexpr int A_TPR = THREADS / BM;          // threads per A row
+    static constexpr int A_BYTES = G128 / A_TPR;        // A bytes per thread per group
+    static constexpr int B_TPC = THREADS / BN;          // threads per B column
+    static constexpr int B_PACKED = (G128 / 2) / B_TPC; // packed B bytes per thread per group
+    static constexpr int LDS_A = BM * kLdsStride, LDS_B = BN * kLdsStride;
+    static constexpr int LDS_STAGE = LDS_A + LDS_B;
+    static_assert(A_BYTES % 16 == 0 && B_PACKED % 16 == 0, "loader granularity");
+};
+
+template <int WM, int WN, bool ISUMS>
+__device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restrict__ qa,
+                                           const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
+                                           int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
+                                           const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
+                                           int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
+                                           int32_t *__restrict__ isums, int64_t M_isums) {
+    using S = TileShape<WM, WN>;
+    constexpr int NA = S::A_BYTES / 16, NB = S::B_PACKED / 16;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int64_t G = K / G128;
 
-    // ---- loader state.  Loads are unconditional: rows/columns outside the tile
-    // read row/column 0 and are zeroed when written to LDS, so no branch sits
-    // between a prefetch and its consumer.
-    const int lrow = tid >> 1, lpart = tid & 1;
+    // ---- loader state
+    const int arow_l = tid / S::A_TPR, apart = tid % S::A_TPR;
     int64_t arow = -1;
-    if (lrow < rows.rows) arow = row_index ? (int64_t)row_index[rows.slot0 + lrow] : rows.slot0 + lrow;
-    const bool avalid = arow >= 0 && arow < R;
-    const v4u *aglob = reinterpret_cast<const v4u *>(qa + (avalid ? arow : 0) * K + lpart * 64);
-    const int64_t bcol = n0 + lrow;
-    const bool bvalid = bcol < N;
-    const v4u *bglob = reinterpret_cast<const v4u *>(wpk + (bvalid ? bcol : 0) * (K / 2) + lpart * 32);
-    const uint16_t *zglob = wzp + (bvalid ? bcol : 0);
+    if (arow_l < rows.rows) arow = row_index ? (int64_t)row_index[rows.slot0 + arow_l] : rows.slot0 + arow_l;
+    if (arow < 0 || arow >= R) arow = 0;
+    const v4u *aglob = reinterpret_cast<const v4u *>(qa + arow * K + apart * S::A_BYTES);
+    const int bcol_l = tid / S::B_TPC, bpart = tid % S::B_TPC;
+    const int64_t bcol = (n0 + bcol_l < N) ? n0 + bcol_l : 0;
+    const v4u *bglob = reinterpret_cast<const v4u *>(wpk + bcol * (K / 2) + bpart * S::B_PACKED);
+    const uint16_t *zglob = wzp + bcol;
 
     // ---- compute state
     const int frow = lane & 31, fk = (lane >> 5) * 16;
     int64_t scol[2];
-    bool svalid[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        scol[j] = n0 + wn * 64 + j * 32 + (lane & 31);
-        svalid[j] = scol[j] < N;
-    }
-    const uint16_t *sglob[2] = {wsc + (svalid[0] ? scol[0] : 0), wsc + (svalid[1] ? scol[1] : 0)};
+    for (int j = 0; j < 2; ++j) scol[j] = n0 + wn * 64 + j * 32 + (lane & 31);
+    const uint16_t *sglob[2] = {wsc + (scol[0] < N ? scol[0] : 0), wsc + (scol[1] < N ? scol[1] : 0)};
 
-    v4u ra[4], rb[2];
-    uint16_t rz = 0, rs[2];
-    auto gload = [&](int64_t g) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = aglob[g * (G128 / 16) + i];
-        rb[0] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16));
-        rb[1] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16) + 1);
-        rz = zglob[g * N];
-        rs[0] = sglob[0][g * N];
-        rs[1] = sglob[1][g * N];
+    // two register slots of prefetched group data (activation bytes, packed weights,
+    // zero point, the two scales of this lane's columns)
+    struct Slot {
+        v4u ra[NA], rb[NB];
+        uint16_t rz, rs[2];
     };
-    auto lstore = [&](int buf) {
-        uint8_t *A = lds + buf * 2 * kLdsTile;
-        uint8_t *B = A + kLdsTile;
-        v4u *ad = reinterpret_cast<v4u *>(A + lrow * kLdsStride + lpart * 64);
-        const v4u zero = {0u, 0u, 0u, 0u};
+    Slot sa, sb;
+    auto gload = [&](Slot &sl, int64_t g) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ad[i] = avalid ? ra[i] : zero;
-        const uint32_t zadd = zp_add_const(rz);
-        uint32_t w[16];
-        const uint32_t d[8] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w, rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+        for (int i = 0; i < NA; ++i) sl.ra[i] = aglob[g * (G128 / 16) + i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) unpack8(d[i], zadd, w[2 * i], w[2 * i + 1]);
-        v4u *bd = reinterpret_cast<v4u *>(B + lrow * kLdsStride + lpart * 64);
+        for (int i = 0; i < NB; ++i) sl.rb[i] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16) + i);
+        sl.rz = zglob[g * N];
+        sl.rs[0] = sglob[0][g * N];
+        sl.rs[1] = sglob[1][g * N];
+    };
+    auto lstore = [&](const Slot &sl, int buf) {
+        uint8_t *A = lds + buf * S::LDS_STAGE;
+        uint8_t *B = A + S::LDS_A;
+        v4u *ad = reinterpret_cast<v4u *>(A + arow_l * kLdsStride + apart * S::A_BYTES);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const v4u v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-            bd[i] = bvalid ? v : zero;
+        for (int i = 0; i < NA; ++i) ad[i] = sl.ra[i];
+        const uint32_t zadd = zp_add_const(sl.rz);
+        v4u *bd = reinterpret_cast<v4u *>(B + bcol_l * kLdsStride + bpart * (2 * S::B_PACKED));
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const uint32_t d4[4] = {sl.rb[i].x, sl.rb[i].y, sl.rb[i].z, sl.rb[i].w};
+            uint32_t w[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) unpack8(d4[k], zadd, w[2 * k], w[2 * k + 1]);
+            bd[2 * i] = v4u{w[0], w[1], w[2], w[3]};
+            bd[2 * i + 1] = v4u{w[4], w[5], w[6], w[7]};
         }
     };
 
@@ -507,24 +683,10 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    gload(0);
-    lstore(0);
-    float sc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) sc[j] = svalid[j] ? half_bits_to_float(rs[j]) : 0.0f;
-    __syncthreads();
-
-    for (int64_t g = 0; g < G; ++g) {
-        const int buf = (int)(g & 1);
-        // prefetch the next group (past the end: the last group again, never consumed)
-        gload(g + 1 < G ? g + 1 : G - 1);
-        // keep the prefetch at the top: the scheduler would otherwise sink the loads
-        // next to their use in lstore and expose the full memory latency
-        __builtin_amdgcn_sched_barrier(0);
-
-        const uint8_t *A = lds + buf * 2 * kLdsTile;
-        const uint8_t *B = A + kLdsTile;
-        v16i d[2][2];
+    // the 16 MFMAs of one group: 4 independent accumulator chains, k-step outer
+    auto mfma_group = [&](int buf, v16i (&d)[2][2]) {
+        const uint8_t *A = lds + buf * S::LDS_STAGE;
+        const uint8_t *B = A + S::LDS_A;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -545,6 +707,9 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
 #pragma unroll
                 for (int j = 0; j < 2; ++j) d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], d[i][j], 0, 0, 0);
         }
+    };
+    // fold one group's int32 sums into the fp32 accumulators (or store them)
+    auto epilogue = [&](int64_t g, const v16i (&d)[2][2], const float (&sc)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -553,21 +718,51 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
                 for (int r = 0; r < 16; ++r) {
                     if (ISUMS) {
                         const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        if (m < rows.rows && svalid[j])
+                        if (m < rows.rows && scol[j] < N)
                             isums[(g * M_isums + rows.slot0 + m) * N + scol[j]] = d[i][j][r];
                     } else {
                         acc[i][j][r] = fmaf(sc[j], (float)d[i][j][r], acc[i][j][r]);
                     }
                 }
-        // unconditional: on the last group this rewrites the idle buffer with data
-        // nobody reads, which keeps the prefetch loads from being sunk below the MFMAs;
-        // fenced so that its waits on the prefetch are not hoisted above the MFMAs
+    };
+
+    // Per group g: issue the global loads of group g+2 into the free register slot,
+    // run the 16 MFMAs of group g from LDS (4 independent accumulator chains) and its
+    // fp32 epilogue, then write group g+1 (loaded one iteration earlier) into the idle
+    // LDS buffer and pass one barrier.  Each global load thus has a whole iteration
+    // of compute to arrive.  Unrolled by two so the slots stay in registers; indices
+    // past the end re-load the last group, whose copies are never consumed.
+    v16i d[2][2];
+    float sc[2];
+    gload(sa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(sb, G > 1 ? 1 : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(sa, 0);
+    sc[0] = half_bits_to_float(sa.rs[0]);
+    sc[1] = half_bits_to_float(sa.rs[1]);
+    __syncthreads();
+    auto body = [&](int64_t g, Slot &fill, const Slot &next) {
+        // compiler fences keep the prefetch where it is written (IR passes would
+        // otherwise merge it into the other half of the unrolled loop)
+        __asm__ volatile("" ::: "memory");
+        gload(fill, g + 2 < G ? g + 2 : G - 1);
+        __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        lstore(buf ^ 1);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) sc[j] = svalid[j] ? half_bits_to_float(rs[j]) : 0.0f;
+        mfma_group((int)(g & 1), d);
+        epilogue(g, d, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(next, (int)((g + 1) & 1));
+        sc[0] = half_bits_to_float(next.rs[0]);
+        sc[1] = half_bits_to_float(next.rs[1]);
         __syncthreads();
+    };
+    int64_t g = 0;
+    for (; g + 1 < G; g += 2) {
+        body(g, sa, sb);                 // group g from LDS; group g+1 (slot b) -> LDS
+        body(g + 1, sb, sa);             // group g+1 from LDS; group g+2 (slot a) -> LDS
     }
+    if (g < G) body(g, sa, sb);          // odd G: the last group
 
     if (!ISUMS) {
 #pragma unroll
@@ -582,30 +777,31 @@ __device__ __forceinline__ void tile_unit(uint8_t *lds, const int8_t *__restrict
                         const float as = a_scale[row];
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
-                            if (svalid[j]) out[slot * ldo + scol[j]] = as * acc[i][j][r];
+                            if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
                     }
                 }
             }
     }
 }
 
-template <bool ISUMS>
-__global__ __launch_bounds__(kTileThreads, 2) void gemm_tiled_kernel(const int8_t *__restrict__ qa,
-                                                                     const float *__restrict__ a_scale, int64_t M,
-                                                                     int64_t K, const uint8_t *__restrict__ packed,
-                                                                     const uint16_t *__restrict__ scale,
-                                                                     const uint16_t *__restrict__ zp, int64_t N,
-                                                                     float *__restrict__ out,
-                                                                     int32_t *__restrict__ isums) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kLdsTile];
-    const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
+template <int WM, int WN, bool ISUMS>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *__restrict__ qa,
+                                                                  const float *__restrict__ a_scale, int64_t M,
+                                                                  int64_t K, const uint8_t *__restrict__ packed,
+                                                                  const uint16_t *__restrict__ scale,
+                                                                  const uint16_t *__restrict__ zp, int64_t N,
+                                                                  float *__restrict__ out,
+                                                                  int32_t *__restrict__ isums) {
+    using S = TileShape<WM, WN>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    const int64_t mt = (M + S::BM - 1) / S::BM, nt = (N + S::BN - 1) / S::BN;
     const int64_t tile = xcd_tile(blockIdx.x, mt * nt);
     // m fastest inside an XCD's range: concurrently running tiles share weight columns
     const int64_t tm = tile % mt, tn = tile / mt;
-    const int64_t m0 = tm * BM;
-    const int rows = (int)((M - m0) < BM ? (M - m0) : BM);
-    tile_unit<ISUMS>(lds, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * BN, out, N, isums,
-                     M);
+    const int64_t m0 = tm * S::BM;
+    const int rows = (int)((M - m0) < S::BM ? (M - m0) : S::BM);
+    tile2_unit<WM, WN, ISUMS>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * S::BN,
+                              out, N, isums, M);
 }
 
 // ------------------------------------------------------------------ expert-grouped forms
@@ -697,33 +893,35 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
     }
 }
 
-__global__ __launch_bounds__(kTileThreads, 2) void grouped_tiled_kernel(
+template <int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
     float *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kLdsTile];
+    using S = TileShape<WM, WN>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
-    const int64_t ntn = (N + BN - 1) / BN;
-    const int64_t total = expert_prefix(E, pfx, kTileThreads, [&](int e) -> int64_t {
+    const int64_t ntn = (N + S::BN - 1) / S::BN;
+    const int64_t total = expert_prefix(E, pfx, S::THREADS, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return c > kSmallRows ? ((c + BM - 1) / BM) * ntn : 0;
+        return c > kSmallRows ? ((c + S::BM - 1) / S::BM) * ntn : 0;
     });
     const int64_t G = K / G128;
     for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
         const int e = find_expert(pfx, E, u);
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        const int64_t mt = (c + BM - 1) / BM;
+        const int64_t mt = (c + S::BM - 1) / S::BM;
         const int64_t local = u - pfx[e];
         const int64_t tm = local % mt, tn = local / mt;
-        const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * BM;
-        const int rows = (int)((c - tm * BM) < BM ? (c - tm * BM) : BM);
-        tile_unit<false>(lds, qa, a_scale, row_index, R, TileRows{s0, rows}, K, packed + (int64_t)e * N * (K / 2),
-                         scale + (int64_t)e * G * N, zp + (int64_t)e * G * N, N, tn * BN, out, N, nullptr, 0);
+        const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * S::BM;
+        const int rows = (int)((c - tm * S::BM) < S::BM ? (c - tm * S::BM) : S::BM);
+        tile2_unit<WM, WN, false>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
+                                  packed + (int64_t)e * N * (K / 2), scale + (int64_t)e * G * N,
+                                  zp + (int64_t)e * G * N, N, tn * S::BN, out, N, nullptr, 0);
         __syncthreads();  // the next unit reuses the LDS buffers
     }
 }
-
 
 #ifndef W4A8_STREAM_U1
 #define W4A8_STREAM_U1 2
@@ -768,6 +966,72 @@ hipError_t launch_stream2(int mt, int u, int split, const int8_t *qa, const floa
     return launch_stream2_s<4, 1>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
 }
 
+template <int WM, int WN>
+hipError_t launch_tiled(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                        const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
+                        hipStream_t stream) {
+    using S = TileShape<WM, WN>;
+    const int64_t tiles = ((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
+    const size_t lds = 2 * S::LDS_STAGE;
+    const dim3 grid((uint32_t)tiles), block(S::THREADS);
+    if (isums) {
+        if (hipFuncSetAttribute((const void *)gemm_tiled_kernel<WM, WN, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return hipGetLastError();
+        hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, true>), grid, block, lds, stream, qa, a_scale, M, K, packed,
+                           scale, zp, N, out, isums);
+    } else {
+        if (hipFuncSetAttribute((const void *)gemm_tiled_kernel<WM, WN, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return hipGetLastError();
+        hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, false>), grid, block, lds, stream, qa, a_scale, M, K, packed,
+                           scale, zp, N, out, isums);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                         const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
+                         hipStream_t stream) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipGetLastError();
+    const int64_t G = K / G128;
+    const int split = (G % 4 == 0) ? 2 : 1;
+    const int64_t ntiles = N / 16;
+    const int64_t tpw = (ntiles + cus - 1) / cus;
+    const int64_t nwg = (ntiles + tpw - 1) / tpw;
+    const int64_t red_bytes = (kDecWaves / split) * 4 * 64 * 4;
+    const size_t lds = (size_t)(((dec_lds_bytes(M, K) + 15) / 16) * 16 + red_bytes);
+    const int64_t nwin = G / 2 / split;
+    const dim3 grid((uint32_t)nwg), block(kDecThreads);
+#define W4A8_DEC(UU, SS)                                                                                            \
+    do {                                                                                                            \
+        if (isums) {                                                                                                \
+            if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, true>,                                 \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)            \
+                return hipGetLastError();                                                                           \
+            hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, true>), grid, block, lds, stream, qa, a_scale, M, K,     \
+                               packed, scale, zp, N, tpw, out, isums);                                              \
+        } else {                                                                                                    \
+            if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, false>,                                \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)            \
+                return hipGetLastError();                                                                           \
+            hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, false>), grid, block, lds, stream, qa, a_scale, M, K,    \
+                               packed, scale, zp, N, tpw, out, isums);                                              \
+        }                                                                                                           \
+    } while (0)
+    if (split == 2) {
+        if (nwin % 2 == 0) W4A8_DEC(2, 2);
+        else W4A8_DEC(1, 2);
+    } else {
+        if (nwin % 2 == 0) W4A8_DEC(2, 1);
+        else W4A8_DEC(1, 1);
+    }
+#undef W4A8_DEC
+    return hipGetLastError();
+}
+
 }  // namespace
 
 namespace w4a8 {
@@ -775,9 +1039,15 @@ namespace w4a8 {
 hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                        const uint16_t *scale, const uint16_t *zp, int64_t N, int path, float *out, int32_t *isums,
                        hipStream_t stream) {
+    // The debug entry has no scale array.  Kernels may load scale and zero point with
+    // one instruction (different lanes, same [G][N] shape), so they always get a valid
+    // pointer: the zero-point array stands in, and its values are never used as scales.
+    if (!scale) scale = zp;
     if (path == 1) {
         const int64_t G = K / G128;
         const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        if (G % 2 == 0 && M <= 16 && dec_lds_bytes(M, K) <= kDecLdsMax)
+            return launch_decode(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
         if (G % 2 == 0) {
             // line-wide loop: two-group windows, K split over two waves when it divides
             const int split = (G % 4 == 0) ? 2 : 1;
@@ -810,14 +1080,8 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
 #undef W4A8_STREAM
 #undef W4A8_STREAM_U
     } else {
-        const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        const dim3 grid((uint32_t)tiles), block(kTileThreads);
-        if (isums)
-            hipLaunchKernelGGL(gemm_tiled_kernel<true>, grid, block, 0, stream, qa, a_scale, M, K, packed, scale, zp,
-                               N, out, isums);
-        else
-            hipLaunchKernelGGL(gemm_tiled_kernel<false>, grid, block, 0, stream, qa, a_scale, M, K, packed, scale, zp,
-                               N, out, isums);
+        if (M > 128) return launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        return launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     }
     return hipGetLastError();
 }
@@ -842,8 +1106,13 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                            expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_tiled_kernel, dim3((uint32_t)(cus * 2)), dim3(kTileThreads), 0, stream, qa, a_scale, R,
-                       row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+    using S = TileShape<4, 2>;
+    const size_t lds = 2 * S::LDS_STAGE;
+    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<4, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+        return hipGetLastError();
+    hipLaunchKernelGGL((grouped_tiled_kernel<4, 2>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa, a_scale,
+                       R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     return hipGetLastError();
 }
 

@@ -69,6 +69,45 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const float *
     }
 }
 
+// Single-pass form for rows of K <= 4 * VPT4 * 1024 floats: one 1024-thread workgroup
+// per row keeps the row in registers between the maximum and the quantization, so
+// the row is read from memory once (this is the latency-critical small-M case).
+constexpr int kRowThreads = 1024;
+template <int VPT4>
+__global__ __launch_bounds__(kRowThreads) void quantize_act_row_kernel(const float *__restrict__ x, int64_t K,
+                                                                       int64_t ldx, int8_t *__restrict__ qa,
+                                                                       float *__restrict__ a_scale) {
+    __shared__ float red[kRowThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const float4 *row = reinterpret_cast<const float4 *>(x + m * ldx);
+    const int64_t K4 = K / 4;
+    float4 v[VPT4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT4; ++i) {
+        const int64_t c = threadIdx.x + (int64_t)i * kRowThreads;
+        v[i] = c < K4 ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+    amax = wave_max(amax);
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = red[0];
+#pragma unroll
+    for (int i = 1; i < kRowThreads / kWave; ++i) amax = fmaxf(amax, red[i]);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) a_scale[m] = s;
+    uint32_t *out = reinterpret_cast<uint32_t *>(qa + m * K);
+#pragma unroll
+    for (int i = 0; i < VPT4; ++i) {
+        const int64_t c = threadIdx.x + (int64_t)i * kRowThreads;
+        if (c < K4)
+            out[c] = pack4_i8(quantize_i8(v[i].x, s), quantize_i8(v[i].y, s), quantize_i8(v[i].z, s),
+                              quantize_i8(v[i].w, s));
+    }
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // One workgroup per row p of gu [P][2I]; h lives in registers between the max
@@ -168,6 +207,16 @@ namespace w4a8 {
 hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa, float *a_scale,
                                hipStream_t stream) {
     const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
+    if (vec && K <= 4 * 2 * kRowThreads) {
+        hipLaunchKernelGGL(quantize_act_row_kernel<2>, dim3((uint32_t)M), dim3(kRowThreads), 0, stream, x, K, ldx, qa,
+                           a_scale);
+        return hipGetLastError();
+    }
+    if (vec && K <= 4 * 4 * kRowThreads) {
+        hipLaunchKernelGGL(quantize_act_row_kernel<4>, dim3((uint32_t)M), dim3(kRowThreads), 0, stream, x, K, ldx, qa,
+                           a_scale);
+        return hipGetLastError();
+    }
     if (vec)
         hipLaunchKernelGGL(quantize_act_kernel<true>, dim3((uint32_t)M), dim3(kActThreads), 0, stream, x, K, ldx, qa,
                            a_scale);
