@@ -44,6 +44,104 @@ def quant_bytes(M, K):
     return 4 * M * K + M * K + 4 * M
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "gemm_decode_kernel.decode_K8192_N28672_M1-8-16.traffic.txt")
+DECODE_KERNEL = "gemm_decode_kernel"
+COPY_BYTES = 512 << 20
+KERNEL_SOURCES = ("w4a8_quantized_gemm_token_amd/csrc/gemm_kernels.hip",
+                  "w4a8_quantized_gemm_token_amd/csrc/w4a8_internal.hpp")
+
+
+def kernel_digest():
+    """sha256 over the GEMM kernel sources: a traffic figure taken from counters is only
+    reported while the kernels it was measured on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per decode-GEMM launch from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_digest():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_traffic(fetch_csv, write_csv, cmd):
+    """Text summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch):
+    the decode GEMM's per-launch figures, scaled by what the same counters read for one plain
+    512 MiB device copy."""
+    out = []
+    vals = {}
+    for label, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == label]
+        gem = [float(r["Counter_Value"]) for r in rows if DECODE_KERNEL in r["Kernel_Name"]]
+        cop = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not gem or not cop:
+            raise SystemExit(f"{path}: no {DECODE_KERNEL} or copy dispatch with {label}")
+        copy_kib, copy_name = max(cop)
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        vals[label] = (float(np.mean(gem)), len(gem), copy_kib, copy_name, factor)
+    f_kib, f_n, f_copy, copy_name, f_fac = vals["FETCH_SIZE"]
+    w_kib, w_n, w_copy, _, w_fac = vals["WRITE_SIZE"]
+    traffic = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
+    alg = float(np.mean([dense_bytes(M, N_DEC, K_DEC) for M in M_DEC]))
+    out.append(f"# HBM traffic of {DECODE_KERNEL}: decode W4A8 GEMM, K={K_DEC} N={N_DEC}, M=1,8,16 rotated")
+    out.append("# commands (run from /tmp with TMPDIR=/tmp; <repo> = the repository root):")
+    for c in cmd:
+        out.append("#   " + c)
+    out.append(f"# calibration kernel: {copy_name[:60]} copying {COPY_BYTES} bytes once")
+    out.append(f"kernel_sources_sha256: {kernel_digest()}")
+    out.append(f"gemm_dispatches: {f_n} (FETCH_SIZE run), {w_n} (WRITE_SIZE run)")
+    out.append(f"fetch_kib_per_launch_raw: {f_kib:.1f}")
+    out.append(f"write_kib_per_launch_raw: {w_kib:.1f}")
+    out.append(f"copy_fetch_kib_raw: {f_copy:.1f}")
+    out.append(f"copy_write_kib_raw: {w_copy:.1f}")
+    out.append(f"fetch_scale: {f_fac:.4f}")
+    out.append(f"write_scale: {w_fac:.4f}")
+    out.append(f"fetch_bytes_per_launch: {f_kib * 1024 * f_fac:.0f}")
+    out.append(f"write_bytes_per_launch: {w_kib * 1024 * w_fac:.0f}")
+    out.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+    out.append(f"algorithmic_bytes_per_launch: {alg:.0f}")
+    out.append(f"traffic_over_algorithmic: {traffic / alg:.4f}")
+    return "\n".join(out)
+
+
+def summarize_stats(stats_csv, cmd, top=12):
+    """Short text table of a rocprofv3 --kernel-trace --stats kernel summary."""
+    rows = _counter_rows(stats_csv)
+    out = ["# rocprofv3 kernel statistics", "# command (run from /tmp with TMPDIR=/tmp; <repo> = the repository root):"]
+    for c in cmd:
+        out.append("#   " + c)
+    out.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+    for r in rows[:top]:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("at::native::", "")
+        if name.startswith("void "):
+            name = name[5:]
+        short = name.split("(")[0][:70]
+        out.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                   f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>6.2f}  {short.strip()}")
+    return "\n".join(out)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -54,28 +152,12 @@ def parse():
     p.add_argument("--no-secondary", action="store_true", help="skip the prefill / MoE figures")
     p.add_argument("--profile-copy", action="store_true",
                    help="also launch one plain 512 MiB device copy (calibrates HBM counters)")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="print the traffic summary of two rocprofv3 --pmc counter_collection.csv files; no GPU")
+    p.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                   help="print a short table of a rocprofv3 kernel_stats.csv; no GPU")
+    p.add_argument("--cmd", action="append", default=[], help="command text recorded in a summary")
     return p.parse_args()
-
-
-class EventTimer:
-    """HIP events recorded on the stream the library launches on."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(self.torch.cuda.current_stream())
-        return e
-
-    def stop(self, s):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(self.torch.cuda.current_stream())
-        self.pairs.append((s, e))
-
-    def mean_ms(self):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
 
 
 def decode_setup(torch, w4, synthetic, copies):
@@ -93,38 +175,61 @@ def decode_setup(torch, w4, synthetic, copies):
 
 
 def run_decode(torch, w4, layers, xs, steps, warmup):
-    calls = [0]
-    gemm_timer = EventTimer(torch)
+    """Times `steps` decode steps, then the GEMM kernel alone.
 
-    def step(timed):
+    Each launch is prepared once (pointers marshalled), so the host stays ahead of the GPU and
+    kernels run back to back.  HIP event records are themselves queue packets that cost a few
+    microseconds each, so none sits between the kernels of a step; the GEMM's launch duration is
+    taken from one event pair around `steps` back-to-back GEMM launches per M (rotating weight
+    copies, activations from the step) on the same stream."""
+    dev = torch.device("cuda:0")
+    quant, gemms = {}, {}
+    for M in M_DEC:
+        qa = torch.empty((M, K_DEC), dtype=torch.int8, device=dev)
+        sc = torch.empty((M,), dtype=torch.float32, device=dev)
+        out = torch.empty((M, N_DEC), dtype=torch.float32, device=dev)
+        quant[M] = w4.prepare_quantize_act(xs[M], qa, sc)
+        gemms[M] = [w4.prepare_gemm(qa, sc, *layer, out) for layer in layers]
+    n_layers = len(layers)
+    stream = torch.cuda.current_stream()
+    calls = 0
+
+    def step():
+        nonlocal calls
         for M in M_DEC:
-            layer = layers[calls[0] % len(layers)]
-            calls[0] += 1
-            qa, sc = w4.quantize_act(xs[M])
-            if timed:
-                s = gemm_timer.start()
-            w4.gemm(qa, sc, *layer)
-            if timed:
-                gemm_timer.stop(s)
+            quant[M]()
+            gemms[M][calls % n_layers]()
+            calls += 1
 
     for _ in range(warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(True)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
     step_bytes = sum(dense_bytes(M, N_DEC, K_DEC) + quant_bytes(M, K_DEC) for M in M_DEC)
-    gemm_bytes = float(np.mean([dense_bytes(M, N_DEC, K_DEC) for M in M_DEC]))
-    gemm_ms = gemm_timer.mean_ms()
-    per_m = {}
-    for i, M in enumerate(M_DEC):
-        ms = float(np.mean([s.elapsed_time(e) for s, e in gemm_timer.pairs[i::len(M_DEC)]]))
+
+    per_m, launch_ms = {}, []
+    for M in M_DEC:
+        for i in range(n_layers):            # GPU busy when the start event is reached
+            gemms[M][i]()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for i in range(steps):
+            gemms[M][i % n_layers]()
+        e.record(stream)
+        e.synchronize()
+        ms = s.elapsed_time(e) / steps
+        launch_ms.append(ms)
         per_m[str(M)] = {"gemm_us": round(ms * 1e3, 2),
                          "GB/s": round(dense_bytes(M, N_DEC, K_DEC) / (ms * 1e-3) / 1e9, 1),
                          "TOPS": round(2 * M * N_DEC * K_DEC / (ms * 1e-3) / 1e12, 3)}
+    gemm_bytes = float(np.mean([dense_bytes(M, N_DEC, K_DEC) for M in M_DEC]))
+    gemm_ms = float(np.mean(launch_ms))
     return ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m
 
 
@@ -137,7 +242,7 @@ def cpu_baseline(synthetic):
     del W
     x = synthetic.activations_with_outlier_channels(0, 16, K_DEC)
     reps, t_total = 0, 0.0
-    while t_total < 10.0 and reps < 20:
+    while t_total < 12.0 and reps < 200:
         t0 = time.perf_counter()
         for M in M_DEC:
             qa, sc = orc.quantize_act(x[:M])
@@ -145,7 +250,7 @@ def cpu_baseline(synthetic):
         t_total += time.perf_counter() - t0
         reps += 1
     step_bytes = sum(dense_bytes(M, N_DEC, K_DEC) + quant_bytes(M, K_DEC) for M in M_DEC)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = orc.num_threads()
     return {"value": round(step_bytes * reps / t_total / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the full decode step (M=1,8,16; K=8192; N=28672), {reps} repetitions, "
@@ -166,13 +271,16 @@ def secondary(torch, w4, synthetic):
     qa, sc = w4.quantize_act(x)
     for _ in range(3):
         w4.gemm(qa, sc, *layer)
-    t = EventTimer(torch)
+    out_buf = torch.empty((M, N), dtype=torch.float32, device=dev)
+    launch = w4.prepare_gemm(qa, sc, *layer, out_buf)
+    stream = torch.cuda.current_stream()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
     for _ in range(10):
-        s = t.start()
-        w4.gemm(qa, sc, *layer)
-        t.stop(s)
+        launch()
+    e.record(stream)
     torch.cuda.synchronize()
-    ms = t.mean_ms()
+    ms = s.elapsed_time(e) / 10
     tops = 2 * M * N * K / (ms * 1e-3) / 1e12
     out["prefill_M4096_K8192_N8192"] = {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1),
                                         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
@@ -186,15 +294,19 @@ def secondary(torch, w4, synthetic):
     for T in (64, 4096):
         x = torch.from_numpy(synthetic.activations(0, T, H)).to(dev)
         logits = torch.from_numpy(synthetic.router_logits_skewed(0, T, E)).to(dev)
+        total, _ = w4.moe_ffn_workspace(T, H, I, E, k)
+        ws = torch.empty((total,), dtype=torch.uint8, device=dev)
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
         for _ in range(2):
-            w4.moe_ffn(x, logits, k, gate_up, down)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
+            _, inter = w4.moe_ffn(x, logits, k, gate_up, down, workspace=ws, out=y)
         reps = 5
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(torch.cuda.current_stream())
         for _ in range(reps):
-            _, inter = w4.moe_ffn(x, logits, k, gate_up, down)
+            w4.moe_ffn(x, logits, k, gate_up, down, workspace=ws, out=y)
+        e.record(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / reps
+        ms = s.elapsed_time(e) / reps
         counts = np.diff(inter["offsets"].cpu().numpy())
         touched = int((counts > 0).sum())
         wbytes = touched * (2 * I * H // 2 + 4 * 2 * I * H // GROUP + H * I // 2 + 4 * H * I // GROUP)
@@ -202,14 +314,22 @@ def secondary(torch, w4, synthetic):
         out[f"moe_ffn_T{T}"] = {"layer_us": round(ms * 1e3, 1), "experts_touched": touched,
                                 "weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
                                 "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)}
+        del ws, y, inter
+        torch.cuda.empty_cache()
     return out
 
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, args.cmd))
+        return
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats, args.cmd))
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer's multi-GPU sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding the layer over several GPUs is designed but not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -228,6 +348,7 @@ def main():
     del layers
     torch.cuda.empty_cache()
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic = read_traffic()
     achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -246,8 +367,8 @@ def main():
                                "M=1,8,16 per step (0.1% x20 weight outliers, 4 x50 activation channels)",
                    "weight_copies_rotated": args.copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemm_stream_kernel (streaming W4A8 GEMM)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "gemm_decode_kernel (decode W4A8 GEMM, activations staged in LDS)",
                      "bytes_per_launch": gemm_bytes, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "decode_per_M": per_m,
     }

@@ -68,10 +68,11 @@ typedef enum {
     W4A8_OK = 0,
     W4A8_EINVAL = 1,        /* bad pointer, size, alignment or value */
     W4A8_EUNSUPPORTED = 2,  /* valid request this library does not implement (e.g. group != 128) */
-    W4A8_EHIP = 3           /* a HIP runtime call or kernel launch failed */
+    W4A8_EHIP = 3,          /* a HIP runtime call or kernel launch failed */
+    W4A8_EWORKSPACE = 4     /* the caller's workspace is smaller than the call needs */
 } w4a8_status;
 
-#define W4A8_ABI_VERSION 1
+#define W4A8_ABI_VERSION 2
 #define W4A8_GROUP 128
 
 int w4a8_abi_version(void);
@@ -150,18 +151,25 @@ w4a8_status w4a8_gemm_path(const int8_t *qa, const float *a_scale, int64_t M, in
  * high precision and sends each token to its experts; [p4]: toy top-1 model).
  *   topk_ids[T][k]  the k largest logits per token, descending, ties -> lower id
  *   topk_w[T][k]    softmax over the k selected logits (fp32)
- *   expert_offsets[E+1]  exclusive scan of the per-expert pair counts
+ *   expert_offsets[E+1+with_shared]  exclusive scan of the per-expert pair
+ *                   counts; with with_shared = 1 a shared expert (index E) that
+ *                   every token visits follows: expert_offsets[E+1] = T*k + T
  *   perm[T*k]       pair indices p = t*k + j grouped by ascending expert and,
  *                   within an expert, ascending p ("slot" s holds pair perm[s])
+ *   slot_row[T*k + with_shared*T]  (may be NULL) the activation row of each
+ *                   slot: perm[s] / k for routed slots, s - T*k for the shared
+ *                   expert's slots -- the row_index of w4a8_moe_grouped_gemm
  *   slot_of_pair[T*k]  the inverse of perm
- * logits: device fp32 [T][E].  Requires 1 <= k <= min(E, 8), E <= 1024 and
- * T * k < 2^31.  With T == 0 only expert_offsets is written (all zeros) and the
- * other pointers may be NULL.  The bucketing runs in one workgroup, in chunks of pairs taken
- * in increasing p, which is what makes the order within an expert stable.
- * Errors: W4A8_EINVAL (null, T < 0, bad E/k). */
+ * logits: device fp32 [T][E].  Requires 1 <= k <= min(E, 8), E <= 1024,
+ * with_shared in {0, 1} and T*k + T < 2^31.  With T == 0 only expert_offsets is
+ * written (all zeros) and the other pointers may be NULL.  The bucketing runs in
+ * one workgroup, in chunks of pairs taken in increasing p, which is what makes
+ * the order within an expert stable.
+ * Errors: W4A8_EINVAL (null, T < 0, bad E/k/with_shared). */
 w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk,
-                           int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
-                           int32_t *perm, int32_t *slot_of_pair, hipStream_t stream);
+                           int32_t with_shared, int32_t *topk_ids, float *topk_w,
+                           int32_t *expert_offsets, int32_t *perm, int32_t *slot_row,
+                           int32_t *slot_of_pair, hipStream_t stream);
 
 /* Device.  Expert-grouped W4A8 GEMM.  Slots s in [expert_offsets[e],
  * expert_offsets[e+1]) belong to expert e; slot s multiplies activation row
@@ -197,6 +205,38 @@ w4a8_status w4a8_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t
 w4a8_status w4a8_moe_combine(const float *y, const int32_t *slot_of_pair, const float *topk_w,
                              const float *y_shared, int64_t T, int32_t topk, int64_t H,
                              float *out, hipStream_t stream);
+
+/* ------------------------------------------------------------ MoE FFN layer */
+
+/* The whole expert FFN of one MoE layer in one call (the composition the
+ * entry points above provide, [p1 §5.1-§5.3]: route in high precision, quantize
+ * the tokens once, group them by expert, run the experts' W4A8 products):
+ *   1. w4a8_moe_route (with_shared = 1)          logits [T][E]
+ *   2. w4a8_quantize_act                         x [T][H] -> qa, a_scale
+ *   3. w4a8_moe_grouped_gemm, E+1 experts        gate/up weights [E+1][2I][H/2]
+ *   4. w4a8_silu_mul_quantize                    gu [S][2I] -> qh [S][I], h_scale
+ *   5. w4a8_moe_grouped_gemm, E+1 experts        down weights [E+1][H][I/2]
+ *   6. w4a8_moe_combine (y_shared = the shared expert's rows)  -> out [T][H]
+ * with S = T*k + T slots (routed pairs, then one shared slot per token).
+ * Expert E of each weight stack is the shared expert.  The intermediates live in
+ * the caller's workspace (device memory, at least w4a8_moe_ffn_workspace_size
+ * bytes, 256-byte aligned); w4a8_moe_ffn_workspace_layout gives each part's byte
+ * offset in it (enum w4a8_moe_ws_part order), so a caller can read any stage.
+ * Errors: as the steps, W4A8_EINVAL for H or I not multiples of 128 and for a
+ * misaligned workspace, W4A8_EWORKSPACE when ws_bytes is too small. */
+enum w4a8_moe_ws_part {
+    W4A8_WS_TOPK_IDS = 0, W4A8_WS_TOPK_W, W4A8_WS_OFFSETS, W4A8_WS_PERM, W4A8_WS_SLOT_ROW,
+    W4A8_WS_SLOT_OF_PAIR, W4A8_WS_QA, W4A8_WS_A_SCALE, W4A8_WS_GU, W4A8_WS_QH, W4A8_WS_H_SCALE,
+    W4A8_WS_Y, W4A8_WS_PARTS
+};
+size_t      w4a8_moe_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk);
+w4a8_status w4a8_moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk,
+                                          int64_t *offsets /* [W4A8_WS_PARTS + 1], host */);
+w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t H, int64_t I,
+                         int32_t E, int32_t topk,
+                         const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
+                         const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp,
+                         float *out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,8 @@ class Oracle:
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         i32 = ctypes.c_int32
+        lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_num_threads.argtypes = []
         lib.orc_f32_to_f16.restype = ctypes.c_uint16
         lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
         lib.orc_f16_to_f32.restype = ctypes.c_float
@@ -86,6 +88,10 @@ class Oracle:
         self.lib = lib
 
     # --------------------------------------------------------------------------- fp16
+    def num_threads(self) -> int:
+        """Host threads the oracle's parallel loops run on."""
+        return int(self.lib.orc_num_threads())
+
     def f32_to_f16_bits(self, x) -> np.ndarray:
         """fp32 -> fp16 bit pattern, round to nearest even (binary16 definition)."""
         lib = self.lib

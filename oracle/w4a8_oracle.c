@@ -38,6 +38,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format's definition:    */
@@ -394,3 +395,6 @@ void orc_combine(const float *y, const int32_t *slot_of_pair, const float *w, co
             out[t * H + c] = acc;
         }
 }
+
+/* Number of host threads the parallel loops above use (OpenMP's team size). */
+int orc_num_threads(void) { return omp_get_max_threads(); }

@@ -14,7 +14,7 @@ import w4a8_quantized_gemm_token_amd as w4
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a8.h")
 
-EINVAL, EUNSUPPORTED = 1, 2
+EINVAL, EUNSUPPORTED, EWORKSPACE = 1, 2, 4
 
 
 def header_functions():
@@ -30,7 +30,8 @@ def test_library_exports_every_header_function():
     for name in names:
         assert hasattr(lib, name), f"{name} declared in w4a8.h but not exported"
     assert sorted(w4.EXPORTS) == names
-    assert lib.w4a8_abi_version() == 1
+    version = int(re.search(r"#define W4A8_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.w4a8_abi_version() == version == w4.ABI_VERSION
     assert lib.w4a8_status_str(2) == b"unsupported"
 
 
@@ -70,9 +71,10 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_quantize_act(f, 4, 250, 256, f, f, None) == EINVAL
     assert lib.w4a8_quantize_act(f, 0, 256, 256, f, f, None) == 0
     # router
-    assert lib.w4a8_moe_route(f, 4, 8, 9, f, f, f, f, f, None) == EINVAL
-    assert lib.w4a8_moe_route(f, 4, 2000, 8, f, f, f, f, f, None) == EINVAL
-    assert lib.w4a8_moe_route(f, 4, 8, 0, f, f, f, f, f, None) == EINVAL
+    assert lib.w4a8_moe_route(f, 4, 8, 9, 0, f, f, f, f, f, f, None) == EINVAL
+    assert lib.w4a8_moe_route(f, 4, 2000, 8, 0, f, f, f, f, f, f, None) == EINVAL
+    assert lib.w4a8_moe_route(f, 4, 8, 0, 0, f, f, f, f, f, f, None) == EINVAL
+    assert lib.w4a8_moe_route(f, 4, 8, 2, 2, f, f, f, f, f, f, None) == EINVAL
     # grouped gemm
     assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, None, 8, 256, f, f, f, 128, 128, 16, f, None) == EINVAL
     assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 0, 256, f, f, f, 128, 128, 16, f, None) == EINVAL
@@ -83,6 +85,32 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_moe_combine(f, f, f, None, 4, 0, 128, f, None) == EINVAL
     # device packer sizes
     assert lib.w4a8_pack_weights_device(f, 128, 200, 128, f, f, f, None) == EINVAL
+    # MoE FFN layer: sizes, workspace alignment and size
+    need = lib.w4a8_moe_ffn_workspace_size(64, 7168, 2048, 384, 8)
+    assert need > 0
+    assert lib.w4a8_moe_ffn_workspace_size(64, 7100, 2048, 384, 8) == 0
+    args = (f, f, 64, 7168, 2048, 384, 8, f, f, f, f, f, f, f)
+    assert lib.w4a8_moe_ffn(*args, f, need - 1, None) == EWORKSPACE
+    assert lib.w4a8_moe_ffn(*args, _fake(4096 + 64), need, None) == EINVAL
+    assert lib.w4a8_moe_ffn(f, f, 64, 7168, 2048, 384, 9, f, f, f, f, f, f, f, f, need, None) == EINVAL
+    assert lib.w4a8_moe_ffn(f, f, 64, 7168, 2048, 1024, 8, f, f, f, f, f, f, f, f, need, None) == EINVAL
+
+
+def test_moe_ffn_workspace_layout():
+    """Parts in enum order, 256-byte aligned, each at least its tensor's size, total = size query."""
+    T, H, I, E, k = 64, 7168, 2048, 384, 8
+    total, parts = w4.moe_ffn_workspace(T, H, I, E, k)
+    assert total == w4.load().w4a8_moe_ffn_workspace_size(T, H, I, E, k)
+    P, S = T * k, T * k + T
+    need = {"ids": 4 * P, "w": 4 * P, "offsets": 4 * (E + 2), "perm": 4 * P, "row_index": 4 * S,
+            "slot_of_pair": 4 * P, "qa": T * H, "a_scale": 4 * T, "gu": 4 * S * 2 * I, "qh": S * I,
+            "h_scale": 4 * S, "y": 4 * S * H}
+    last_end = 0
+    for name in w4.WS_PARTS:
+        off, size = parts[name]
+        assert off % 256 == 0 and off >= last_end and size >= need[name], name
+        last_end = off + need[name]
+    assert last_end <= total
 
 
 def test_host_packer_rejects_bad_weights():

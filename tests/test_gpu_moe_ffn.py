@@ -87,6 +87,10 @@ def test_moe_ffn_small_all_tokens(orc):
             cache_d[e] = orc.quantize_weights(synthetic.weights(3, synthetic.TAG_W_DOWN, e, H, I))
         return cache_d[e]
 
+    off_r, perm_r = orc.bucket(ids_r, E)
+    assert np.array_equal(to_host(inter["perm"]), perm_r)
+    assert np.array_equal(to_host(inter["offsets"]), np.concatenate([off_r, [T * k + T]]))
+    assert np.array_equal(to_host(inter["row_index"]), np.concatenate([perm_r // k, np.arange(T)]))
     # first GEMM integer stage: activation codes bit-exact
     qa_r, sa_r = orc.quantize_act(x)
     assert np.array_equal(to_host(inter["qa"]), qa_r)

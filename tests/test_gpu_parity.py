@@ -267,7 +267,7 @@ def test_prefill_full_size_sampled(orc):
 def test_route_bit_exact(orc, T, E, k, kind):
     w4 = w4mod()
     logits = (synthetic.router_logits_iid(7, T, E) if kind == "iid" else synthetic.router_logits_skewed(0, T, E))
-    ids, w, off, perm, sop = (to_host(t) for t in w4.moe_route(to_dev(logits).reshape(T, E), k))
+    ids, w, off, perm, rows, sop = (to_host(t) for t in w4.moe_route(to_dev(logits).reshape(T, E), k))
     ids_r, w_r = orc.route_topk(logits.reshape(T, E), k)
     off_r, perm_r = orc.bucket(ids_r, E)
     assert np.array_equal(ids, ids_r)
@@ -276,13 +276,14 @@ def test_route_bit_exact(orc, T, E, k, kind):
     inv = np.empty_like(perm_r)
     inv[perm_r] = np.arange(len(perm_r), dtype=np.int32)
     assert np.array_equal(sop, inv)
+    assert np.array_equal(rows, perm_r // k)
 
 
 def test_route_ties_go_to_lower_expert():
     w4 = w4mod()
     logits = np.zeros((3, 16), np.float32)
     logits[1, [3, 9, 12]] = 2.0
-    ids, w, off, perm, sop = (to_host(t) for t in w4.moe_route(to_dev(logits), 2))
+    ids, w, off, perm, rows, sop = (to_host(t) for t in w4.moe_route(to_dev(logits), 2))
     assert ids[0].tolist() == [0, 1] and ids[1].tolist() == [3, 9] and ids[2].tolist() == [0, 1]
     assert np.allclose(w, 0.5)
 
@@ -329,9 +330,8 @@ def test_toy_moe_full_size_sampled(orc, B):
     packed, scale, zp = device_experts(0, synthetic.TAG_W, E, N, K)
     logits = synthetic.router_logits_iid(100 + B, B, E)
     x = synthetic.activations(100 + B, B, K)
-    ids, w, off, perm, sop = w4.moe_route(to_dev(logits), 1)
+    ids, w, off, perm, row_index, sop = w4.moe_route(to_dev(logits), 1)
     qa, sc = w4.quantize_act(to_dev(x))
-    row_index = (perm // 1).to(torch.int32).contiguous()
     y = w4.moe_grouped_gemm(qa, sc, row_index, off, packed, scale, zp, max_slots=B)
     out = to_host(w4.moe_combine(y, sop, w))
     ids_r, w_r = orc.route_topk(logits, 1)

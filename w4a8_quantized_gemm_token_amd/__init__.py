@@ -16,6 +16,7 @@ import os
 import numpy as np
 
 GROUP = 128
+ABI_VERSION = 2          # W4A8_ABI_VERSION of the header this binding follows
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
@@ -25,7 +26,11 @@ EXPORTS = (
     "w4a8_pack_weights", "w4a8_pack_weights_device", "w4a8_unpack_weights",
     "w4a8_quantize_act", "w4a8_gemm", "w4a8_gemm_debug_isums", "w4a8_gemm_path",
     "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_silu_mul_quantize", "w4a8_moe_combine",
+    "w4a8_moe_ffn_workspace_size", "w4a8_moe_ffn_workspace_layout", "w4a8_moe_ffn",
 )
+# order of the parts of the MoE FFN workspace (enum w4a8_moe_ws_part)
+WS_PARTS = ("ids", "w", "offsets", "perm", "row_index", "slot_of_pair", "qa", "a_scale", "gu", "qh",
+            "h_scale", "y")
 
 _lib = None
 
@@ -57,16 +62,21 @@ def load() -> ctypes.CDLL:
         "w4a8_gemm": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, p, p]),
         "w4a8_gemm_debug_isums": (ctypes.c_int, [p, i64, i64, p, p, i64, i32, i32, p, p]),
         "w4a8_gemm_path": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, i32, p, p]),
-        "w4a8_moe_route": (ctypes.c_int, [p, i64, i32, i32, p, p, p, p, p, p]),
+        "w4a8_moe_route": (ctypes.c_int, [p, i64, i32, i32, i32, p, p, p, p, p, p, p]),
         "w4a8_moe_grouped_gemm": (ctypes.c_int, [p, p, i64, p, p, i32, i64, p, p, p, i64, i32, i64, p, p]),
         "w4a8_silu_mul_quantize": (ctypes.c_int, [p, i64, i64, p, p, p, p]),
         "w4a8_moe_combine": (ctypes.c_int, [p, p, p, p, i64, i32, i64, p, p]),
+        "w4a8_moe_ffn_workspace_size": (sz, [i64, i64, i64, i32, i32]),
+        "w4a8_moe_ffn_workspace_layout": (ctypes.c_int, [i64, i64, i64, i32, i32, p]),
+        "w4a8_moe_ffn": (ctypes.c_int, [p, p, i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    del sz
+    if lib.w4a8_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.w4a8_abi_version()}, this binding needs {ABI_VERSION}: "
+                          "rebuild it")
     _lib = lib
     return lib
 
@@ -79,6 +89,26 @@ def _check(fn: str, status: int):
 
 def _call(name: str, *args):
     _check(name, getattr(load(), name)(*args))
+
+
+class Launch:
+    """One library call with its arguments marshalled once (device pointers, sizes and the
+    stream current at preparation time).  Calling it re-issues the call with no per-call
+    Python work beyond the ctypes dispatch; the tensors it was prepared from must stay alive.
+    Raises W4A8Error on a non-zero status."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name = name
+        self.fn = getattr(load(), name)
+        self.args = args
+        self.keep = keep
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != 0:
+            _check(self.name, status)
 
 
 # ----------------------------------------------------------------- torch plumbing
@@ -182,6 +212,24 @@ def gemm(qa, a_scale, packed, scale, zp, path: int = 0, out=None, group: int = G
     return out
 
 
+def prepare_quantize_act(x, qa, a_scale) -> Launch:
+    """Prepared w4a8_quantize_act writing into preallocated qa int8 [M][K] and a_scale float32 [M]."""
+    M, K = x.shape
+    assert tuple(qa.shape) == (M, K) and tuple(a_scale.shape) == (M,)
+    return Launch("w4a8_quantize_act", (_dev_rows_ptr(x), M, K, x.stride(0), _dev_ptr(qa), _dev_ptr(a_scale),
+                                        _stream(x.device)), (x, qa, a_scale))
+
+
+def prepare_gemm(qa, a_scale, packed, scale, zp, out, group: int = GROUP) -> Launch:
+    """Prepared w4a8_gemm writing into a preallocated out float32 [M][N]."""
+    M, K = qa.shape
+    N = packed.shape[0]
+    assert tuple(out.shape) == (M, N)
+    return Launch("w4a8_gemm", (_dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(packed), _dev_ptr(scale),
+                                _dev_ptr(zp), N, group, _dev_ptr(out), _stream(qa.device)),
+                  (qa, a_scale, packed, scale, zp, out))
+
+
 def gemm_debug_isums(qa, packed, zp, path: int = 0, group: int = GROUP):
     """int32 [K/128][M][N] per-group integer sums (test aid)."""
     torch = _torch()
@@ -200,18 +248,22 @@ def linear(x, packed, scale, zp, path: int = 0):
 
 
 # ----------------------------------------------------------------- MoE
-def moe_route(logits, topk: int):
-    """-> (ids [T][k] i32, w [T][k] f32, offsets [E+1] i32, perm [T*k] i32, slot_of_pair [T*k] i32)."""
+def moe_route(logits, topk: int, with_shared: bool = False):
+    """-> (ids [T][k] i32, w [T][k] f32, offsets [E+1(+1)] i32, perm [T*k] i32,
+    row_index [T*k(+T)] i32, slot_of_pair [T*k] i32).  with_shared appends a shared expert
+    (index E) visited by every token; row_index is the activation row of each slot."""
     torch = _torch()
     T, E = logits.shape
+    sh = 1 if with_shared else 0
     ids = _empty((T, topk), torch.int32, logits)
     w = _empty((T, topk), torch.float32, logits)
-    off = _empty((E + 1,), torch.int32, logits)
+    off = _empty((E + 1 + sh,), torch.int32, logits)
     perm = _empty((T * topk,), torch.int32, logits)
+    rows = _empty((T * topk + sh * T,), torch.int32, logits)
     sop = _empty((T * topk,), torch.int32, logits)
-    _call("w4a8_moe_route", _dev_ptr(logits), T, E, topk, _dev_ptr(ids), _dev_ptr(w), _dev_ptr(off),
-          _dev_ptr(perm), _dev_ptr(sop), _stream(logits.device))
-    return ids, w, off, perm, sop
+    _call("w4a8_moe_route", _dev_ptr(logits), T, E, topk, sh, _dev_ptr(ids), _dev_ptr(w), _dev_ptr(off),
+          _dev_ptr(perm), _dev_ptr(rows), _dev_ptr(sop), _stream(logits.device))
+    return ids, w, off, perm, rows, sop
 
 
 def moe_grouped_gemm(qa, a_scale, row_index, offsets, packed, scale, zp, max_slots: int, out=None,
@@ -252,27 +304,42 @@ def moe_combine(y, slot_of_pair, topk_w, y_shared=None, out=None):
     return out
 
 
-def moe_ffn(x, logits, topk: int, gate_up, down, max_routed: int | None = None):
-    """One MoE FFN layer: route -> quantize x -> gate/up grouped GEMM (routed experts plus a
-    shared expert stored at index E) -> silu*up + INT8 requant -> down grouped GEMM -> combine.
+def moe_ffn_workspace(T: int, H: int, I: int, E: int, topk: int):
+    """(total bytes, {part name: (byte offset, byte size)}) of the MoE FFN workspace."""
+    lib = load()
+    offs = (ctypes.c_int64 * (len(WS_PARTS) + 1))()
+    _check("w4a8_moe_ffn_workspace_layout", lib.w4a8_moe_ffn_workspace_layout(T, H, I, E, topk, offs))
+    parts = {name: (offs[i], offs[i + 1] - offs[i]) for i, name in enumerate(WS_PARTS)}
+    return offs[len(WS_PARTS)], parts
+
+
+def moe_ffn(x, logits, topk: int, gate_up, down, workspace=None, out=None):
+    """One MoE FFN layer in one library call (w4a8_moe_ffn): route (+ shared expert at index E)
+    -> quantize x -> gate/up grouped GEMM -> silu*up + INT8 requant -> down grouped GEMM -> combine.
 
     gate_up = (packed [E+1][2I][H/2], scale, zp); down = (packed [E+1][H][I/2], scale, zp).
-    Returns (out [T][H] float32, intermediates dict)."""
+    Returns (out [T][H] float32, intermediates: views of the workspace)."""
     torch = _torch()
     T, H = x.shape
     E = logits.shape[1]
-    ids, w, off, perm, sop = moe_route(logits, topk)
-    P = T * topk
-    S = P + T
-    # slots [0, P): routed pairs in expert order (row = token of pair perm[s]);
-    # slots [P, P+T): the shared expert, row = token t
-    row_index = torch.cat([torch.div(perm, topk, rounding_mode="floor"),
-                           torch.arange(T, dtype=torch.int32, device=x.device)]).to(torch.int32).contiguous()
-    offsets = torch.cat([off, (off[-1:] + T)]).contiguous()
-    qa, sc = quantize_act(x)
-    gu = moe_grouped_gemm(qa, sc, row_index, offsets, *gate_up, max_slots=S)
-    qh, hs = silu_mul_quantize(gu)
-    y = moe_grouped_gemm(qh, hs, None, offsets, *down, max_slots=S)
-    out = moe_combine(y, sop, w, y_shared=y[P:])
-    return out, dict(ids=ids, w=w, offsets=offsets, perm=perm, slot_of_pair=sop, row_index=row_index,
-                     qa=qa, a_scale=sc, gu=gu, qh=qh, h_scale=hs, y=y)
+    I = gate_up[0].shape[1] // 2
+    total, parts = moe_ffn_workspace(T, H, I, E, topk)
+    if workspace is None:
+        workspace = torch.empty((total,), dtype=torch.uint8, device=x.device)
+    assert workspace.numel() >= total and workspace.data_ptr() % 256 == 0, "workspace too small or misaligned"
+    if out is None:
+        out = _empty((T, H), torch.float32, x)
+    _call("w4a8_moe_ffn", _dev_ptr(x), _dev_ptr(logits), T, H, I, E, topk, _dev_ptr(gate_up[0]),
+          _dev_ptr(gate_up[1]), _dev_ptr(gate_up[2]), _dev_ptr(down[0]), _dev_ptr(down[1]), _dev_ptr(down[2]),
+          _dev_ptr(out), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(x.device))
+    P, S = T * topk, T * topk + T
+    shapes = {"ids": ((T, topk), torch.int32), "w": ((T, topk), torch.float32), "offsets": ((E + 2,), torch.int32),
+              "perm": ((P,), torch.int32), "row_index": ((S,), torch.int32), "slot_of_pair": ((P,), torch.int32),
+              "qa": ((T, H), torch.int8), "a_scale": ((T,), torch.float32), "gu": ((S, 2 * I), torch.float32),
+              "qh": ((S, I), torch.int8), "h_scale": ((S,), torch.float32), "y": ((S, H), torch.float32)}
+    inter = {}
+    for name, (shape, dt) in shapes.items():
+        o, _ = parts[name]
+        n = int(np.prod(shape)) * torch.empty((), dtype=dt).element_size()
+        inter[name] = workspace[o:o + n].view(dt).view(shape)
+    return out, inter

@@ -118,6 +118,7 @@ const char *w4a8_status_str(int status) {
     case W4A8_EINVAL: return "invalid argument";
     case W4A8_EUNSUPPORTED: return "unsupported";
     case W4A8_EHIP: return "HIP error";
+    case W4A8_EWORKSPACE: return "workspace too small";
     default: return "unknown status";
     }
 }
@@ -237,18 +238,20 @@ w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K, const 
     return gemm_common(qa, nullptr, M, K, packed, nullptr, zp, N, group, path, nullptr, isums, stream);
 }
 
-w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t *topk_ids, float *topk_w,
-                           int32_t *expert_offsets, int32_t *perm, int32_t *slot_of_pair, hipStream_t stream) {
+w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared,
+                           int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *perm,
+                           int32_t *slot_row, int32_t *slot_of_pair, hipStream_t stream) {
     clear_error();
     W4A8_REQUIRE(expert_offsets && (T == 0 || (logits && topk_ids && topk_w && perm && slot_of_pair)), W4A8_EINVAL,
                  "null pointer");
     W4A8_REQUIRE(T >= 0, W4A8_EINVAL, "T=%lld must be >= 0", (long long)T);
     W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
     W4A8_REQUIRE(topk >= 1 && topk <= 8 && topk <= E, W4A8_EINVAL, "topk=%d must be in [1, min(E, 8)]", (int)topk);
-    W4A8_REQUIRE(T * topk < (1ll << 31), W4A8_EINVAL, "T*topk too large");
-    return hip_status(
-        launch_moe_route(logits, T, E, topk, topk_ids, topk_w, expert_offsets, perm, slot_of_pair, stream),
-        "moe_route launch");
+    W4A8_REQUIRE(with_shared == 0 || with_shared == 1, W4A8_EINVAL, "with_shared=%d must be 0 or 1", (int)with_shared);
+    W4A8_REQUIRE(T * (topk + 1) < (1ll << 31), W4A8_EINVAL, "T*(topk+1) too large");
+    return hip_status(launch_moe_route(logits, T, E, topk, with_shared, topk_ids, topk_w, expert_offsets, perm,
+                                       slot_row, slot_of_pair, stream),
+                      "moe_route launch");
 }
 
 w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
@@ -289,6 +292,113 @@ w4a8_status w4a8_moe_combine(const float *y, const int32_t *slot_of_pair, const 
     W4A8_REQUIRE(T < (1ll << 31), W4A8_EINVAL, "T too large");
     return hip_status(launch_moe_combine(y, slot_of_pair, topk_w, y_shared, T, topk, H, out, stream),
                       "moe_combine launch");
+}
+
+// ------------------------------------------------------------------ MoE FFN layer
+namespace {
+
+constexpr int64_t kWsAlign = 256;
+
+int64_t ws_round(int64_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// byte offsets of the workspace parts; off[W4A8_WS_PARTS] = total size
+void ws_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk, int64_t *off) {
+    const int64_t P = T * topk, S = P + T;
+    const int64_t bytes[W4A8_WS_PARTS] = {
+        4 * P,            // topk ids
+        4 * P,            // topk weights
+        4 * (E + 2),      // offsets (E routed + shared)
+        4 * P,            // perm
+        4 * S,            // slot_row
+        4 * P,            // slot_of_pair
+        T * H,            // qa
+        4 * T,            // a_scale
+        4 * S * 2 * I,    // gate/up output
+        S * I,            // qh
+        4 * S,            // h_scale
+        4 * S * H,        // down output
+    };
+    int64_t o = 0;
+    for (int i = 0; i < W4A8_WS_PARTS; ++i) {
+        off[i] = o;
+        o += ws_round(bytes[i]);
+    }
+    off[W4A8_WS_PARTS] = o;
+}
+
+w4a8_status check_ffn_sizes(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk) {
+    W4A8_REQUIRE(T >= 0 && H > 0 && I > 0 && H % W4A8_GROUP == 0 && I % W4A8_GROUP == 0, W4A8_EINVAL,
+                 "bad sizes T=%lld H=%lld I=%lld (H and I must be positive multiples of 128)", (long long)T,
+                 (long long)H, (long long)I);
+    W4A8_REQUIRE(E > 0 && E + 1 <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1023]", (int)E);
+    W4A8_REQUIRE(topk >= 1 && topk <= 8 && topk <= E, W4A8_EINVAL, "topk=%d must be in [1, min(E, 8)]", (int)topk);
+    W4A8_REQUIRE(T * (topk + 1) < (1ll << 31) && T * (topk + 1) * 2 * I < (1ll << 40), W4A8_EINVAL,
+                 "T=%lld too large", (long long)T);
+    return W4A8_OK;
+}
+
+}  // namespace
+
+size_t w4a8_moe_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk) {
+    if (check_ffn_sizes(T, H, I, E, topk) != W4A8_OK) return 0;
+    int64_t off[W4A8_WS_PARTS + 1];
+    ws_layout(T, H, I, E, topk, off);
+    return (size_t)off[W4A8_WS_PARTS];
+}
+
+w4a8_status w4a8_moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk, int64_t *offsets) {
+    clear_error();
+    W4A8_REQUIRE(offsets, W4A8_EINVAL, "null pointer");
+    if (w4a8_status st = check_ffn_sizes(T, H, I, E, topk)) return st;
+    ws_layout(T, H, I, E, topk, offsets);
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t H, int64_t I, int32_t E,
+                         int32_t topk, const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
+                         const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp, float *out,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    if (w4a8_status st = check_ffn_sizes(T, H, I, E, topk)) return st;
+    W4A8_REQUIRE(workspace && (T == 0 || (x && logits && out)), W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(gu_packed && gu_scale && gu_zp && dn_packed && dn_scale && dn_zp, W4A8_EINVAL, "null weight pointer");
+    W4A8_REQUIRE(((uintptr_t)workspace % kWsAlign) == 0, W4A8_EINVAL, "workspace must be 256-byte aligned");
+    W4A8_REQUIRE(aligned16(gu_packed) && aligned16(dn_packed) && (T == 0 || (aligned16(x) && aligned16(out))),
+                 W4A8_EINVAL, "x, out and packed weights must be 16-byte aligned");
+    int64_t off[W4A8_WS_PARTS + 1];
+    ws_layout(T, H, I, E, topk, off);
+    W4A8_REQUIRE((int64_t)ws_bytes >= off[W4A8_WS_PARTS], W4A8_EWORKSPACE, "workspace of %zu bytes, %lld needed",
+                 ws_bytes, (long long)off[W4A8_WS_PARTS]);
+    char *ws = (char *)workspace;
+    int32_t *ids = (int32_t *)(ws + off[W4A8_WS_TOPK_IDS]);
+    float *w = (float *)(ws + off[W4A8_WS_TOPK_W]);
+    int32_t *offsets = (int32_t *)(ws + off[W4A8_WS_OFFSETS]);
+    int32_t *perm = (int32_t *)(ws + off[W4A8_WS_PERM]);
+    int32_t *slot_row = (int32_t *)(ws + off[W4A8_WS_SLOT_ROW]);
+    int32_t *sop = (int32_t *)(ws + off[W4A8_WS_SLOT_OF_PAIR]);
+    int8_t *qa = (int8_t *)(ws + off[W4A8_WS_QA]);
+    float *a_scale = (float *)(ws + off[W4A8_WS_A_SCALE]);
+    float *gu = (float *)(ws + off[W4A8_WS_GU]);
+    int8_t *qh = (int8_t *)(ws + off[W4A8_WS_QH]);
+    float *h_scale = (float *)(ws + off[W4A8_WS_H_SCALE]);
+    float *y = (float *)(ws + off[W4A8_WS_Y]);
+    const int64_t P = T * topk, S = P + T;
+    hipError_t err = launch_moe_route(logits, T, E, topk, 1, ids, w, offsets, perm, slot_row, sop, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_ffn: route");
+    if (T == 0) return W4A8_OK;
+    if ((err = launch_quantize_act(x, T, H, H, qa, a_scale, stream)) != hipSuccess)
+        return hip_status(err, "moe_ffn: quantize");
+    if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S,
+                                   gu, stream)) != hipSuccess)
+        return hip_status(err, "moe_ffn: gate/up grouped GEMM");
+    if ((err = launch_silu_mul_quantize(gu, S, I, qh, h_scale, nullptr, stream)) != hipSuccess)
+        return hip_status(err, "moe_ffn: silu*up requant");
+    if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E + 1, I, dn_packed, dn_scale, dn_zp, H, S, y,
+                                   stream)) != hipSuccess)
+        return hip_status(err, "moe_ffn: down grouped GEMM");
+    if ((err = launch_moe_combine(y, sop, w, y + P * H, T, topk, H, out, stream)) != hipSuccess)
+        return hip_status(err, "moe_ffn: combine");
+    return W4A8_OK;
 }
 
 }  // extern "C"

@@ -94,9 +94,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
 constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / kWave;
 
+// shared_T > 0 appends a shared expert (index E) whose T slots follow the routed
+// ones: offsets[E+1] = P + T, and slot P + t reads activation row t.
 __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *__restrict__ ids, int64_t P, int32_t E,
+                                                                int32_t k, int64_t shared_T,
                                                                 int32_t *__restrict__ offsets,
                                                                 int32_t *__restrict__ perm,
+                                                                int32_t *__restrict__ slot_row,
                                                                 int32_t *__restrict__ slot_of_pair) {
     __shared__ int32_t count[kMaxE];
     __shared__ int32_t base[kMaxE];      // offsets[e] + pairs of e already placed
@@ -124,7 +128,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *_
         base[tid] = excl;
         offsets[tid] = excl;
     }
-    if (tid == 0) offsets[E] = scan[kBucketThreads - 1];
+    if (tid == 0) {
+        offsets[E] = scan[kBucketThreads - 1];
+        if (shared_T > 0) offsets[E + 1] = scan[kBucketThreads - 1] + (int32_t)shared_T;
+    }
     __syncthreads();
 
     int nbits = 0;
@@ -151,6 +158,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *_
             const int32_t slot = before + rank_in_wave;
             perm[slot] = (int32_t)p;
             slot_of_pair[p] = slot;
+            if (slot_row) slot_row[slot] = (int32_t)(p / k);
         }
         __syncthreads();
         if (tid < E) {
@@ -162,6 +170,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *_
         if (leader) wave_cnt[wave][e] = 0;
         __syncthreads();
     }
+    if (slot_row)
+        for (int64_t t = tid; t < shared_T; t += kBucketThreads) slot_row[P + t] = (int32_t)t;
 }
 
 constexpr int kCombineThreads = 256;
@@ -198,8 +208,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *_
 
 namespace w4a8 {
 
-hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t *ids, float *w,
-                            int32_t *offsets, int32_t *perm, int32_t *slot_of_pair, hipStream_t stream) {
+hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared, int32_t *ids,
+                            float *w, int32_t *offsets, int32_t *perm, int32_t *slot_row, int32_t *slot_of_pair,
+                            hipStream_t stream) {
     if (T > 0) {
         const int64_t per = kRouteThreads / kWave;
         hipLaunchKernelGGL(route_topk_kernel, dim3((uint32_t)((T + per - 1) / per)), dim3(kRouteThreads), 0, stream,
@@ -207,8 +218,8 @@ hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t t
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, T * topk, E, offsets, perm,
-                       slot_of_pair);
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, T * topk, E, topk,
+                       with_shared ? T : (int64_t)0, offsets, perm, slot_row, slot_of_pair);
     return hipGetLastError();
 }
 

@@ -37,9 +37,9 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                                const uint16_t *zp, int64_t N, int64_t max_slots, float *out,
                                hipStream_t stream);
 
-hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t *ids,
-                            float *w, int32_t *offsets, int32_t *perm, int32_t *slot_of_pair,
-                            hipStream_t stream);
+hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared,
+                            int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *slot_row,
+                            int32_t *slot_of_pair, hipStream_t stream);
 
 hipError_t launch_moe_combine(const float *y, const int32_t *slot_of_pair, const float *topk_w,
                               const float *y_shared, int64_t T, int32_t topk, int64_t H, float *out,
