@@ -134,7 +134,9 @@ w4a8_status w4a8_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t
 /* Device, test/debug aid.  Same main loop as w4a8_gemm, but instead of the fp32
  * epilogue it stores every per-group int32 sum: isums[K/128][M][N] ([p2 §5.4]).
  * `path` selects the main loop: 0 = the one w4a8_gemm would pick for M,
- * 1 = the small-M streaming loop (M <= 64), 2 = the large-M tiled loop. */
+ * 1 = the small-M streaming loop (M <= 64), 2 = the large-M tiled loop with the
+ * tile w4a8_gemm would pick, 3 = tiled with 128x128 workgroup tiles,
+ * 4 = tiled with 256x128 workgroup tiles. */
 w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K,
                                   const uint8_t *packed, const uint16_t *zp, int64_t N,
                                   int32_t group, int32_t path, int32_t *isums, hipStream_t stream);

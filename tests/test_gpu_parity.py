@@ -130,17 +130,20 @@ def test_device_packer_bit_exact(orc, case):
 
 
 # ------------------------------------------------------------------ dense GEMM, small shapes
+ALL = (1, 2, 3, 4)             # streaming; tiled with the default tile, 128x128, 256x128
+TILED = (2, 3, 4)
 SHAPES = [  # (M, N, K, paths)
-    (4, 128, 256, (1, 2)),      # the small config
-    (1, 16, 128, (1, 2)),
-    (3, 48, 384, (1, 2)),
-    (16, 272, 1024, (1, 2)),
-    (17, 64, 256, (1, 2)),
-    (33, 32, 512, (1, 2)),
-    (64, 16, 128, (1, 2)),
-    (65, 128, 256, (2,)),
-    (130, 144, 384, (2,)),      # ragged M and an N tail inside a 128-wide tile
-    (257, 400, 640, (2,)),
+    (4, 128, 256, ALL),         # the small config
+    (1, 16, 128, ALL),
+    (3, 48, 384, ALL),
+    (16, 272, 1024, ALL),
+    (17, 64, 256, ALL),
+    (33, 32, 512, ALL),
+    (64, 16, 128, ALL),
+    (65, 128, 256, TILED),
+    (130, 144, 384, TILED),     # ragged M and an N tail inside a 128-wide tile
+    (257, 400, 640, TILED),
+    (300, 128, 1152, TILED),    # odd group count over several groups
 ]
 
 

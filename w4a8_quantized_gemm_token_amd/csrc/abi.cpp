@@ -208,7 +208,7 @@ static w4a8_status check_gemm(const int8_t *qa, int64_t M, int64_t K, const uint
 static w4a8_status gemm_common(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group, int32_t path,
                                float *out, int32_t *isums, hipStream_t stream) {
-    W4A8_REQUIRE(path >= 0 && path <= 2, W4A8_EINVAL, "path=%d must be 0, 1 or 2", (int)path);
+    W4A8_REQUIRE(path >= 0 && path <= 4, W4A8_EINVAL, "path=%d must be in [0, 4]", (int)path);
     if (path == 0) path = (M <= kStreamMaxM) ? 1 : 2;
     W4A8_REQUIRE(!(path == 1 && M > kStreamMaxM), W4A8_EINVAL, "the streaming loop takes M <= %lld",
                  (long long)kStreamMaxM);

@@ -60,6 +60,19 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles) {
     return x * q + (x < r ? x : r) + i;
 }
 
+// Tile (tm, tn) of linear position i in panel order: panels of up to PM m-tiles,
+// inside a panel n fastest-varying over the panel's m-tiles.  Consecutive positions
+// (the workgroups one XCD runs at a time) then cover a PM x (32 / PM) block of
+// tiles, whose activation rows and weight columns its L2 serves to all of them.
+template <int PM>
+__device__ __forceinline__ void panel_tile(int64_t i, int64_t mt, int64_t nt, int64_t &tm, int64_t &tn) {
+    const int64_t p = i / (PM * nt);
+    const int64_t pm = (mt - PM * p) < PM ? (mt - PM * p) : PM;
+    const int64_t ip = i - p * PM * nt;
+    tm = PM * p + ip % pm;
+    tn = ip / pm;
+}
+
 // Largest power of two <= umax that divides the group count G (prefetch ring depth).
 __host__ __device__ inline int ring_depth(int64_t G, int umax) {
     int u = umax;
@@ -795,9 +808,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *
     using S = TileShape<WM, WN>;
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     const int64_t mt = (M + S::BM - 1) / S::BM, nt = (N + S::BN - 1) / S::BN;
-    const int64_t tile = xcd_tile(blockIdx.x, mt * nt);
-    // m fastest inside an XCD's range: concurrently running tiles share weight columns
-    const int64_t tm = tile % mt, tn = tile / mt;
+    int64_t tm, tn;
+    panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
     const int64_t m0 = tm * S::BM;
     const int rows = (int)((M - m0) < S::BM ? (M - m0) : S::BM);
     tile2_unit<WM, WN, ISUMS>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * S::BN,
@@ -1080,7 +1092,8 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
 #undef W4A8_STREAM
 #undef W4A8_STREAM_U
     } else {
-        if (M > 128) return launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        if (path == 4 || (path == 2 && M > 128))
+            return launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
         return launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     }
     return hipGetLastError();
