@@ -292,12 +292,14 @@ def test_route_ties_go_to_lower_expert():
 
 
 # ------------------------------------------------------------------ grouped GEMM
-def test_grouped_gemm_mixed_bucket_sizes(orc):
-    """Experts with 0, 1, 17, 64, 65 and 200 slots: both loops, an empty expert,
-    ragged tails, gathered rows; every output element checked."""
+@pytest.mark.parametrize("K", [384, 1024])
+def test_grouped_gemm_mixed_bucket_sizes(orc, K):
+    """Experts with 0, 1, 17, 64, 65 and 200 slots: both loops (K=1024 takes the
+    decode-style loop for the small experts, K=384 the streaming one), an empty
+    expert, ragged tails, gathered rows; every output element checked."""
     w4 = w4mod()
     counts = [0, 1, 17, 64, 65, 200]
-    E, N, K = len(counts), 160, 384
+    E, N = len(counts), 160
     R = 90
     rng = np.random.default_rng(4)
     S = sum(counts)

@@ -411,69 +411,92 @@ constexpr int kDecThreads = kDecWaves * 64;
 __host__ __device__ inline int64_t dec_lds_bytes(int64_t M, int64_t K) { return M * (K + 16); }
 constexpr int64_t kDecLdsMax = 140 * 1024;
 
-template <int U, int SPLIT, bool ISUMS>
-__global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *__restrict__ qa,
-                                                                 const float *__restrict__ a_scale, int64_t M,
-                                                                 int64_t K, const uint8_t *__restrict__ wpk,
-                                                                 const uint16_t *__restrict__ wsc,
-                                                                 const uint16_t *__restrict__ wzp, int64_t N,
-                                                                 int64_t tiles_per_wg, float *__restrict__ out,
-                                                                 int32_t *__restrict__ isums) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-    const int64_t lda = K + 16;
-    const int tid = threadIdx.x;
-    // stage qa[M][K] (16-byte pieces)
-    {
-        const int64_t pieces = M * (K / 16);
-        for (int64_t i = tid; i < pieces; i += kDecThreads) {
-            const int64_t r = i / (K / 16), c = i % (K / 16);
-            *reinterpret_cast<v4u *>(dsm + r * lda + c * 16) = reinterpret_cast<const v4u *>(qa + r * K)[c];
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Raw buffer resource over [p, p + 4 GB): no stride, no format conversion.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
+
+// Copy `nrows` activation rows of K bytes (source row src_row(r)) into LDS rows of
+// stride lda, straight from memory to LDS (buffer_load ... lds: lane L of a load
+// fills bytes [16 L, 16 L + 16) of a 1 KB block); lanes past the end of a row are
+// switched off.  Source offsets src_row(r) * K must stay below 2^32.  The caller
+// waits for the loads (vmcnt) before the rows are read.
+template <typename SrcRow>
+__device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const int8_t *qa, int64_t K, int nrows,
+                                               SrcRow src_row) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(qa);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int bpr = (int)((K + 1023) / 1024);  // 1 KB blocks per row
+    for (int i = wave; i < nrows * bpr; i += nwaves) {
+        const int r = i / bpr;
+        const int b = i - r * bpr;
+        if (b * 1024 + lane * 16 < K) {
+            const uint32_t off = (uint32_t)(src_row(r) * K + b * 1024 + lane * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + r * lda + b * 1024), 16, (int)off, 0, 0, 0);
         }
     }
-    __syncthreads();
+}
 
+// Tiles [t0, t1) of 16 columns for the M <= 16 activation rows staged in `rows`
+// (row stride K + 16).  `store(m, col, v)` receives a_scale-free fp32 sums; with
+// ISUMS the per-group int32 sums go to isums[g][m][col] instead.
+// `stage()` runs after the first weight windows are issued (so their latency overlaps
+// it) and is followed by a workgroup barrier: it fills `rows` when they change.
+template <int U, int SPLIT, bool ISUMS, typename Stage, typename Store>
+__device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M, int64_t K,
+                                          const uint8_t *__restrict__ wpk, const uint16_t *__restrict__ wsc,
+                                          const uint16_t *__restrict__ wzp, int64_t N, int64_t t0, int64_t t1,
+                                          Stage stage, Store store, int32_t *__restrict__ isums) {
+    const int64_t lda = K + 16;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int kq = lane >> 4;
     const int half = wave % SPLIT;
     const int64_t G = K / G128;
     const int64_t nwin = G / 2 / SPLIT;
     const int64_t win0 = half * nwin;
-    const int64_t ntiles = N / 16;
-    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_wg;
-    const int64_t t1 = (t0 + tiles_per_wg < ntiles) ? t0 + tiles_per_wg : ntiles;
     constexpr int per_round = kDecWaves / SPLIT;
     const int arow = (lane & 15) < M ? (lane & 15) : 0;
-    const uint8_t *abase = dsm + arow * lda + kq * 32;
+    const uint8_t *abase = rows + arow * lda + kq * 32;
     const int lchunk = ((lane >> 3) & 1) * 64 + kq * 16;
     const bool hi8 = (lane & 8) != 0;
-    float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(M, K) + 15) / 16) * 16);
 
+    // Each wave streams tile t0 + wave / SPLIT, then the tile per_round further, and so
+    // on; the window ring runs on across tiles, so the first windows of a wave's
+    // next tile are already in flight while it finishes the current one.
+    const int64_t colbyte = (int64_t)(lane & 7) * (K / 2) + lchunk;
+    const uint16_t *szbase = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
+    v4u rb0[U], rb1[U];
+    uint32_t rsz[U];
+    auto load_window = [&](int u, int64_t tile, int64_t w) {
+        const uint8_t *b = wpk + tile * 16 * (K / 2) + colbyte;
+        rb0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b) + w * 8);
+        rb1[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b + 8 * (K / 2)) + w * 8);
+        rsz[u] = szbase[tile * 16 + 2 * w * N];
+    };
+    {
+        const int64_t tile = t0 + wave / SPLIT;
+        if ((wave / SPLIT) < per_round && tile < t1) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_window(u, tile, win0 + u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    stage();
+    __syncthreads();
     for (int64_t tb = t0; tb < t1; tb += per_round) {
         const int64_t tile = tb + wave / SPLIT;
         const bool active = (wave / SPLIT) < per_round && tile < t1;
+        const int64_t ntile = tile + per_round < t1 ? tile + per_round : tile;  // where the ring runs on to
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (active) {
             const int64_t n0 = tile * 16;
             const int64_t col = n0 + (lane & 15);
-            const v4u *b0p = reinterpret_cast<const v4u *>(wpk + (n0 + (lane & 7)) * (K / 2) + lchunk);
-            const v4u *b1p = reinterpret_cast<const v4u *>(wpk + (n0 + 8 + (lane & 7)) * (K / 2) + lchunk);
-            // one 2-byte load per window gives all four per-column constants of the
-            // window: lane row kq fetches scale (kq = 0, 1) or zp (kq = 2, 3) of
-            // group 2w + (kq & 1); ds_bpermute then broadcasts them across rows
-            const uint16_t *szptr = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + col;
-            v4u rb0[U], rb1[U];
-            uint32_t rsz[U];
-            auto load_window = [&](int u, int64_t w) {
-                rb0[u] = __builtin_nontemporal_load(b0p + w * 8);
-                rb1[u] = __builtin_nontemporal_load(b1p + w * 8);
-                rsz[u] = szptr[2 * w * N];
-            };
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                __builtin_amdgcn_sched_barrier(0);
-                load_window(u, win0 + u);
-            }
-            __builtin_amdgcn_sched_barrier(0);
             for (int64_t w0 = 0; w0 < nwin; w0 += U) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -524,9 +547,14 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
                             for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, (float)d[r], acc[r]);
                         }
                     }
-                    const int64_t wn = (w0 + u + U < nwin) ? w + U : win0 + nwin - 1;
+                    // refill: window w + U of this tile, else the next tile's window
+                    // (w + U - nwin) of the same K half, else (last tile) a repeat
+                    const int64_t wa = w0 + u + U;
+                    const bool here = wa < nwin;
+                    const int64_t lt = here ? tile : ntile;
+                    const int64_t lw = here ? win0 + wa : (ntile != tile ? win0 + wa - nwin : win0 + nwin - 1);
                     __builtin_amdgcn_sched_barrier(0);
-                    load_window(u, wn);
+                    load_window(u, lt, lw);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -538,9 +566,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
                     for (int r = 0; r < 4; ++r) red[((wave / SPLIT) * 4 + r) * 64 + lane] = acc[r];
                 }
                 __syncthreads();
-                if (active && half == 1) {
-                    // nothing more for this wave in this round
-                } else if (active) {
+                if (active && half == 0) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[r] += red[((wave / SPLIT) * 4 + r) * 64 + lane];
                 }
@@ -551,11 +577,39 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 4 * kq + r;
-                    if (m < M) out[m * N + col] = a_scale[m] * acc[r];
+                    if (m < M) store(m, col, acc[r]);
                 }
             }
         }
     }
+}
+
+template <int U, int SPLIT, bool ISUMS>
+__global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *__restrict__ qa,
+                                                                 const float *__restrict__ a_scale, int64_t M,
+                                                                 int64_t K, const uint8_t *__restrict__ wpk,
+                                                                 const uint16_t *__restrict__ wsc,
+                                                                 const uint16_t *__restrict__ wzp, int64_t N,
+                                                                 int64_t tiles_per_wg, float *__restrict__ out,
+                                                                 int32_t *__restrict__ isums) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    const int64_t lda = K + 16;
+    const int64_t ntiles = N / 16;
+    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_wg;
+    const int64_t t1 = (t0 + tiles_per_wg < ntiles) ? t0 + tiles_per_wg : ntiles;
+    float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(M, K) + 15) / 16) * 16);
+    dec_tiles<U, SPLIT, ISUMS>(
+        dsm, red, (int)M, K, wpk, wsc, wzp, N, t0, t1,
+        [&]() {  // qa[M][K] -> LDS, 16-byte pieces through registers (measured a little
+                 // faster here than loads straight to LDS, whose wait would also cover
+                 // the weight loads just issued)
+            const int64_t pieces = M * (K / 16);
+            for (int64_t i = threadIdx.x; i < pieces; i += kDecThreads) {
+                const int64_t r = i / (K / 16), c = i % (K / 16);
+                *reinterpret_cast<v4u *>(dsm + r * lda + c * 16) = reinterpret_cast<const v4u *>(qa + r * K)[c];
+            }
+        },
+        [&](int m, int64_t col, float v) { out[m * N + col] = a_scale[m] * v; }, isums);
 }
 
 // Dense layer through the line-wide loop: a workgroup of SPLIT waves per 16-column tile.
@@ -825,12 +879,12 @@ constexpr int kSmallRows = 64;
 constexpr int kMaxExperts = 1024;
 
 // Exclusive prefix over experts of units(e) into lds_pfx[0..E]; returns the
-// total.  Run by the whole workgroup (nthreads = blockDim.x <= 256): thread t
+// total.  Run by the whole workgroup (nthreads = blockDim.x <= 1024): thread t
 // sums a contiguous run of experts, the runs are scanned with wave shuffles and
 // one LDS step, then each thread writes its run's prefixes.
 template <typename UnitsFn>
 __device__ __forceinline__ int64_t expert_prefix(int32_t E, int64_t *lds_pfx, int nthreads, UnitsFn units) {
-    __shared__ int64_t wave_tot[4];
+    __shared__ int64_t wave_tot[16];
     const int t = threadIdx.x;
     const int chunk = (E + nthreads - 1) / nthreads;
     const int e0 = t * chunk;
@@ -902,6 +956,78 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
             stream_unit<2, U2, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
         else
             stream_unit<4, U4, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+    }
+}
+
+// Experts with at most kSmallRows slots, decode style: one 1024-thread workgroup
+// per CU stages 16 gathered activation rows of one expert in LDS and streams a
+// round of 8 column tiles of that expert's weights (the loop of the dense decode
+// kernel).  Work units are (expert, 16-row chunk, round); each workgroup takes a
+// contiguous range of units, so it restages rows only when the chunk changes.
+template <int U, int SPLIT>
+__global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
+    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
+    const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
+    float *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ int64_t pfx[kMaxExperts + 1];
+    __shared__ int32_t srow[16];
+    __shared__ float sasc[16];  // row scales of the staged rows (no global load at the stores)
+    constexpr int per_round = kDecWaves / SPLIT;
+    const int64_t ntiles = N / 16;
+    const int64_t nblk = (ntiles + per_round - 1) / per_round;
+    const int64_t total = expert_prefix(E, pfx, kDecThreads, [&](int e) -> int64_t {
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        return (c > 0 && c <= kSmallRows) ? ((c + 15) / 16) * nblk : 0;
+    });
+    const int64_t G = K / G128;
+    const int64_t lda = K + 16;
+    float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(16, K) + 15) / 16) * 16);
+    const int64_t u0 = total * blockIdx.x / gridDim.x, u1 = total * (blockIdx.x + 1) / gridDim.x;
+    int staged_e = -1;
+    int64_t staged_chunk = -1;
+    for (int64_t u = u0; u < u1;) {
+        const int e = find_expert(pfx, E, u);
+        const int64_t local = u - pfx[e];
+        const int64_t chunk = local / nblk, blk = local % nblk;
+        // this workgroup's consecutive rounds of the same rows run as one stream
+        const int64_t blk_end = (blk + (u1 - u) < nblk) ? blk + (u1 - u) : nblk;
+        u += blk_end - blk;
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        const int64_t s0 = clamp_slots(offsets[e], max_slots) + chunk * 16;
+        const int rows = (int)((c - chunk * 16) < 16 ? (c - chunk * 16) : 16);
+        const bool restage = e != staged_e || chunk != staged_chunk;
+        if (restage) {
+            __syncthreads();  // every wave is done with the previous rows
+            if (threadIdx.x < 16) {
+                int32_t row = -1;
+                if ((int)threadIdx.x < rows) {
+                    const int64_t r = row_index ? (int64_t)row_index[s0 + threadIdx.x] : s0 + threadIdx.x;
+                    row = (r >= 0 && r < R) ? (int32_t)r : -1;
+                }
+                srow[threadIdx.x] = row;
+                sasc[threadIdx.x] = row >= 0 ? a_scale[row] : 0.0f;
+            }
+            __syncthreads();
+            staged_e = e;
+            staged_chunk = chunk;
+        }
+        const int64_t t0 = blk * per_round;
+        const int64_t t1 = (blk_end * per_round < ntiles) ? blk_end * per_round : ntiles;
+        dec_tiles<U, SPLIT, false>(
+            dsm, red, rows, K, packed + (int64_t)e * N * (K / 2), scale + (int64_t)e * G * N, zp + (int64_t)e * G * N,
+            N, t0, t1,
+            [&]() {  // the chunk's activation rows -> LDS (only when they changed); rows
+                     // outside [0, R) read row 0 and are never stored
+                if (!restage) return;
+                stage_rows_dma(dsm, lda, qa, K, rows, [&](int r) { return (int64_t)(srow[r] >= 0 ? srow[r] : 0); });
+                __builtin_amdgcn_s_waitcnt(0);
+            },
+            [&](int m, int64_t col, float v) {
+                if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
+            },
+            nullptr);
     }
 }
 
@@ -1099,6 +1225,20 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
     return hipGetLastError();
 }
 
+static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
+                                       const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
+                                       const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
+                                       float *out, int cus, hipStream_t stream) {
+    using S = TileShape<4, 2>;
+    const size_t lds = 2 * S::LDS_STAGE;
+    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<4, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+        return hipGetLastError();
+    hipLaunchKernelGGL((grouped_tiled_kernel<4, 2>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa, a_scale,
+                       R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots, float *out,
@@ -1106,7 +1246,30 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
-    const int U = ring_depth(K / G128, 4);
+    const int64_t G = K / G128;
+    const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + (kDecWaves / 2) * 4 * 64 * 4);
+    if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax) {
+        const int64_t nwin = G / 4;
+        const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
+        if (nwin % 2 == 0) {
+            if (hipFuncSetAttribute((const void *)grouped_decode_kernel<2, 2>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)
+                return hipGetLastError();
+            hipLaunchKernelGGL((grouped_decode_kernel<2, 2>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,
+                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+        } else {
+            if (hipFuncSetAttribute((const void *)grouped_decode_kernel<1, 2>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)
+                return hipGetLastError();
+            hipLaunchKernelGGL((grouped_decode_kernel<1, 2>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,
+                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+        }
+        hipError_t derr = hipGetLastError();
+        if (derr != hipSuccess) return derr;
+        return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
+                                    out, cus, stream);
+    }
+    const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
     if (U == 4)
         hipLaunchKernelGGL(grouped_stream_kernel<4>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
@@ -1119,14 +1282,8 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                            expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    using S = TileShape<4, 2>;
-    const size_t lds = 2 * S::LDS_STAGE;
-    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<4, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-        return hipGetLastError();
-    hipLaunchKernelGGL((grouped_tiled_kernel<4, 2>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa, a_scale,
-                       R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
-    return hipGetLastError();
+    return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
+                                cus, stream);
 }
 
 }  // namespace w4a8
