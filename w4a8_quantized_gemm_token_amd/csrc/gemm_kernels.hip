@@ -542,7 +542,8 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                                 if (m < M) isums[(g * M + m) * N + col] = d[r];
                             }
                         } else {
-                            const float sc = half_bits_to_float((uint16_t)sz[h]);
+                            float sc = half_bits_to_float((uint16_t)sz[h]);
+                            __asm__ volatile("" : "+v"(sc));  // one conversion, plain fmas
 #pragma unroll
                             for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, (float)d[r], acc[r]);
                         }
@@ -822,6 +823,9 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
         lstore(next, (int)((g + 1) & 1));
         sc[0] = half_bits_to_float(next.rs[0]);
         sc[1] = half_bits_to_float(next.rs[1]);
+        // keep the scales as fp32 values: folding the fp16->fp32 conversion into the
+        // epilogue (v_fma_mix_f32) measured slower than converting once per group
+        __asm__ volatile("" : "+v"(sc[0]), "+v"(sc[1]));
         __syncthreads();
     };
     int64_t g = 0;
