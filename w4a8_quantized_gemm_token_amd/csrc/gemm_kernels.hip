@@ -413,6 +413,9 @@ constexpr int64_t kDecLdsMax = 140 * 1024;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
+// s_waitcnt immediate for "vmcnt <= vm, lgkmcnt <= lgkm" (gfx9 encoding; expcnt not waited)
+constexpr int t3_waitcnt(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
 // Raw buffer resource over [p, p + 4 GB): no stride, no format conversion.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)0xFFFFFFFF, 0x00020000);
@@ -973,7 +976,7 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out) {
+    float *__restrict__ out, int small_max) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
     __shared__ int32_t srow[16];
@@ -983,7 +986,7 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int64_t nblk = (ntiles + per_round - 1) / per_round;
     const int64_t total = expert_prefix(E, pfx, kDecThreads, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return (c > 0 && c <= kSmallRows) ? ((c + 15) / 16) * nblk : 0;
+        return (c > 0 && c <= small_max) ? ((c + 15) / 16) * nblk : 0;
     });
     const int64_t G = K / G128;
     const int64_t lda = K + 16;
@@ -1032,6 +1035,237 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
                 if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
             },
             nullptr);
+    }
+}
+
+// Experts with 17..64 slots: one weight pass for all their rows.  A unit is (expert,
+// round of 8 column tiles); 16 waves = 8 tiles x 2 K halves, each wave computing
+// four 16-row fragments.  The 64 gathered activation rows do not fit in LDS at
+// once for large K, so they are staged in K slices of two windows per half
+// (double-buffered, straight from memory, issued one slice ahead) while the weight
+// window ring streams on.  Within each 256-byte window of a staged row, 16-byte
+// chunk j of row r sits at j ^ (r & 15), so the 16 rows of a fragment read 16
+// different bank groups.  The halves' partial sums are added through LDS at the end
+// of a round (half 0 + half 1), in storage that aliases the slice buffers.
+constexpr int kD64S = 2;                                   // windows per half per slice
+constexpr int kD64Buf = 64 * 2 * kD64S * 256;              // one slice buffer (64 KB)
+constexpr int kD64Lds = 2 * kD64Buf;                       // two slice buffers; the reduction aliases them
+
+template <int U>
+__global__ __launch_bounds__(kDecThreads) void grouped_decode64_kernel(
+    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
+    const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
+    float *__restrict__ out);
+template <int U>
+__global__ __launch_bounds__(kDecThreads) void grouped_decode64_kernel(
+    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
+    const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
+    float *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ int64_t pfx[kMaxExperts + 1];
+    __shared__ int32_t srow[64];
+    __shared__ float sasc[64];
+    constexpr int MT = 4, per_round = 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kq = lane >> 4, half = wave & 1, tslot = wave >> 1;
+    const int64_t ntiles = N / 16;
+    const int64_t nblk = (ntiles + per_round - 1) / per_round;
+    const int64_t G = K / G128;
+    const int nwh = (int)(G / 4);        // two-group windows per K half
+    const int nslice = nwh / kD64S;
+    const int64_t total = expert_prefix(E, pfx, kDecThreads, [&](int e) -> int64_t {
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        return (c > 16 && c <= kSmallRows) ? nblk : 0;
+    });
+    const int64_t u0 = total * blockIdx.x / gridDim.x, u1 = total * (blockIdx.x + 1) / gridDim.x;
+    const __amdgpu_buffer_rsrc_t qa_rs = make_rsrc(qa);
+    const bool hi8 = (lane & 8) != 0;
+    const int lchunk = ((lane >> 3) & 1) * 64 + kq * 16;
+    int aoff[2][2];  // [group of the window][fragment half]: swizzled chunk offset in a 256-byte window
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) aoff[h][j] = ((8 * h + 2 * kq + j) ^ (lane & 15)) * 16;
+    float *red = reinterpret_cast<float *>(dsm);  // [tile slot][fragment][r][lane], aliases the buffers
+    int staged_e = -1;
+    int bufc = 0;  // running slice-buffer counter
+
+    for (int64_t u = u0; u < u1;) {
+        const int e = find_expert(pfx, E, u);
+        const int64_t blk = u - pfx[e];
+        const int64_t blk_end = (blk + (u1 - u) < nblk) ? blk + (u1 - u) : nblk;
+        u += blk_end - blk;
+        const int64_t s0 = clamp_slots(offsets[e], max_slots);
+        const int rows = (int)(clamp_slots(offsets[e + 1], max_slots) - s0);
+        const int mt = (rows + 15) / 16;
+        if (e != staged_e) {
+            __syncthreads();
+            if (tid < 64) {
+                int32_t row = -1;
+                if (tid < rows) {
+                    const int64_t r = row_index ? (int64_t)row_index[s0 + tid] : s0 + tid;
+                    row = (r >= 0 && r < R) ? (int32_t)r : -1;
+                }
+                srow[tid] = row;
+                sasc[tid] = row >= 0 ? a_scale[row] : 0.0f;
+            }
+            __syncthreads();
+            staged_e = e;
+        }
+        const uint8_t *wpk = packed + (int64_t)e * N * (K / 2);
+        const uint16_t *wsc = scale + (int64_t)e * G * N, *wzp = zp + (int64_t)e * G * N;
+        const int64_t t0 = blk * per_round;
+        const int64_t t1 = (blk_end * per_round < ntiles) ? blk_end * per_round : ntiles;
+
+        // weight window ring over this wave's (tile, window of its half) sequence
+        const int64_t colbyte = (int64_t)(lane & 7) * (K / 2) + lchunk;
+        const uint16_t *szbase = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
+        v4u rb0[U], rb1[U];
+        uint16_t rsz[U];
+        auto load_window = [&](int uu, int64_t tile, int64_t w) {
+            const uint8_t *b = wpk + tile * 16 * (K / 2) + colbyte;
+            rb0[uu] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b) + w * 8);
+            rb1[uu] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b + 8 * (K / 2)) + w * 8);
+            rsz[uu] = szbase[tile * 16 + 2 * w * N];
+        };
+        // every wave runs the ring (an idle wave re-reads a valid window), so every
+        // wave issues the same number of loads per window, which the waits rely on
+        const int64_t tlast = t1 - 1;
+        {
+            const int64_t tile = t0 + tslot < t1 ? t0 + tslot : tlast;
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_window(uu, tile, half * nwh + uu);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // slice s of the current round -> buffer b: rows x halves x kD64S windows
+        auto stage_slice = [&](int s, int b) {
+            uint8_t *dst = dsm + b * kD64Buf;
+            for (int i = wave; i < rows; i += kDecWaves) {  // instruction i: row i, both halves
+                const int hh = lane >> 5, j = (lane & 31) >> 4, c = lane & 15;
+                const int32_t row = srow[i] >= 0 ? srow[i] : 0;
+                const int64_t wglob = (int64_t)hh * nwh + (int64_t)s * kD64S + j;
+                const uint32_t off = (uint32_t)((int64_t)row * K + wglob * 256 + ((c ^ (i & 15)) * 16));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qa_rs, (lds_ptr_t)(dst + i * 1024), 16, (int)off, 0, 0, 0);
+            }
+        };
+
+        for (int64_t tb = t0; tb < t1; tb += per_round) {
+            const int64_t tile = tb + tslot;
+            const bool active = tile < t1;
+            const int64_t ctile = active ? tile : tlast;
+            const int64_t ntile = tile + per_round < t1 ? tile + per_round : ctile;
+            // round prologue: slice 0 (buffers are free: the previous round ended with a barrier)
+            stage_slice(0, bufc & 1);
+            __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 0));
+            __syncthreads();
+            float acc[MT][4];
+#pragma unroll
+            for (int f = 0; f < MT; ++f)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[f][r] = 0.0f;
+            int wi = 0;  // window index within this wave's half
+            for (int s = 0; s < nslice; ++s) {
+                const int b = bufc & 1;
+                if (s + 1 < nslice) stage_slice(s + 1, b ^ 1);
+                const uint8_t *abuf = dsm + b * kD64Buf + half * 512;
+#pragma unroll
+                for (int j = 0; j < kD64S; ++j, ++wi) {
+                    const int uu = j % U;  // U divides kD64S: the ring slot is known at compile time
+                    const int64_t w = half * nwh + wi;
+                    uint32_t xy[2][4];
+                    {
+                        const uint32_t r0[4] = {rb0[uu].x, rb0[uu].y, rb0[uu].z, rb0[uu].w};
+                        const uint32_t r1[4] = {rb1[uu].x, rb1[uu].y, rb1[uu].z, rb1[uu].w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t t1v = dpp_ror8(r1[i]);
+                            const uint32_t t0v = dpp_ror8(r0[i]);
+                            xy[0][i] = hi8 ? t1v : r0[i];
+                            xy[1][i] = hi8 ? r1[i] : t0v;
+                        }
+                    }
+                    uint32_t sz[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sz[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)(uint32_t)rsz[uu]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        // codes minus zero point as INT8 (SWAR, as in the tiled loop): with
+                        // four row fragments this costs less than the zero-point MFMAs
+                        const uint32_t zadd = zp_add_const((uint16_t)sz[2 + h]);
+                        uint32_t q[8];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            spread8(xy[h][i], q[2 * i], q[2 * i + 1]);
+                            q[2 * i] = (q[2 * i] + zadd) ^ 0x80808080u;
+                            q[2 * i + 1] = (q[2 * i + 1] + zadd) ^ 0x80808080u;
+                        }
+                        const v4i bq0 = {(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                        const v4i bq1 = {(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+                        float sc = half_bits_to_float((uint16_t)sz[h]);
+                        __asm__ volatile("" : "+v"(sc));
+#pragma unroll
+                        for (int f = 0; f < MT; ++f) {
+                            if (f >= mt) break;  // fragments past the expert's rows (wave-uniform)
+                            __builtin_amdgcn_sched_barrier(0);  // one fragment at a time: register budget
+                            const uint8_t *ar = abuf + (f * 16 + (lane & 15)) * 1024 + j * 256;
+                            const v4i a0 = *reinterpret_cast<const v4i *>(ar + aoff[h][0]);
+                            const v4i a1 = *reinterpret_cast<const v4i *>(ar + aoff[h][1]);
+                            v4i d = {0, 0, 0, 0};
+                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq1, d, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[f][r] = fmaf(sc, (float)d[r], acc[f][r]);
+                        }
+                    }
+                    // refill: window wi + U of this tile, else of the next tile (same half)
+                    const int wa = wi + U;
+                    const bool here = wa < nwh;
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_window(uu, here ? ctile : ntile, half * nwh + (here ? wa : (ntile != ctile ? wa - nwh : nwh - 1)));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // the next slice's rows (issued before this slice's refills) must have landed
+                __builtin_amdgcn_s_waitcnt(t3_waitcnt(3 * kD64S, 0));
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                __asm__ volatile("" ::: "memory");
+                ++bufc;
+            }
+            // K halves: half 1 leaves its sums in LDS, half 0 adds them and stores
+            if (half == 1) {
+#pragma unroll
+                for (int f = 0; f < MT; ++f)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((tslot * MT + f) * 4 + r) * 64 + lane] = acc[f][r];
+            }
+            __syncthreads();
+            if (half == 0 && active) {
+                // row and column of each value computed here (an opaque copy of the lane
+                // index keeps the compiler from precomputing the 16 row offsets for the
+                // whole kernel, which would not fit the register budget)
+                int ln = lane;
+                __asm__ volatile("" : "+v"(ln));
+                const int kq2 = ln >> 4;
+                float *ocol = out + tile * 16 + (ln & 15);
+#pragma unroll
+                for (int f = 0; f < MT; ++f)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = f * 16 + 4 * kq2 + r;
+                        const float v = acc[f][r] + red[((tslot * MT + f) * 4 + r) * 64 + ln];
+                        if (m < rows && srow[m] >= 0) ocol[(s0 + m) * N] = sasc[m] * v;
+                    }
+            }
+            __syncthreads();
+        }
+        // drain the ring's last loads before the next unit reuses the registers' targets
+        __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 0));
     }
 }
 
@@ -1255,21 +1489,32 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax) {
         const int64_t nwin = G / 4;
         const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
+        // experts with 17..64 slots: one weight pass over K slices when the slicing fits
+        const bool d64 = G % (4 * kD64S) == 0 && (int64_t)R * K < (1ll << 32);
+        const int small_max = d64 ? 16 : (int)kSmallRows;
         if (nwin % 2 == 0) {
             if (hipFuncSetAttribute((const void *)grouped_decode_kernel<2, 2>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)
                 return hipGetLastError();
             hipLaunchKernelGGL((grouped_decode_kernel<2, 2>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,
-                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max);
         } else {
             if (hipFuncSetAttribute((const void *)grouped_decode_kernel<1, 2>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)
                 return hipGetLastError();
             hipLaunchKernelGGL((grouped_decode_kernel<1, 2>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,
-                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max);
         }
         hipError_t derr = hipGetLastError();
         if (derr != hipSuccess) return derr;
+        if (d64) {
+            if (hipFuncSetAttribute((const void *)grouped_decode64_kernel<2>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kD64Lds) != hipSuccess)
+                return hipGetLastError();
+            hipLaunchKernelGGL((grouped_decode64_kernel<2>), dgrid, dblock, kD64Lds, stream, qa, a_scale, R,
+                               row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+            if ((derr = hipGetLastError()) != hipSuccess) return derr;
+        }
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
                                     out, cus, stream);
     }
