@@ -287,8 +287,58 @@ def secondary(torch, w4, synthetic):
                                         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
     del layer, x, qa, sc
     torch.cuda.empty_cache()
-    # MoE FFN layer, 384 experts + shared, top-8, H=7168, I=2048
     from tests.gpu_common import device_experts
+    # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
+    # back-to-back prepared launches that rotate three copies of the 250 MB expert set
+    # (so no call finds its weights in the 256 MB Infinity Cache); the layer (route,
+    # quantize, grouped GEMM, combine) is timed the same way.
+    E8, K8, N8, copies = 8, 4096, 14336, 3
+    sets = [device_experts(0, synthetic.TAG_W, E8, N8, K8) for _ in range(copies)]
+    ebytes = N8 * K8 // 2 + 4 * N8 * (K8 // GROUP)  # packed codes + fp16 scale and zero point
+    stream = torch.cuda.current_stream()
+
+    def timed(fns, reps):
+        for i in range(20):
+            fns[i % len(fns)]()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for i in range(reps):
+            fns[i % len(fns)]()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    for B in (1, 2, 4, 512):
+        x = torch.from_numpy(synthetic.activations(100 + B, B, K8)).to(dev)
+        logits = torch.from_numpy(synthetic.router_logits_iid(100 + B, B, E8)).to(dev)
+        i32, f32 = torch.int32, torch.float32
+        routed = (torch.empty((B, 1), dtype=i32, device=dev), torch.empty((B, 1), dtype=f32, device=dev),
+                  torch.empty((E8 + 1,), dtype=i32, device=dev), torch.empty((B,), dtype=i32, device=dev),
+                  torch.empty((B,), dtype=i32, device=dev), torch.empty((B,), dtype=i32, device=dev))
+        qa8 = torch.empty((B, K8), dtype=torch.int8, device=dev)
+        sc8 = torch.empty((B,), dtype=f32, device=dev)
+        y8 = torch.empty((B, N8), dtype=f32, device=dev)
+        o8 = torch.empty((B, N8), dtype=f32, device=dev)
+        route = w4.prepare_moe_route(logits, 1, routed)
+        quant = w4.prepare_quantize_act(x, qa8, sc8)
+        ggs = [w4.prepare_moe_grouped_gemm(qa8, sc8, routed[4], routed[2], *sets[c], B, y8) for c in range(copies)]
+        comb = w4.prepare_moe_combine(y8, routed[5], routed[1], o8)
+        route()
+        quant()
+        torch.cuda.synchronize()
+        touched = int((np.diff(routed[2].cpu().numpy()) > 0).sum())
+        gemm_ms = timed(ggs, 60)
+        layers = [lambda c=c: (route(), quant(), ggs[c](), comb()) for c in range(copies)]
+        layer_ms = timed(layers, 60)
+        gbytes = touched * ebytes + B * (K8 + 4) + 4 * B * N8
+        t_roof = max(gbytes / (HBM_PEAK_GBS * 1e9), 2.0 * B * N8 * K8 / (INT8_PEAK_TOPS * 1e12))
+        out[f"toy_moe_B{B}"] = {"gemm_us": round(gemm_ms * 1e3, 2), "experts_touched": touched,
+                                "GB/s": round(gbytes / (gemm_ms * 1e-3) / 1e9, 1),
+                                "frac_roofline": round(t_roof / (gemm_ms * 1e-3), 4),
+                                "layer_us": round(layer_ms * 1e3, 2)}
+    del sets, ggs, layers
+    torch.cuda.empty_cache()
+    # MoE FFN layer, 384 experts + shared, top-8, H=7168, I=2048
     E, k, H, I = 384, 8, 7168, 2048
     gate_up = device_experts(0, synthetic.TAG_W, E + 1, 2 * I, H)
     down = device_experts(0, synthetic.TAG_W_DOWN, E + 1, H, I)

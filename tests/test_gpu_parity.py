@@ -137,6 +137,7 @@ SHAPES = [  # (M, N, K, paths)
     (1, 16, 128, ALL),
     (3, 48, 384, ALL),
     (16, 272, 1024, ALL),
+    (8, 336, 2048, ALL),        # decode with four K parts per tile and two windows in flight
     (17, 64, 256, ALL),
     (33, 32, 512, ALL),
     (64, 16, 128, ALL),

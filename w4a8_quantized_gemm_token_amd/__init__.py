@@ -280,6 +280,38 @@ def moe_grouped_gemm(qa, a_scale, row_index, offsets, packed, scale, zp, max_slo
     return out
 
 
+def prepare_moe_route(logits, topk: int, outs) -> Launch:
+    """Prepared w4a8_moe_route (no shared expert) into outs = (ids, w, offsets, perm, row_index,
+    slot_of_pair), shaped as moe_route returns them."""
+    T, E = logits.shape
+    ids, w, off, perm, rows, sop = outs
+    assert tuple(ids.shape) == (T, topk) and tuple(off.shape) == (E + 1,) and tuple(rows.shape) == (T * topk,)
+    return Launch("w4a8_moe_route", (_dev_ptr(logits), T, E, topk, 0, _dev_ptr(ids), _dev_ptr(w), _dev_ptr(off),
+                                     _dev_ptr(perm), _dev_ptr(rows), _dev_ptr(sop), _stream(logits.device)),
+                  (logits,) + tuple(outs))
+
+
+def prepare_moe_grouped_gemm(qa, a_scale, row_index, offsets, packed, scale, zp, max_slots: int, out,
+                             group: int = GROUP) -> Launch:
+    """Prepared w4a8_moe_grouped_gemm writing into a preallocated out float32 [max_slots][N]."""
+    R, K = qa.shape
+    E, N = packed.shape[0], packed.shape[1]
+    assert tuple(out.shape) == (max_slots, N)
+    return Launch("w4a8_moe_grouped_gemm", (_dev_ptr(qa), _dev_ptr(a_scale), R, _dev_ptr(row_index),
+                                            _dev_ptr(offsets), E, K, _dev_ptr(packed), _dev_ptr(scale),
+                                            _dev_ptr(zp), N, group, max_slots, _dev_ptr(out), _stream(qa.device)),
+                  (qa, a_scale, row_index, offsets, packed, scale, zp, out))
+
+
+def prepare_moe_combine(y, slot_of_pair, topk_w, out) -> Launch:
+    """Prepared w4a8_moe_combine (no shared expert) into a preallocated out float32 [T][H]."""
+    T, k = topk_w.shape
+    H = y.shape[1]
+    assert tuple(out.shape) == (T, H)
+    return Launch("w4a8_moe_combine", (_dev_ptr(y), _dev_ptr(slot_of_pair), _dev_ptr(topk_w), None, T, k, H,
+                                       _dev_ptr(out), _stream(y.device)), (y, slot_of_pair, topk_w, out))
+
+
 def silu_mul_quantize(gu, want_h: bool = False):
     """gu float32 [P][2I] -> (qh int8 [P][I], h_scale float32 [P][, h float32 [P][I]])."""
     torch = _torch()

@@ -28,6 +28,8 @@
 //    waves each run a 64x64 sub-tile with v_mfma_i32_32x32x32_i8.
 // Both keep the per-group int32 sum in the MFMA accumulator and fold it into an
 // fp32 accumulator with one fma per element per group, groups in increasing g.
+#include <algorithm>
+
 #include "w4a8_internal.hpp"
 
 using namespace w4a8dev;
@@ -403,12 +405,14 @@ __device__ __forceinline__ void stream2_unit(float *lds_red, const int8_t *__res
 // so the 16 rows of an MFMA fragment fall in different banks); its 16 waves then
 // stream full-line weight windows (as in the loop above) and read activation
 // fragments from LDS.  Workgroup b owns a contiguous range of 16-column tiles; wave
-// w takes tile w / SPLIT, K half w % SPLIT of each round, and the two halves are
-// added through LDS at the end of the round (fixed order: half 0 + half 1).
+// w takes tile w / SPLIT, K part w % SPLIT of each round, and the parts are added
+// through LDS at the end of the round (fixed order: part 0 + part 1 + ...).
 constexpr int kDecWaves = 16;
 constexpr int kDecThreads = kDecWaves * 64;
 
 __host__ __device__ inline int64_t dec_lds_bytes(int64_t M, int64_t K) { return M * (K + 16); }
+// partial sums of K parts 1..split-1 of one round: [part][tile][4][64] fp32
+__host__ __device__ inline int64_t dec_red_bytes(int split) { return (int64_t)(split - 1) * (kDecWaves / split) * 1024; }
 constexpr int64_t kDecLdsMax = 140 * 1024;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -564,15 +568,19 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
             }
         }
         if (!ISUMS) {
-            if (SPLIT > 1) {
-                if (active && half == 1) {
+            if (SPLIT > 1) {  // K parts 1.. leave their sums in LDS; part 0 adds them in order
+                if (active && half != 0) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) red[((wave / SPLIT) * 4 + r) * 64 + lane] = acc[r];
+                    for (int r = 0; r < 4; ++r)
+                        red[(((half - 1) * per_round + wave / SPLIT) * 4 + r) * 64 + lane] = acc[r];
                 }
                 __syncthreads();
                 if (active && half == 0) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] += red[((wave / SPLIT) * 4 + r) * 64 + lane];
+                    for (int h = 1; h < SPLIT; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[r] += red[(((h - 1) * per_round + wave / SPLIT) * 4 + r) * 64 + lane];
                 }
                 __syncthreads();
             }
@@ -967,10 +975,12 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
 }
 
 // Experts with at most kSmallRows slots, decode style: one 1024-thread workgroup
-// per CU stages 16 gathered activation rows of one expert in LDS and streams a
-// round of 8 column tiles of that expert's weights (the loop of the dense decode
-// kernel).  Work units are (expert, 16-row chunk, round); each workgroup takes a
-// contiguous range of units, so it restages rows only when the chunk changes.
+// per CU stages 16 gathered activation rows of one expert in LDS and streams
+// 16-column tiles of that expert's weights (the loop of the dense decode kernel).
+// Work units are (expert, 16-row chunk, tile); each workgroup takes a contiguous
+// range of units, so it restages rows only when the chunk changes, and its tiles of
+// one chunk run as one stream.  Each tile is split over SPLIT K parts: four when no
+// workgroup can get more than four tiles (so that all 16 waves stream), else two.
 template <int U, int SPLIT>
 __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
@@ -981,12 +991,10 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     __shared__ int64_t pfx[kMaxExperts + 1];
     __shared__ int32_t srow[16];
     __shared__ float sasc[16];  // row scales of the staged rows (no global load at the stores)
-    constexpr int per_round = kDecWaves / SPLIT;
     const int64_t ntiles = N / 16;
-    const int64_t nblk = (ntiles + per_round - 1) / per_round;
     const int64_t total = expert_prefix(E, pfx, kDecThreads, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return (c > 0 && c <= small_max) ? ((c + 15) / 16) * nblk : 0;
+        return (c > 0 && c <= small_max) ? ((c + 15) / 16) * ntiles : 0;
     });
     const int64_t G = K / G128;
     const int64_t lda = K + 16;
@@ -997,10 +1005,9 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     for (int64_t u = u0; u < u1;) {
         const int e = find_expert(pfx, E, u);
         const int64_t local = u - pfx[e];
-        const int64_t chunk = local / nblk, blk = local % nblk;
-        // this workgroup's consecutive rounds of the same rows run as one stream
-        const int64_t blk_end = (blk + (u1 - u) < nblk) ? blk + (u1 - u) : nblk;
-        u += blk_end - blk;
+        const int64_t chunk = local / ntiles, t0 = local % ntiles;
+        const int64_t t1 = (t0 + (u1 - u) < ntiles) ? t0 + (u1 - u) : ntiles;
+        u += t1 - t0;
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
         const int64_t s0 = clamp_slots(offsets[e], max_slots) + chunk * 16;
         const int rows = (int)((c - chunk * 16) < 16 ? (c - chunk * 16) : 16);
@@ -1014,27 +1021,30 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
                     row = (r >= 0 && r < R) ? (int32_t)r : -1;
                 }
                 srow[threadIdx.x] = row;
-                sasc[threadIdx.x] = row >= 0 ? a_scale[row] : 0.0f;
             }
             __syncthreads();
             staged_e = e;
             staged_chunk = chunk;
         }
-        const int64_t t0 = blk * per_round;
-        const int64_t t1 = (blk_end * per_round < ntiles) ? blk_end * per_round : ntiles;
-        dec_tiles<U, SPLIT, false>(
-            dsm, red, rows, K, packed + (int64_t)e * N * (K / 2), scale + (int64_t)e * G * N, zp + (int64_t)e * G * N,
-            N, t0, t1,
-            [&]() {  // the chunk's activation rows -> LDS (only when they changed); rows
-                     // outside [0, R) read row 0 and are never stored
-                if (!restage) return;
-                stage_rows_dma(dsm, lda, qa, K, rows, [&](int r) { return (int64_t)(srow[r] >= 0 ? srow[r] : 0); });
-                __builtin_amdgcn_s_waitcnt(0);
-            },
-            [&](int m, int64_t col, float v) {
-                if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
-            },
-            nullptr);
+        const uint8_t *wpk = packed + (int64_t)e * N * (K / 2);
+        const uint16_t *wsc = scale + (int64_t)e * G * N, *wzp = zp + (int64_t)e * G * N;
+        auto stage = [&]() {  // the chunk's activation rows -> LDS (only when they changed);
+                              // rows outside [0, R) read row 0 and are never stored.  The row
+                              // scales load alongside (their latency overlaps the rows').
+            if (!restage) return;
+            stage_rows_dma(dsm, lda, qa, K, rows, [&](int r) { return (int64_t)(srow[r] >= 0 ? srow[r] : 0); });
+            float asc = 0.0f;
+            if (threadIdx.x < 16) {
+                const int32_t row = srow[threadIdx.x];
+                asc = a_scale[row >= 0 ? row : 0];
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            if (threadIdx.x < 16) sasc[threadIdx.x] = srow[threadIdx.x] >= 0 ? asc : 0.0f;
+        };
+        auto store = [&](int m, int64_t col, float v) {
+            if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
+        };
+        dec_tiles<U, SPLIT, false>(dsm, red, rows, K, wpk, wsc, wzp, N, t0, t1, stage, store, nullptr);
     }
 }
 
@@ -1176,7 +1186,6 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode64_kernel(
 #pragma unroll
                 for (int j = 0; j < kD64S; ++j, ++wi) {
                     const int uu = j % U;  // U divides kD64S: the ring slot is known at compile time
-                    const int64_t w = half * nwh + wi;
                     uint32_t xy[2][4];
                     {
                         const uint32_t r0[4] = {rb0[uu].x, rb0[uu].y, rb0[uu].z, rb0[uu].w};
@@ -1274,14 +1283,14 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out) {
+    float *__restrict__ out, int64_t cmin, int64_t cmax) {
     using S = TileShape<WM, WN>;
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
     const int64_t ntn = (N + S::BN - 1) / S::BN;
     const int64_t total = expert_prefix(E, pfx, S::THREADS, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return c > kSmallRows ? ((c + S::BM - 1) / S::BM) * ntn : 0;
+        return (c > cmin && c <= cmax) ? ((c + S::BM - 1) / S::BM) * ntn : 0;
     });
     const int64_t G = K / G128;
     for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
@@ -1373,12 +1382,13 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
     const int64_t G = K / G128;
-    const int split = (G % 4 == 0) ? 2 : 1;
     const int64_t ntiles = N / 16;
     const int64_t tpw = (ntiles + cus - 1) / cus;
     const int64_t nwg = (ntiles + tpw - 1) / tpw;
-    const int64_t red_bytes = (kDecWaves / split) * 4 * 64 * 4;
-    const size_t lds = (size_t)(((dec_lds_bytes(M, K) + 15) / 16) * 16 + red_bytes);
+    // K parts per tile: two, or four when a workgroup has at most four tiles (so
+    // that all 16 waves stream), as far as the groups divide evenly
+    const int split = (G % 8 == 0 && tpw <= 4) ? 4 : ((G % 4 == 0) ? 2 : 1);
+    const size_t lds = (size_t)(((dec_lds_bytes(M, K) + 15) / 16) * 16 + dec_red_bytes(split));
     const int64_t nwin = G / 2 / split;
     const dim3 grid((uint32_t)nwg), block(kDecThreads);
 #define W4A8_DEC(UU, SS)                                                                                            \
@@ -1397,7 +1407,10 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
                                packed, scale, zp, N, tpw, out, isums);                                              \
         }                                                                                                           \
     } while (0)
-    if (split == 2) {
+    if (split == 4) {
+        if (nwin % 2 == 0) W4A8_DEC(2, 4);
+        else W4A8_DEC(1, 4);
+    } else if (split == 2) {
         if (nwin % 2 == 0) W4A8_DEC(2, 2);
         else W4A8_DEC(1, 2);
     } else {
@@ -1463,18 +1476,32 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
     return hipGetLastError();
 }
 
+// Experts with more than kSmallRows slots: 128-row tiles up to 128 slots, 256-row
+// tiles above (a 256-row tile over a 65..128-slot expert would waste most of its work).
+template <int WM, int WN>
+static hipError_t launch_grouped_tiled_t(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
+                                         const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
+                                         const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
+                                         float *out, int64_t cmin, int64_t cmax, int cus, hipStream_t stream) {
+    using S = TileShape<WM, WN>;
+    const size_t lds = 2 * S::LDS_STAGE;
+    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<WM, WN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+        return hipGetLastError();
+    hipLaunchKernelGGL((grouped_tiled_kernel<WM, WN>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa,
+                       a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, cmin, cmax);
+    return hipGetLastError();
+}
+
 static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                        const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                        const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
                                        float *out, int cus, hipStream_t stream) {
-    using S = TileShape<4, 2>;
-    const size_t lds = 2 * S::LDS_STAGE;
-    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<4, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-        return hipGetLastError();
-    hipLaunchKernelGGL((grouped_tiled_kernel<4, 2>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa, a_scale,
-                       R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
-    return hipGetLastError();
+    hipError_t err = launch_grouped_tiled_t<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp,
+                                                  N, max_slots, out, kSmallRows, 128, cus, stream);
+    if (err != hipSuccess || max_slots <= 128) return err;
+    return launch_grouped_tiled_t<4, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
+                                        max_slots, out, 128, INT64_MAX, cus, stream);
 }
 
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
@@ -1485,29 +1512,36 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
     const int64_t G = K / G128;
-    const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + (kDecWaves / 2) * 4 * 64 * 4);
     if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax) {
-        const int64_t nwin = G / 4;
         const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
         // experts with 17..64 slots: one weight pass over K slices when the slicing fits
         const bool d64 = G % (4 * kD64S) == 0 && (int64_t)R * K < (1ll << 32);
         const int small_max = d64 ? 16 : (int)kSmallRows;
-        if (nwin % 2 == 0) {
-            if (hipFuncSetAttribute((const void *)grouped_decode_kernel<2, 2>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)
-                return hipGetLastError();
-            hipLaunchKernelGGL((grouped_decode_kernel<2, 2>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,
-                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max);
+#define W4A8_GDEC(UU, SS)                                                                                           \
+    do {                                                                                                            \
+        const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + dec_red_bytes(SS));                 \
+        if (hipFuncSetAttribute((const void *)grouped_decode_kernel<UU, SS>,                                        \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)               \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((grouped_decode_kernel<UU, SS>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,  \
+                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max);                  \
+    } while (0)
+        // four K parts per tile when no workgroup can get more than four tiles (an upper
+        // bound of the work: each expert's last chunk may be partial)
+        const int64_t chunks = std::min<int64_t>(max_slots, (max_slots + 15) / 16 + E);
+        const bool four = G % 8 == 0 && chunks * (N / 16) <= 4 * (int64_t)cus;
+        if (four) {
+            if ((G / 8) % 2 == 0) W4A8_GDEC(2, 4);
+            else W4A8_GDEC(1, 4);
         } else {
-            if (hipFuncSetAttribute((const void *)grouped_decode_kernel<1, 2>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)
-                return hipGetLastError();
-            hipLaunchKernelGGL((grouped_decode_kernel<1, 2>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,
-                               expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max);
+            if ((G / 4) % 2 == 0) W4A8_GDEC(2, 2);
+            else W4A8_GDEC(1, 2);
         }
+#undef W4A8_GDEC
         hipError_t derr = hipGetLastError();
         if (derr != hipSuccess) return derr;
-        if (d64) {
+        // the other two loops only when some expert can have more than 16 slots
+        if (d64 && max_slots > 16) {
             if (hipFuncSetAttribute((const void *)grouped_decode64_kernel<2>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, kD64Lds) != hipSuccess)
                 return hipGetLastError();
@@ -1515,6 +1549,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                                row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
             if ((derr = hipGetLastError()) != hipSuccess) return derr;
         }
+        if (max_slots <= kSmallRows) return hipSuccess;
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
                                     out, cus, stream);
     }
@@ -1530,7 +1565,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         hipLaunchKernelGGL(grouped_stream_kernel<1>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
                            expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || max_slots <= kSmallRows) return err;
     return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
                                 cus, stream);
 }
