@@ -29,6 +29,7 @@
 // Both keep the per-group int32 sum in the MFMA accumulator and fold it into an
 // fp32 accumulator with one fma per element per group, groups in increasing g.
 #include <algorithm>
+#include <type_traits>
 
 #include "w4a8_internal.hpp"
 
@@ -1048,234 +1049,236 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     }
 }
 
-// Experts with 17..64 slots: one weight pass for all their rows.  A unit is (expert,
-// round of 8 column tiles); 16 waves = 8 tiles x 2 K halves, each wave computing
-// four 16-row fragments.  The 64 gathered activation rows do not fit in LDS at
-// once for large K, so they are staged in K slices of two windows per half
-// (double-buffered, straight from memory, issued one slice ahead) while the weight
-// window ring streams on.  Within each 256-byte window of a staged row, 16-byte
-// chunk j of row r sits at j ^ (r & 15), so the 16 rows of a fragment read 16
-// different bank groups.  The halves' partial sums are added through LDS at the end
-// of a round (half 0 + half 1), in storage that aliases the slice buffers.
-constexpr int kD64S = 2;                                   // windows per half per slice
-constexpr int kD64Buf = 64 * 2 * kD64S * 256;              // one slice buffer (64 KB)
-constexpr int kD64Lds = 2 * kD64Buf;                       // two slice buffers; the reduction aliases them
+// Experts with a middle number of slots (up to 32 * MF): one weight pass over all
+// their rows with full-rate 32x32x32 INT8 MFMAs.  A work unit is (expert, block of
+// 256 columns); a 512-thread workgroup takes a contiguous range of units, and wave w
+// owns the 32 columns [256 b + 32 w, +32) of the unit for all rows and all K.
+//
+// Weights go straight from memory to registers: lane l holds column l % 32 and, per
+// group, the packed bytes [32 h, 32 h + 32) (h = l / 32), i.e. codes 64 h + [0, 64) of
+// the group.  MFMA step s of the group takes the 16 codes 64 h + 16 s + [0, 16); each
+// packed dword splits into its low nibbles (codes 0 2 4 6) and high nibbles (1 3 5 7)
+// with two operations, so operand byte order within every 8 codes is 0 2 4 6 1 3 5 7.
+// The activation rows are staged in LDS with the same byte order (one v_perm per four
+// bytes, once per workgroup instead of once per wave), so both operands agree.
+//
+// Activations are staged in K slices of kMidSlice groups (all rows of the unit,
+// double-buffered, issued one slice ahead through registers); the slice sequence runs
+// on from one unit into the next, and so does each wave's ring of U groups of
+// weights, so a workgroup streams without draining between units.
+constexpr int kMidThreads = 512;
+constexpr int kMidSlice = 4;                       // groups per activation slice
+constexpr int kMidRow = kMidSlice * G128 + 16;     // LDS bytes per staged row and slice
+__host__ __device__ inline int64_t mid_lds_bytes(int mf) { return 2ll * 32 * mf * kMidRow; }
 
-template <int U>
-__global__ __launch_bounds__(kDecThreads) void grouped_decode64_kernel(
+template <int MF, int U>
+__global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out);
-template <int U>
-__global__ __launch_bounds__(kDecThreads) void grouped_decode64_kernel(
-    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
-    const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
-    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out) {
+    float *__restrict__ out, int64_t cmin) {
+    constexpr int RM = 32 * MF;                    // staged rows
+    constexpr int BUF = RM * kMidRow;
+    constexpr int TPR = kMidThreads / RM;          // staging threads per row
+    constexpr int NV = kMidSlice * G128 / TPR / 16; // 16-byte pieces per thread and slice
+    static_assert(kMidSlice % U == 0, "ring slots must repeat within a slice");
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
-    __shared__ int32_t srow[64];
-    __shared__ float sasc[64];
-    constexpr int MT = 4, per_round = 8;
+    __shared__ float sasc[2][RM];                  // row scale per unit parity; -1: no store
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int kq = lane >> 4, half = wave & 1, tslot = wave >> 1;
-    const int64_t ntiles = N / 16;
-    const int64_t nblk = (ntiles + per_round - 1) / per_round;
+    const int h = lane >> 5;
     const int64_t G = K / G128;
-    const int nwh = (int)(G / 4);        // two-group windows per K half
-    const int nslice = nwh / kD64S;
-    const int64_t total = expert_prefix(E, pfx, kDecThreads, [&](int e) -> int64_t {
+    const int nsl = (int)(G / kMidSlice);
+    const int64_t nblk = (N + 255) / 256;
+    const int64_t cmax = RM;
+    const int64_t total = expert_prefix(E, pfx, kMidThreads, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return (c > 16 && c <= kSmallRows) ? nblk : 0;
+        return (c > cmin && c <= cmax) ? nblk : 0;
     });
     const int64_t u0 = total * blockIdx.x / gridDim.x, u1 = total * (blockIdx.x + 1) / gridDim.x;
-    const __amdgpu_buffer_rsrc_t qa_rs = make_rsrc(qa);
-    const bool hi8 = (lane & 8) != 0;
-    const int lchunk = ((lane >> 3) & 1) * 64 + kq * 16;
-    int aoff[2][2];  // [group of the window][fragment half]: swizzled chunk offset in a 256-byte window
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) aoff[h][j] = ((8 * h + 2 * kq + j) ^ (lane & 15)) * 16;
-    float *red = reinterpret_cast<float *>(dsm);  // [tile slot][fragment][r][lane], aliases the buffers
-    int staged_e = -1;
-    int bufc = 0;  // running slice-buffer counter
+    if (u0 >= u1) return;  // the whole workgroup
 
-    for (int64_t u = u0; u < u1;) {
-        const int e = find_expert(pfx, E, u);
-        const int64_t blk = u - pfx[e];
-        const int64_t blk_end = (blk + (u1 - u) < nblk) ? blk + (u1 - u) : nblk;
-        u += blk_end - blk;
-        const int64_t s0 = clamp_slots(offsets[e], max_slots);
-        const int rows = (int)(clamp_slots(offsets[e + 1], max_slots) - s0);
-        const int mt = (rows + 15) / 16;
-        if (e != staged_e) {
-            __syncthreads();
-            if (tid < 64) {
-                int32_t row = -1;
-                if (tid < rows) {
-                    const int64_t r = row_index ? (int64_t)row_index[s0 + tid] : s0 + tid;
-                    row = (r >= 0 && r < R) ? (int32_t)r : -1;
-                }
-                srow[tid] = row;
-                sasc[tid] = row >= 0 ? a_scale[row] : 0.0f;
-            }
-            __syncthreads();
-            staged_e = e;
-        }
-        const uint8_t *wpk = packed + (int64_t)e * N * (K / 2);
-        const uint16_t *wsc = scale + (int64_t)e * G * N, *wzp = zp + (int64_t)e * G * N;
-        const int64_t t0 = blk * per_round;
-        const int64_t t1 = (blk_end * per_round < ntiles) ? blk_end * per_round : ntiles;
+    struct Unit {
+        int e;
+        int64_t s0, c;                 // slot base, slots
+        bool store;                    // this lane's column is inside [0, N)
+        int64_t col;                   // this lane's column (clamped into [0, N))
+        __amdgpu_buffer_rsrc_t rw, rs, rz;  // the expert's codes, scales, zero points
+        uint32_t vw, vs;               // this lane's byte offsets in them (group 0)
+    };
+    auto unit_of = [&](int64_t u) {
+        Unit x;
+        x.e = find_expert(pfx, E, u);
+        const int64_t b = u - pfx[x.e];
+        x.s0 = clamp_slots(offsets[x.e], max_slots);
+        x.c = clamp_slots(offsets[x.e + 1], max_slots) - x.s0;
+        const int64_t col = b * 256 + wave * 32 + (lane & 31);
+        x.store = col < N;
+        x.col = col < N ? col : N - 1;
+        x.rw = make_rsrc(packed + (int64_t)x.e * N * (K / 2));
+        x.rs = make_rsrc(scale + (int64_t)x.e * G * N);
+        x.rz = make_rsrc(zp + (int64_t)x.e * G * N);
+        x.vw = (uint32_t)(x.col * (K / 2) + 32 * h);
+        x.vs = (uint32_t)(x.col * 2);
+        return x;
+    };
+    // activation row of slot row r of a unit (rows past the expert read row 0: never stored)
+    auto qa_row = [&](const Unit &x, int r) -> int64_t {
+        if (r >= x.c) return 0;
+        const int64_t q = row_index ? (int64_t)row_index[x.s0 + r] : x.s0 + r;
+        return (q >= 0 && q < R) ? q : 0;
+    };
+    auto row_scale = [&](const Unit &x, int r) -> float {
+        if (r >= x.c) return -1.0f;
+        const int64_t q = row_index ? (int64_t)row_index[x.s0 + r] : x.s0 + r;
+        return (q >= 0 && q < R) ? a_scale[q] : -1.0f;
+    };
 
-        // weight window ring over this wave's (tile, window of its half) sequence
-        const int64_t colbyte = (int64_t)(lane & 7) * (K / 2) + lchunk;
-        const uint16_t *szbase = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
-        v4u rb0[U], rb1[U];
-        uint16_t rsz[U];
-        auto load_window = [&](int uu, int64_t tile, int64_t w) {
-            const uint8_t *b = wpk + tile * 16 * (K / 2) + colbyte;
-            rb0[uu] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b) + w * 8);
-            rb1[uu] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b + 8 * (K / 2)) + w * 8);
-            rsz[uu] = szbase[tile * 16 + 2 * w * N];
-        };
-        // every wave runs the ring (an idle wave re-reads a valid window), so every
-        // wave issues the same number of loads per window, which the waits rely on
-        const int64_t tlast = t1 - 1;
-        {
-            const int64_t tile = t0 + tslot < t1 ? t0 + tslot : tlast;
+    // ---- activation staging: thread -> (row srow_t, bytes [spart * 16 NV, +16 NV) of a
+    // slice); offsets stay below 2^32 (R * K < 2^32 is required)
+    const int srow_t = tid / TPR, spart = tid % TPR;
+    const __amdgpu_buffer_rsrc_t rqa = make_rsrc(qa);
+    v4u st[NV];
+    auto load_slice = [&](int64_t qrow, int j) {
+        const uint32_t vo = (uint32_t)(qrow * K) + spart * (16 * NV);
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                __builtin_amdgcn_sched_barrier(0);
-                load_window(uu, tile, half * nwh + uu);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < NV; ++i)
+            st[i] = __builtin_amdgcn_raw_buffer_load_b128(rqa, vo + 16 * i, j * (kMidSlice * G128), 0);
+    };
+    auto store_slice = [&](int b) {
+        v4u *dst = reinterpret_cast<v4u *>(dsm + b * BUF + srow_t * kMidRow + spart * (16 * NV));
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const v4u v = st[i];
+            dst[i] = v4u{__builtin_amdgcn_perm(v.y, v.x, 0x06040200u), __builtin_amdgcn_perm(v.y, v.x, 0x07050301u),
+                         __builtin_amdgcn_perm(v.w, v.z, 0x06040200u), __builtin_amdgcn_perm(v.w, v.z, 0x07050301u)};
         }
-        // slice s of the current round -> buffer b: rows x halves x kD64S windows
-        auto stage_slice = [&](int s, int b) {
-            uint8_t *dst = dsm + b * kD64Buf;
-            for (int i = wave; i < rows; i += kDecWaves) {  // instruction i: row i, both halves
-                const int hh = lane >> 5, j = (lane & 31) >> 4, c = lane & 15;
-                const int32_t row = srow[i] >= 0 ? srow[i] : 0;
-                const int64_t wglob = (int64_t)hh * nwh + (int64_t)s * kD64S + j;
-                const uint32_t off = (uint32_t)((int64_t)row * K + wglob * 256 + ((c ^ (i & 15)) * 16));
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(qa_rs, (lds_ptr_t)(dst + i * 1024), 16, (int)off, 0, 0, 0);
-            }
-        };
+    };
 
-        for (int64_t tb = t0; tb < t1; tb += per_round) {
-            const int64_t tile = tb + tslot;
-            const bool active = tile < t1;
-            const int64_t ctile = active ? tile : tlast;
-            const int64_t ntile = tile + per_round < t1 ? tile + per_round : ctile;
-            // round prologue: slice 0 (buffers are free: the previous round ended with a barrier)
-            stage_slice(0, bufc & 1);
-            __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 0));
-            __syncthreads();
-            float acc[MT][4];
+    // ---- weight ring: U groups in flight per wave (cached loads: the other half of each
+    // 128-byte line, the next group, is read a few groups later from L2)
+    v4u rw0[U], rw1[U];
+    uint16_t rs[U], rz[U];
+    auto load_group = [&](int slot, const Unit &x, int64_t g) {
+        const int gw = (int)(g * (G128 / 2)), gs2 = (int)(g * N * 2);
+        rw0[slot] = __builtin_amdgcn_raw_buffer_load_b128(x.rw, x.vw, gw, 0);
+        rw1[slot] = __builtin_amdgcn_raw_buffer_load_b128(x.rw, x.vw + 16, gw, 0);
+        rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(x.rs, x.vs, gs2, 0);
+        rz[slot] = __builtin_amdgcn_raw_buffer_load_b16(x.rz, x.vs, gs2, 0);
+    };
+    // the same without a branch between the two units (the memory-counter waits stay exact)
+    auto load_group_sel = [&](int slot, bool here, const Unit &a, const Unit &b, int64_t ga, int64_t gb) {
+        const int64_t g = here ? ga : gb;
+        const int gw = (int)(g * (G128 / 2)), gs2 = (int)(g * N * 2);
+        const __amdgpu_buffer_rsrc_t rw = here ? a.rw : b.rw, rsc = here ? a.rs : b.rs, rzp = here ? a.rz : b.rz;
+        const uint32_t vw = here ? a.vw : b.vw, vs = here ? a.vs : b.vs;
+        rw0[slot] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw, gw, 0);
+        rw1[slot] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw + 16, gw, 0);
+        rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(rsc, vs, gs2, 0);
+        rz[slot] = __builtin_amdgcn_raw_buffer_load_b16(rzp, vs, gs2, 0);
+    };
+
+    int64_t u = u0;
+    Unit cur = unit_of(u);
+    int64_t qrow = qa_row(cur, srow_t);
+    if (tid < RM) sasc[u & 1][tid] = row_scale(cur, tid);
 #pragma unroll
-            for (int f = 0; f < MT; ++f)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[f][r] = 0.0f;
-            int wi = 0;  // window index within this wave's half
-            for (int s = 0; s < nslice; ++s) {
-                const int b = bufc & 1;
-                if (s + 1 < nslice) stage_slice(s + 1, b ^ 1);
-                const uint8_t *abuf = dsm + b * kD64Buf + half * 512;
-#pragma unroll
-                for (int j = 0; j < kD64S; ++j, ++wi) {
-                    const int uu = j % U;  // U divides kD64S: the ring slot is known at compile time
-                    uint32_t xy[2][4];
-                    {
-                        const uint32_t r0[4] = {rb0[uu].x, rb0[uu].y, rb0[uu].z, rb0[uu].w};
-                        const uint32_t r1[4] = {rb1[uu].x, rb1[uu].y, rb1[uu].z, rb1[uu].w};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const uint32_t t1v = dpp_ror8(r1[i]);
-                            const uint32_t t0v = dpp_ror8(r0[i]);
-                            xy[0][i] = hi8 ? t1v : r0[i];
-                            xy[1][i] = hi8 ? r1[i] : t0v;
-                        }
-                    }
-                    uint32_t sz[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sz[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)(uint32_t)rsz[uu]);
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        // codes minus zero point as INT8 (SWAR, as in the tiled loop): with
-                        // four row fragments this costs less than the zero-point MFMAs
-                        const uint32_t zadd = zp_add_const((uint16_t)sz[2 + h]);
-                        uint32_t q[8];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            spread8(xy[h][i], q[2 * i], q[2 * i + 1]);
-                            q[2 * i] = (q[2 * i] + zadd) ^ 0x80808080u;
-                            q[2 * i + 1] = (q[2 * i + 1] + zadd) ^ 0x80808080u;
-                        }
-                        const v4i bq0 = {(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
-                        const v4i bq1 = {(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
-                        float sc = half_bits_to_float((uint16_t)sz[h]);
-                        __asm__ volatile("" : "+v"(sc));
-#pragma unroll
-                        for (int f = 0; f < MT; ++f) {
-                            if (f >= mt) break;  // fragments past the expert's rows (wave-uniform)
-                            __builtin_amdgcn_sched_barrier(0);  // one fragment at a time: register budget
-                            const uint8_t *ar = abuf + (f * 16 + (lane & 15)) * 1024 + j * 256;
-                            const v4i a0 = *reinterpret_cast<const v4i *>(ar + aoff[h][0]);
-                            const v4i a1 = *reinterpret_cast<const v4i *>(ar + aoff[h][1]);
-                            v4i d = {0, 0, 0, 0};
-                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
-                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq1, d, 0, 0, 0);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) acc[f][r] = fmaf(sc, (float)d[r], acc[f][r]);
-                        }
-                    }
-                    // refill: window wi + U of this tile, else of the next tile (same half)
-                    const int wa = wi + U;
-                    const bool here = wa < nwh;
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_window(uu, here ? ctile : ntile, half * nwh + (here ? wa : (ntile != ctile ? wa - nwh : nwh - 1)));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // the next slice's rows (issued before this slice's refills) must have landed
-                __builtin_amdgcn_s_waitcnt(t3_waitcnt(3 * kD64S, 0));
-                __asm__ volatile("" ::: "memory");
-                __builtin_amdgcn_s_barrier();
-                __asm__ volatile("" ::: "memory");
-                ++bufc;
-            }
-            // K halves: half 1 leaves its sums in LDS, half 0 adds them and stores
-            if (half == 1) {
-#pragma unroll
-                for (int f = 0; f < MT; ++f)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) red[((tslot * MT + f) * 4 + r) * 64 + lane] = acc[f][r];
-            }
-            __syncthreads();
-            if (half == 0 && active) {
-                // row and column of each value computed here (an opaque copy of the lane
-                // index keeps the compiler from precomputing the 16 row offsets for the
-                // whole kernel, which would not fit the register budget)
-                int ln = lane;
-                __asm__ volatile("" : "+v"(ln));
-                const int kq2 = ln >> 4;
-                float *ocol = out + tile * 16 + (ln & 15);
-#pragma unroll
-                for (int f = 0; f < MT; ++f)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int m = f * 16 + 4 * kq2 + r;
-                        const float v = acc[f][r] + red[((tslot * MT + f) * 4 + r) * 64 + ln];
-                        if (m < rows && srow[m] >= 0) ocol[(s0 + m) * N] = sasc[m] * v;
-                    }
-            }
-            __syncthreads();
-        }
-        // drain the ring's last loads before the next unit reuses the registers' targets
-        __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 0));
+    for (int i = 0; i < U; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(i, cur, i);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_slice(qrow, 0);
+    store_slice(0);
+    __syncthreads();
+    int q = 0;  // running slice counter: slice q reads buffer q & 1
+    for (;;) {
+        const bool more = u + 1 < u1;
+        const Unit nxt = more ? unit_of(u + 1) : cur;
+        const int64_t nqrow = more ? qa_row(nxt, srow_t) : qrow;
+        const float nasc = (more && tid < RM) ? row_scale(nxt, tid) : 0.0f;
+        // 32-row fragments that hold rows of this expert (wave-uniform)
+        const int mt = cur.c > 32 ? MF : 1;
+        float acc[MF][16];
+#pragma unroll
+        for (int f = 0; f < MF; ++f)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[f][i] = 0.0f;
+        for (int j = 0; j < nsl; ++j) {
+            const bool last = j + 1 == nsl;
+            const bool stage_next = !last || more;
+            if (stage_next) load_slice(last ? nqrow : qrow, last ? 0 : j + 1);
+            const uint8_t *abuf = dsm + (q & 1) * BUF + (lane & 31) * kMidRow + 64 * h;
+#pragma unroll
+            for (int gs = 0; gs < kMidSlice; ++gs) {
+                const int slot = gs % U;
+                const int64_t g = (int64_t)j * kMidSlice + gs;
+                const uint32_t zadd = zp_add_const(rz[slot]);
+                float sc = half_bits_to_float(rs[slot]);
+                __asm__ volatile("" : "+v"(sc));
+                const uint32_t d8[8] = {rw0[slot].x, rw0[slot].y, rw0[slot].z, rw0[slot].w,
+                                        rw1[slot].x, rw1[slot].y, rw1[slot].z, rw1[slot].w};
+                v16i dacc[MF];
+#pragma unroll
+                for (int f = 0; f < MF; ++f)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) dacc[f][i] = 0;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const uint32_t a0 = d8[2 * s4], a1 = d8[2 * s4 + 1];
+                    const v4i bq = {(int)(((a0 & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u),
+                                    (int)((((a0 >> 4) & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u),
+                                    (int)(((a1 & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u),
+                                    (int)((((a1 >> 4) & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u)};
+#pragma unroll
+                    for (int f = 0; f < MF; ++f) {
+                        if (f >= mt) break;
+                        const v4i av = *reinterpret_cast<const v4i *>(abuf + f * 32 * kMidRow + gs * G128 + 16 * s4);
+                        dacc[f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bq, dacc[f], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < MF; ++f) {
+                    if (f >= mt) break;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[f][i] = fmaf(sc, (float)dacc[f][i], acc[f][i]);
+                }
+                // refill: group g + U of this unit, else of the next one (the last unit
+                // re-reads its own first groups, which nothing consumes)
+                const int64_t ga = g + U;
+                __builtin_amdgcn_sched_barrier(0);
+                load_group_sel(slot, ga < G, cur, nxt, ga, ga - G);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (last && more && tid < RM) sasc[(u + 1) & 1][tid] = nasc;
+            if (stage_next) store_slice((q + 1) & 1);
+            __syncthreads();
+            ++q;
+        }
+        // outputs of this unit: lane holds column col, rows f*32 + 8*(i/4) + 4*h + i%4
+        // (an opaque copy of the lane index keeps the compiler from computing the row
+        // addresses before the slice loop, where they would hold registers throughout)
+        if (cur.store) {
+            int ln = lane;
+            __asm__ volatile("" : "+v"(ln));
+            const int h2 = ln >> 5;
+            float *ocol = out + cur.s0 * N + cur.col;
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (f >= mt) break;
+                    const int r = f * 32 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+                    const float as = sasc[u & 1][r];
+                    if (as >= 0.0f) ocol[(int64_t)r * N] = as * acc[f][i];
+                }
+        }
+        if (!more) break;
+        ++u;
+        cur = nxt;
+        qrow = nqrow;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the ring's last (unused) loads
 }
 
 template <int WM, int WN>
@@ -1493,13 +1496,17 @@ static hipError_t launch_grouped_tiled_t(const int8_t *qa, const float *a_scale,
     return hipGetLastError();
 }
 
+// experts with more than cmin slots
 static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                        const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                        const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                                       float *out, int cus, hipStream_t stream) {
-    hipError_t err = launch_grouped_tiled_t<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp,
-                                                  N, max_slots, out, kSmallRows, 128, cus, stream);
-    if (err != hipSuccess || max_slots <= 128) return err;
+                                       float *out, int64_t cmin, int cus, hipStream_t stream) {
+    if (max_slots <= cmin) return hipSuccess;
+    if (cmin < 128) {
+        hipError_t err = launch_grouped_tiled_t<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
+                                                      zp, N, max_slots, out, cmin, 128, cus, stream);
+        if (err != hipSuccess || max_slots <= 128) return err;
+    }
     return launch_grouped_tiled_t<4, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
                                         max_slots, out, 128, INT64_MAX, cus, stream);
 }
@@ -1514,9 +1521,10 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     const int64_t G = K / G128;
     if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax) {
         const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
-        // experts with 17..64 slots: one weight pass over K slices when the slicing fits
-        const bool d64 = G % (4 * kD64S) == 0 && (int64_t)R * K < (1ll << 32);
-        const int small_max = d64 ? 16 : (int)kSmallRows;
+        // experts with 17..64 slots: one weight pass with all their rows when the K
+        // slicing fits (at least two slices; activation offsets below 2^32)
+        const bool mid = G % kMidSlice == 0 && G >= 2 * kMidSlice && (int64_t)R * K < (1ll << 32);
+        const int small_max = mid ? 16 : (int)kSmallRows;
 #define W4A8_GDEC(UU, SS)                                                                                           \
     do {                                                                                                            \
         const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + dec_red_bytes(SS));                 \
@@ -1540,18 +1548,25 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
 #undef W4A8_GDEC
         hipError_t derr = hipGetLastError();
         if (derr != hipSuccess) return derr;
-        // the other two loops only when some expert can have more than 16 slots
-        if (d64 && max_slots > 16) {
-            if (hipFuncSetAttribute((const void *)grouped_decode64_kernel<2>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kD64Lds) != hipSuccess)
-                return hipGetLastError();
-            hipLaunchKernelGGL((grouped_decode64_kernel<2>), dgrid, dblock, kD64Lds, stream, qa, a_scale, R,
-                               row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
-            if ((derr = hipGetLastError()) != hipSuccess) return derr;
-        }
-        if (max_slots <= kSmallRows) return hipSuccess;
+        if (!mid) return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
+                                              max_slots, out, kSmallRows, cus, stream);
+        // the other loops only when some expert can have that many slots
+#define W4A8_GMID(MF, CMIN)                                                                                         \
+    do {                                                                                                            \
+        if (max_slots > (CMIN)) {                                                                                   \
+            if (hipFuncSetAttribute((const void *)grouped_mid_kernel<MF, 4>,                                        \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes(MF)) != hipSuccess) \
+                return hipGetLastError();                                                                           \
+            hipLaunchKernelGGL((grouped_mid_kernel<MF, 4>), dim3((uint32_t)cus), dim3(kMidThreads),                \
+                               (size_t)mid_lds_bytes(MF), stream, qa, a_scale, R, row_index, expert_offsets, E, K,   \
+                               packed, scale, zp, N, max_slots, out, (int64_t)(CMIN));                              \
+            if ((derr = hipGetLastError()) != hipSuccess) return derr;                                              \
+        }                                                                                                           \
+    } while (0)
+        W4A8_GMID(2, 16);
+#undef W4A8_GMID
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, cus, stream);
+                                    out, 64, cus, stream);
     }
     const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
@@ -1565,9 +1580,9 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         hipLaunchKernelGGL(grouped_stream_kernel<1>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
                            expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || max_slots <= kSmallRows) return err;
+    if (err != hipSuccess) return err;
     return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
-                                cus, stream);
+                                kSmallRows, cus, stream);
 }
 
 }  // namespace w4a8
