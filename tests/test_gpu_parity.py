@@ -138,6 +138,8 @@ SHAPES = [  # (M, N, K, paths)
     (3, 48, 384, ALL),
     (16, 272, 1024, ALL),
     (8, 336, 2048, ALL),        # decode with four K parts per tile and two windows in flight
+    (5, 96, 4096, (1,)),        # decode, rows staged eight loads per thread, the last batch partial
+    (16, 64, 8704, (1,)),       # decode, rows too long for one staging batch (staged in a loop)
     (17, 64, 256, ALL),
     (33, 32, 512, ALL),
     (64, 16, 128, ALL),

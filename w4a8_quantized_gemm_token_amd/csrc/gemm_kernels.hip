@@ -415,6 +415,9 @@ __host__ __device__ inline int64_t dec_lds_bytes(int64_t M, int64_t K) { return 
 // partial sums of K parts 1..split-1 of one round: [part][tile][4][64] fp32
 __host__ __device__ inline int64_t dec_red_bytes(int split) { return (int64_t)(split - 1) * (kDecWaves / split) * 1024; }
 constexpr int64_t kDecLdsMax = 140 * 1024;
+// packed bytes of one matrix the decode loop can address (32-bit buffer offsets; the
+// offset 0xFFFFFFF0 must stay past the end)
+constexpr int64_t kDecCodesMax = 0xFFFFFFF0ll;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -450,8 +453,9 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
 // Tiles [t0, t1) of 16 columns for the M <= 16 activation rows staged in `rows`
 // (row stride K + 16).  `store(m, col, v)` receives a_scale-free fp32 sums; with
 // ISUMS the per-group int32 sums go to isums[g][m][col] instead.
-// `stage()` runs after the first weight windows are issued (so their latency overlaps
-// it) and is followed by a workgroup barrier: it fills `rows` when they change.
+// `stage(0)` runs before the first weight windows are issued and may start loading the
+// rows; `stage(1)` runs after them (so their latency overlaps it) and is followed by a
+// workgroup barrier: it fills `rows` when they change.
 template <int U, int SPLIT, bool ISUMS, typename Stage, typename Store>
 __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M, int64_t K,
                                           const uint8_t *__restrict__ wpk, const uint16_t *__restrict__ wsc,
@@ -474,28 +478,40 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
     // Each wave streams tile t0 + wave / SPLIT, then the tile per_round further, and so
     // on; the window ring runs on across tiles, so the first windows of a wave's
     // next tile are already in flight while it finishes the current one.
-    const int64_t colbyte = (int64_t)(lane & 7) * (K / 2) + lchunk;
+    // Codes are read through a range-checked buffer over the N x K/2 packed bytes (its
+    // size is below 2^32, which the launcher checks): 32-bit offsets, and an offset past
+    // the end reads zeros without touching memory.
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wpk), (short)0, (int)(N * (K / 2)), 0x00020000);
+    const uint32_t colbyte = (uint32_t)((lane & 7) * (K / 2) + lchunk);
     const uint16_t *szbase = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
     v4u rb0[U], rb1[U];
     uint32_t rsz[U];
     auto load_window = [&](int u, int64_t tile, int64_t w) {
-        const uint8_t *b = wpk + tile * 16 * (K / 2) + colbyte;
-        rb0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b) + w * 8);
-        rb1[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(b + 8 * (K / 2)) + w * 8);
+        const uint32_t o = (uint32_t)(tile * 16 * (K / 2)) + colbyte + (uint32_t)w * 128;
+        rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
+        rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o + (uint32_t)(8 * (K / 2)), 0, 2);
         rsz[u] = szbase[tile * 16 + 2 * w * N];
     };
+    stage(0);  // issue the staging loads (older than the ring's, so waiting for them does not wait for the weights)
     {
-        const int64_t tile = t0 + wave / SPLIT;
-        if ((wave / SPLIT) < per_round && tile < t1) {
+        // every wave issues its first windows, with no branch (so the memory-counter waits
+        // for the staged rows stay exact); a wave without a tile reads past the end of
+        // the codes (zeros, no memory traffic) and its scales from a valid tile
+        const bool has = (wave / SPLIT) < per_round && t0 + wave / SPLIT < t1;
+        const int64_t tile = has ? t0 + wave / SPLIT : t0;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                __builtin_amdgcn_sched_barrier(0);
-                load_window(u, tile, win0 + u);
-            }
+        for (int u = 0; u < U; ++u) {
             __builtin_amdgcn_sched_barrier(0);
+            const uint32_t o = has ? (uint32_t)(tile * 16 * (K / 2)) + colbyte + (uint32_t)(win0 + u) * 128 : 0xFFFFFFF0u;
+            const uint32_t o1 = has ? o + (uint32_t)(8 * (K / 2)) : 0xFFFFFFF0u;
+            rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
+            rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, 2);
+            rsz[u] = szbase[tile * 16 + 2 * (win0 + u) * N];
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    stage();
+    stage(1);
     __syncthreads();
     for (int64_t tb = t0; tb < t1; tb += per_round) {
         const int64_t tile = tb + wave / SPLIT;
@@ -597,7 +613,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
     }
 }
 
-template <int U, int SPLIT, bool ISUMS>
+template <int U, int SPLIT, bool ISUMS, int SB>
 __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *__restrict__ qa,
                                                                  const float *__restrict__ a_scale, int64_t M,
                                                                  int64_t K, const uint8_t *__restrict__ wpk,
@@ -606,23 +622,50 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
                                                                  int64_t tiles_per_wg, float *__restrict__ out,
                                                                  int32_t *__restrict__ isums) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ float sasc[16];  // row scales (no global load, and no wait, at the stores)
     const int64_t lda = K + 16;
     const int64_t ntiles = N / 16;
     const int64_t t0 = (int64_t)blockIdx.x * tiles_per_wg;
     const int64_t t1 = (t0 + tiles_per_wg < ntiles) ? t0 + tiles_per_wg : ntiles;
     float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(M, K) + 15) / 16) * 16);
+    constexpr int kStageBatch = SB;  // staging loads per thread issued at once
+    const bool batched = M * K <= (int64_t)kStageBatch * kDecThreads * 16;
+    v4u stg[kStageBatch];
+    float asc = 0.0f;
     dec_tiles<U, SPLIT, ISUMS>(
         dsm, red, (int)M, K, wpk, wsc, wzp, N, t0, t1,
-        [&]() {  // qa[M][K] -> LDS, 16-byte pieces through registers (measured a little
-                 // faster here than loads straight to LDS, whose wait would also cover
-                 // the weight loads just issued)
-            const int64_t pieces = M * (K / 16);
-            for (int64_t i = threadIdx.x; i < pieces; i += kDecThreads) {
-                const int64_t r = i / (K / 16), c = i % (K / 16);
-                *reinterpret_cast<v4u *>(dsm + r * lda + c * 16) = reinterpret_cast<const v4u *>(qa + r * K)[c];
+        [&](int phase) {  // qa[M][K] -> LDS, 16-byte pieces through registers
+            if (phase == 0) {
+                // up to eight pieces per thread in flight at once; pieces past the end
+                // read as zeros (buffer range check) and are not stored
+                if (batched) {
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<int8_t *>(qa), (short)0, (int)(M * K), 0x00020000);
+#pragma unroll
+                    for (int j = 0; j < kStageBatch; ++j)
+                        stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * ((int)threadIdx.x + j * kDecThreads), 0, 0);
+                }
+                if (!ISUMS && threadIdx.x < M) asc = a_scale[threadIdx.x];
+                return;
             }
+            if (batched) {
+                // piece i sits at byte 16 i of qa and at 16 (i + i / (K / 16)) in LDS
+                const int kp = (int)(K / 16), pieces = (int)M * kp;
+#pragma unroll
+                for (int j = 0; j < kStageBatch; ++j) {
+                    const int i = (int)threadIdx.x + j * kDecThreads;
+                    if (i < pieces) *reinterpret_cast<v4u *>(dsm + 16 * (int64_t)(i + i / kp)) = stg[j];
+                }
+            } else {
+                const int64_t pieces = M * (K / 16);
+                for (int64_t i = threadIdx.x; i < pieces; i += kDecThreads) {
+                    const int64_t r = i / (K / 16), c = i % (K / 16);
+                    *reinterpret_cast<v4u *>(dsm + r * lda + c * 16) = reinterpret_cast<const v4u *>(qa + r * K)[c];
+                }
+            }
+            if (!ISUMS && threadIdx.x < M) sasc[threadIdx.x] = asc;
         },
-        [&](int m, int64_t col, float v) { out[m * N + col] = a_scale[m] * v; }, isums);
+        [&](int m, int64_t col, float v) { out[m * N + col] = sasc[m] * v; }, isums);
 }
 
 // Dense layer through the line-wide loop: a workgroup of SPLIT waves per 16-column tile.
@@ -1029,10 +1072,10 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
         }
         const uint8_t *wpk = packed + (int64_t)e * N * (K / 2);
         const uint16_t *wsc = scale + (int64_t)e * G * N, *wzp = zp + (int64_t)e * G * N;
-        auto stage = [&]() {  // the chunk's activation rows -> LDS (only when they changed);
-                              // rows outside [0, R) read row 0 and are never stored.  The row
-                              // scales load alongside (their latency overlaps the rows').
-            if (!restage) return;
+        auto stage = [&](int phase) {  // the chunk's activation rows -> LDS (only when they
+                                       // changed); rows outside [0, R) read row 0 and are
+                                       // never stored.  The row scales load alongside.
+            if (phase == 0 || !restage) return;
             stage_rows_dma(dsm, lda, qa, K, rows, [&](int r) { return (int64_t)(srow[r] >= 0 ? srow[r] : 0); });
             float asc = 0.0f;
             if (threadIdx.x < 16) {
@@ -1394,21 +1437,21 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
     const size_t lds = (size_t)(((dec_lds_bytes(M, K) + 15) / 16) * 16 + dec_red_bytes(split));
     const int64_t nwin = G / 2 / split;
     const dim3 grid((uint32_t)nwg), block(kDecThreads);
+    // rows staged with one load per thread when they fit, else eight at a time
+    const bool one = M * K <= (int64_t)kDecThreads * 16;
+#define W4A8_DEC1(UU, SS, IS, SB)                                                                                   \
+    do {                                                                                                            \
+        if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, IS, SB>,                                   \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)                \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, IS, SB>), grid, block, lds, stream, qa, a_scale, M, K,       \
+                           packed, scale, zp, N, tpw, out, isums);                                                  \
+    } while (0)
 #define W4A8_DEC(UU, SS)                                                                                            \
     do {                                                                                                            \
-        if (isums) {                                                                                                \
-            if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, true>,                                 \
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)            \
-                return hipGetLastError();                                                                           \
-            hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, true>), grid, block, lds, stream, qa, a_scale, M, K,     \
-                               packed, scale, zp, N, tpw, out, isums);                                              \
-        } else {                                                                                                    \
-            if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, false>,                                \
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)            \
-                return hipGetLastError();                                                                           \
-            hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, false>), grid, block, lds, stream, qa, a_scale, M, K,    \
-                               packed, scale, zp, N, tpw, out, isums);                                              \
-        }                                                                                                           \
+        if (isums) W4A8_DEC1(UU, SS, true, 8);                                                                      \
+        else if (one) W4A8_DEC1(UU, SS, false, 1);                                                                  \
+        else W4A8_DEC1(UU, SS, false, 8);                                                                           \
     } while (0)
     if (split == 4) {
         if (nwin % 2 == 0) W4A8_DEC(2, 4);
@@ -1421,6 +1464,7 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
         else W4A8_DEC(1, 1);
     }
 #undef W4A8_DEC
+#undef W4A8_DEC1
     return hipGetLastError();
 }
 
@@ -1438,7 +1482,8 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
     if (path == 1) {
         const int64_t G = K / G128;
         const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-        if (G % 2 == 0 && M <= 16 && dec_lds_bytes(M, K) <= kDecLdsMax)
+        // (the decode loop addresses the packed codes with 32-bit buffer offsets)
+        if (G % 2 == 0 && M <= 16 && dec_lds_bytes(M, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax)
             return launch_decode(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
         if (G % 2 == 0) {
             // line-wide loop: two-group windows, K split over two waves when it divides
@@ -1519,7 +1564,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
     const int64_t G = K / G128;
-    if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax) {
+    if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax) {
         const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
         // experts with 17..64 slots: one weight pass with all their rows when the K
         // slicing fits (at least two slices; activation offsets below 2^32)
