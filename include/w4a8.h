@@ -178,8 +178,10 @@ w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t to
  * row_index[s] (qa/a_scale row; row_index NULL means row s) with expert e's
  * packed weights, and writes out[s][0..N).  The per-expert slot counts stay on
  * the device: the kernel reads expert_offsets itself, so no host round trip
- * is needed between routing and the GEMM.  Experts with few slots take the
- * streaming loop, experts with many the tiled loop.
+ * is needed between routing and the GEMM.  Each expert takes the loop for its
+ * slot count: a streaming loop over 16-row chunks (up to 16 slots), one weight
+ * pass for all rows (17 to 64), or the tiled loop (more); all are launched only
+ * when max_slots allows an expert of that size.
  *   qa [R][K] i8 and a_scale [R] (R = rows of the activation matrix),
  *   packed [E][N][K/2], scale/zp [E][K/128][N], out [max_slots][N].
  * The caller guarantees expert_offsets[E] <= max_slots and row_index[s] < R

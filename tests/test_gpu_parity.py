@@ -329,6 +329,54 @@ def test_grouped_gemm_mixed_bucket_sizes(orc, K):
         check_close(out[s0:s1], ref, mag, f"expert {e} ({s1 - s0} slots)")
 
 
+@pytest.mark.parametrize("clamp", [0, 40])
+def test_grouped_gemm_size_class_edges(orc, clamp):
+    """Slot counts on both sides of every size class (16/17, 32/33, 64/65, 128/129),
+    N = 544 (two full 256-column blocks and a partial one), K = 2048 (16 groups, four
+    activation slices), so the loops cross units, chunks and experts inside one
+    workgroup's range.  Slots whose row index is outside [0, R) are not written, and
+    with `clamp` > 0 the slot count passed is smaller than the slots routed: slots at
+    and past it are ignored and nothing is written beyond the output rows."""
+    w4 = w4mod()
+    counts = [16, 17, 3, 32, 33, 0, 64, 65, 1, 128, 129]
+    E, N, K, R = len(counts), 544, 2048, 150
+    rng = np.random.default_rng(7)
+    S = sum(counts)
+    row_index = rng.integers(0, R, S).astype(np.int32)
+    bad = rng.choice(S, 6, replace=False)
+    row_index[bad[:3]] = R + 5
+    row_index[bad[3:]] = -1
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synthetic.activations(7, R, K)
+    qr, sr = orc.quantize_act(x)
+    packs, refs = [], []
+    for e in range(E):
+        W = synthetic.weights(7, synthetic.TAG_W, e, N, K)
+        packs.append(w4.pack_weights(W))
+        refs.append(orc.quantize_weights(W))
+    packed = to_dev(np.stack([p[0] for p in packs]))
+    scale = to_dev(np.stack([p[1] for p in packs]))
+    zp = to_dev(np.stack([p[2] for p in packs]))
+    qa, sc = w4.quantize_act(to_dev(x))
+    max_slots = S - clamp
+    import torch
+    full = torch.full((S + 8, N), float("nan"), dtype=torch.float32, device=cuda())
+    w4.moe_grouped_gemm(qa, sc, to_dev(row_index), to_dev(offsets), packed, scale, zp, max_slots=max_slots,
+                        out=full[:max_slots])
+    out = to_host(full)
+    assert np.isnan(out[max_slots:]).all(), "rows past max_slots were written"
+    valid = (row_index >= 0) & (row_index < R)
+    for e in range(E):
+        s0, s1 = min(offsets[e], max_slots), min(offsets[e + 1], max_slots)
+        if s0 == s1:
+            continue
+        ok = np.nonzero(valid[s0:s1])[0] + s0
+        assert np.isnan(out[s0:s1][~valid[s0:s1]]).all(), f"expert {e}: slots with an invalid row were written"
+        q, s, z = refs[e]
+        ref, mag = orc.gemm(qr[row_index[ok]], sr[row_index[ok]], q, s, z)
+        check_close(out[ok], ref, mag, f"expert {e} ({offsets[e + 1] - offsets[e]} slots, max_slots {max_slots})")
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 512])
 def test_toy_moe_full_size_sampled(orc, B):
     """8 experts, top-1, K=4096, N=14336: route on the GPU, grouped GEMM, combine; the
