@@ -1092,10 +1092,11 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     }
 }
 
-// Experts with a middle number of slots (up to 32 * MF): one weight pass over all
-// their rows with full-rate 32x32x32 INT8 MFMAs.  A work unit is (expert, block of
-// 256 columns); a 512-thread workgroup takes a contiguous range of units, and wave w
-// owns the 32 columns [256 b + 32 w, +32) of the unit for all rows and all K.
+// Experts with a middle number of slots (cmin, cmax]: one weight pass per block of
+// 32 * MF of their rows with full-rate 32x32x32 INT8 MFMAs.  A work unit is (expert,
+// row block, block of 256 columns); a 512-thread workgroup takes a contiguous range of
+// units, and wave w owns the 32 columns [256 b + 32 w, +32) of the unit for all its
+// rows and all K.
 //
 // Weights go straight from memory to registers: lane l holds column l % 32 and, per
 // group, the packed bytes [32 h, 32 h + 32) (h = l / 32), i.e. codes 64 h + [0, 64) of
@@ -1119,7 +1120,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int64_t cmin) {
+    float *__restrict__ out, int64_t cmin, int64_t cmax) {
     constexpr int RM = 32 * MF;                    // staged rows
     constexpr int BUF = RM * kMidRow;
     constexpr int TPR = kMidThreads / RM;          // staging threads per row
@@ -1133,10 +1134,9 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     const int64_t G = K / G128;
     const int nsl = (int)(G / kMidSlice);
     const int64_t nblk = (N + 255) / 256;
-    const int64_t cmax = RM;
     const int64_t total = expert_prefix(E, pfx, kMidThreads, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return (c > cmin && c <= cmax) ? nblk : 0;
+        return (c > cmin && c <= cmax) ? ((c + RM - 1) / RM) * nblk : 0;
     });
     const int64_t u0 = total * blockIdx.x / gridDim.x, u1 = total * (blockIdx.x + 1) / gridDim.x;
     if (u0 >= u1) return;  // the whole workgroup
@@ -1152,9 +1152,12 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     auto unit_of = [&](int64_t u) {
         Unit x;
         x.e = find_expert(pfx, E, u);
-        const int64_t b = u - pfx[x.e];
-        x.s0 = clamp_slots(offsets[x.e], max_slots);
-        x.c = clamp_slots(offsets[x.e + 1], max_slots) - x.s0;
+        const int64_t local = u - pfx[x.e];
+        const int64_t rb = local / nblk, b = local % nblk;  // row block, column block
+        const int64_t e0 = clamp_slots(offsets[x.e], max_slots);
+        x.s0 = e0 + rb * RM;
+        const int64_t left = clamp_slots(offsets[x.e + 1], max_slots) - x.s0;
+        x.c = left < RM ? left : RM;
         const int64_t col = b * 256 + wave * 32 + (lane & 31);
         x.store = col < N;
         x.col = col < N ? col : N - 1;
@@ -1566,8 +1569,8 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     const int64_t G = K / G128;
     if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax) {
         const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
-        // experts with 17..64 slots: one weight pass with all their rows when the K
-        // slicing fits (at least two slices; activation offsets below 2^32)
+        // experts with 17..128 slots: one weight pass per 64 rows when the K slicing
+        // fits (at least two slices; activation offsets below 2^32)
         const bool mid = G % kMidSlice == 0 && G >= 2 * kMidSlice && (int64_t)R * K < (1ll << 32);
         const int small_max = mid ? 16 : (int)kSmallRows;
 #define W4A8_GDEC(UU, SS)                                                                                           \
@@ -1596,7 +1599,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         if (!mid) return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
                                               max_slots, out, kSmallRows, cus, stream);
         // the other loops only when some expert can have that many slots
-#define W4A8_GMID(MF, CMIN)                                                                                         \
+#define W4A8_GMID(MF, CMIN, CMAX)                                                                                       \
     do {                                                                                                            \
         if (max_slots > (CMIN)) {                                                                                   \
             if (hipFuncSetAttribute((const void *)grouped_mid_kernel<MF, 4>,                                        \
@@ -1604,14 +1607,14 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                 return hipGetLastError();                                                                           \
             hipLaunchKernelGGL((grouped_mid_kernel<MF, 4>), dim3((uint32_t)cus), dim3(kMidThreads),                \
                                (size_t)mid_lds_bytes(MF), stream, qa, a_scale, R, row_index, expert_offsets, E, K,   \
-                               packed, scale, zp, N, max_slots, out, (int64_t)(CMIN));                              \
+                               packed, scale, zp, N, max_slots, out, (int64_t)(CMIN), (int64_t)(CMAX));             \
             if ((derr = hipGetLastError()) != hipSuccess) return derr;                                              \
         }                                                                                                           \
     } while (0)
-        W4A8_GMID(2, 16);
+        W4A8_GMID(2, 16, 128);  // 65..128 slots: two row blocks, the weights read twice
 #undef W4A8_GMID
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, 64, cus, stream);
+                                    out, 128, cus, stream);
     }
     const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
