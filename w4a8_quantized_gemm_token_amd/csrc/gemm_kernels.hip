@@ -16,18 +16,24 @@
 // each byte n in [0,15] plus (0x80 - zp) stays inside [0x71, 0x8F], and xor 0x80
 // maps it to (n - zp) mod 256 -- the signed INT8 operand of the MFMA.
 //
-// Two main loops:
-//  * streaming (small M, HBM-bound): one wave owns 16 output columns and up to
-//    64 rows; it streams its columns' packed bytes with 128-bit loads, prefetched
-//    several groups ahead in registers, and feeds v_mfma_i32_16x16x64_i8
-//    directly from registers.  Workgroups are ordered so that neighbouring
-//    column tiles run on the same XCD (their scale/zp rows share cache lines).
-//  * tiled (large M, MFMA-bound): a 256-thread workgroup computes a 128x128
-//    tile; each group of 128 k is staged in LDS (double-buffered, padded rows),
-//    the weights are unpacked once per workgroup into LDS as INT8, and four
-//    waves each run a 64x64 sub-tile with v_mfma_i32_32x32x32_i8.
-// Both keep the per-group int32 sum in the MFMA accumulator and fold it into an
+// The loops:
+//  * decode (M <= 16, HBM-bound): one 1024-thread workgroup per CU stages the M
+//    activation rows in LDS; its 16 waves stream whole 128-byte lines of their
+//    columns' packed bytes through a ring in registers into
+//    v_mfma_i32_16x16x64_i8, each 16-column tile split over two or four K parts.
+//  * streaming (16 < M <= 64, or an odd group count): one wave owns 16 output
+//    columns and all rows, activations read from memory.
+//  * tiled (large M, MFMA-bound): a 512-thread workgroup computes a 256x128 tile
+//    (or 256 threads a 128x128 one); each group of 128 k is staged in LDS
+//    (double-buffered, padded rows), the weights are unpacked once per workgroup
+//    into LDS as INT8, and each wave runs a 64x64 sub-tile with
+//    v_mfma_i32_32x32x32_i8.
+//  * expert-grouped forms of these, plus a weight-streaming loop on
+//    v_mfma_i32_32x32x32_i8 for experts with 17..128 slots (see below).
+// All keep the per-group int32 sum in the MFMA accumulator and fold it into an
 // fp32 accumulator with one fma per element per group, groups in increasing g.
+// Workgroups are ordered so that neighbouring column tiles run on the same XCD
+// (their scale/zp rows share cache lines).
 #include <algorithm>
 #include <type_traits>
 
@@ -930,10 +936,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *
 }
 
 // ------------------------------------------------------------------ expert-grouped forms
-// Experts with at most kSmallRows slots take the streaming loop (one 64-row
-// chunk, MT chosen from the count), larger experts the tiled loop.  Each
-// workgroup reads expert_offsets itself and walks a persistent unit list, so
-// the slot counts never travel to the host.
+// Each expert takes the loop for its slot count (the launcher picks the classes):
+// the decode loop up to 16 slots, the weight-streaming loop for 17..128, the tiled
+// loop above; when the group count rules the first two out, the streaming loop up to
+// kSmallRows slots and the tiled loop above.  Each workgroup reads expert_offsets
+// itself and walks a persistent unit list, so the slot counts never travel to the
+// host.
 constexpr int kSmallRows = 64;
 constexpr int kMaxExperts = 1024;
 
@@ -1018,7 +1026,7 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
     }
 }
 
-// Experts with at most kSmallRows slots, decode style: one 1024-thread workgroup
+// Experts with at most small_max slots, decode style: one 1024-thread workgroup
 // per CU stages 16 gathered activation rows of one expert in LDS and streams
 // 16-column tiles of that expert's weights (the loop of the dense decode kernel).
 // Work units are (expert, 16-row chunk, tile); each workgroup takes a contiguous
@@ -1357,10 +1365,6 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
     }
 }
 
-#ifndef W4A8_STREAM_U1
-#define W4A8_STREAM_U1 2
-#endif
-
 template <int MT, int U, int SPLIT>
 hipError_t launch_stream2_t(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                             const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
@@ -1387,9 +1391,6 @@ hipError_t launch_stream2(int mt, int u, int split, const int8_t *qa, const floa
                           const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, float *out,
                           int32_t *isums, hipStream_t stream) {
     if (mt == 1) {
-        if (u >= 4 && W4A8_STREAM_U1 >= 4)
-            return launch_stream2_s<1, (W4A8_STREAM_U1 >= 4 ? 4 : 1)>(split, qa, a_scale, M, K, packed, scale, zp, N,
-                                                                        out, isums, stream);
         if (u >= 2) return launch_stream2_s<1, 2>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
         return launch_stream2_s<1, 1>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     }
@@ -1492,7 +1493,7 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
             // line-wide loop: two-group windows, K split over two waves when it divides
             const int split = (G % 4 == 0) ? 2 : 1;
             const int64_t nwin = G / 2 / split;
-            const int u = ring_depth(nwin, mt == 1 ? W4A8_STREAM_U1 : (mt == 2 ? 2 : 1));
+            const int u = ring_depth(nwin, mt == 4 ? 1 : 2);
             return launch_stream2(mt, u, split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
         }
         const dim3 grid((uint32_t)(N / 16)), block(kStreamThreads);
@@ -1527,8 +1528,8 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
     return hipGetLastError();
 }
 
-// Experts with more than kSmallRows slots: 128-row tiles up to 128 slots, 256-row
-// tiles above (a 256-row tile over a 65..128-slot expert would waste most of its work).
+// Experts with more than cmin slots: 128-row tiles up to 128 slots, 256-row tiles
+// above (a 256-row tile over a 65..128-slot expert would waste most of its work).
 template <int WM, int WN>
 static hipError_t launch_grouped_tiled_t(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                          const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
