@@ -377,6 +377,38 @@ def test_grouped_gemm_size_class_edges(orc, clamp):
         check_close(out[ok], ref, mag, f"expert {e} ({offsets[e + 1] - offsets[e]} slots, max_slots {max_slots})")
 
 
+def test_grouped_gemm_weight_streaming_loop(orc):
+    """Experts with 17..128 slots and enough column blocks (N = 9216: 36 blocks of 256,
+    396 units) that the weight-streaming loop runs rather than handing them to the
+    decode loop; three whole column blocks (first, middle, last) checked per expert."""
+    w4 = w4mod()
+    counts = [17, 40, 64, 65, 100, 128, 20, 33]
+    E, N, K, R = len(counts), 9216, 1024, 300
+    rng = np.random.default_rng(11)
+    S = sum(counts)
+    row_index = rng.integers(0, R, S).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synthetic.activations(11, R, K)
+    qr, sr = orc.quantize_act(x)
+    cols = np.concatenate([np.arange(0, 256), np.arange(17 * 256, 18 * 256), np.arange(N - 256, N)])
+    packs, refs = [], []
+    for e in range(E):
+        W = synthetic.weights(11, synthetic.TAG_W, e, N, K)
+        packs.append(w4.pack_weights(W))
+        q, s_, z = orc.quantize_weights(W[cols])
+        refs.append((q, s_, z))
+    packed = to_dev(np.stack([p[0] for p in packs]))
+    scale = to_dev(np.stack([p[1] for p in packs]))
+    zp = to_dev(np.stack([p[2] for p in packs]))
+    qa, sc = w4.quantize_act(to_dev(x))
+    out = to_host(w4.moe_grouped_gemm(qa, sc, to_dev(row_index), to_dev(offsets), packed, scale, zp, max_slots=S))
+    for e in range(E):
+        s0, s1 = offsets[e], offsets[e + 1]
+        q, s_, z = refs[e]
+        ref, mag = orc.gemm(qr[row_index[s0:s1]], sr[row_index[s0:s1]], q, s_, z)
+        check_close(out[s0:s1][:, cols], ref, mag, f"expert {e} ({s1 - s0} slots)")
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 512])
 def test_toy_moe_full_size_sampled(orc, B):
     """8 experts, top-1, K=4096, N=14336: route on the GPU, grouped GEMM, combine; the

@@ -265,7 +265,7 @@ w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_
     W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");
     if (max_slots == 0 || R == 0) return W4A8_OK;
     return hip_status(launch_grouped_gemm(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
-                                          max_slots, out, stream),
+                                          max_slots, max_slots, out, stream),
                       "grouped_gemm launch");
 }
 
@@ -388,12 +388,13 @@ w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t
     if (T == 0) return W4A8_OK;
     if ((err = launch_quantize_act(x, T, H, H, qa, a_scale, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: quantize");
-    if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S,
+    // top-k picks distinct experts per token, so no expert (the shared one included) gets more than T slots
+    if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S, T,
                                    gu, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: gate/up grouped GEMM");
     if ((err = launch_silu_mul_quantize(gu, S, I, qh, h_scale, nullptr, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: silu*up requant");
-    if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E + 1, I, dn_packed, dn_scale, dn_zp, H, S, y,
+    if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E + 1, I, dn_packed, dn_scale, dn_zp, H, S, T, y,
                                    stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: down grouped GEMM");
     if ((err = launch_moe_combine(y, sop, w, y + P * H, T, topk, H, out, stream)) != hipSuccess)

@@ -944,6 +944,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *
 // host.
 constexpr int kSmallRows = 64;
 constexpr int kMaxExperts = 1024;
+// slot-count class of the weight-streaming loop: (kMidMin, kMidMax], 64-row blocks
+// of 256 columns as work units
+constexpr int kMidMin = 16, kMidMax = 128, kMidRows = 64;
 
 // Exclusive prefix over experts of units(e) into lds_pfx[0..E]; returns the
 // total.  Run by the whole workgroup (nthreads = blockDim.x <= 1024): thread t
@@ -994,6 +997,23 @@ __device__ __forceinline__ int64_t clamp_slots(int64_t v, int64_t max_slots) {
     return v < 0 ? 0 : (v > max_slots ? max_slots : v);
 }
 
+// Work units of the weight-streaming loop's slot class.  When they are too few for the
+// machine (a lone mid-size expert, say), that loop would leave most CUs idle; the
+// decode loop then takes those experts in 16-row chunks instead.  Both
+// kernels compute this from the device-side offsets, so they agree without the host.
+// Uses lds_pfx as scratch (as expert_prefix does).
+__device__ __forceinline__ int64_t mid_class_units(int32_t E, int64_t *lds_pfx, int nthreads,
+                                                   const int32_t *__restrict__ offsets, int64_t max_slots,
+                                                   int64_t N) {
+    const int64_t nblk = (N + 255) / 256;
+    const int64_t total = expert_prefix(E, lds_pfx, nthreads, [&](int e) -> int64_t {
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        return (c > kMidMin && c <= kMidMax) ? ((c + kMidRows - 1) / kMidRows) * nblk : 0;
+    });
+    __syncthreads();  // every thread has read the total before lds_pfx is reused
+    return total;
+}
+
 template <int U>
 __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
@@ -1038,15 +1058,20 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int small_max) {
+    float *__restrict__ out, int small_max, int64_t mid_floor) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
     __shared__ int32_t srow[16];
     __shared__ float sasc[16];  // row scales of the staged rows (no global load at the stores)
     const int64_t ntiles = N / 16;
+    // also the weight-streaming loop's experts when that loop has too few units
+    // (mid_floor > 0: it is launched too, and skips them then)
+    const int small_eff =
+        (mid_floor > 0 && mid_class_units(E, pfx, kDecThreads, offsets, max_slots, N) < mid_floor) ? kMidMax
+                                                                                                    : small_max;
     const int64_t total = expert_prefix(E, pfx, kDecThreads, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
-        return (c > 0 && c <= small_max) ? ((c + 15) / 16) * ntiles : 0;
+        return (c > 0 && c <= small_eff) ? ((c + 15) / 16) * ntiles : 0;
     });
     const int64_t G = K / G128;
     const int64_t lda = K + 16;
@@ -1128,7 +1153,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int64_t cmin, int64_t cmax) {
+    float *__restrict__ out, int64_t cmin, int64_t cmax, int64_t mid_floor) {
     constexpr int RM = 32 * MF;                    // staged rows
     constexpr int BUF = RM * kMidRow;
     constexpr int TPR = kMidThreads / RM;          // staging threads per row
@@ -1146,6 +1171,9 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
         return (c > cmin && c <= cmax) ? ((c + RM - 1) / RM) * nblk : 0;
     });
+    // too few units for the machine: the decode loop has taken these experts (the same
+    // count as mid_class_units when cmin, cmax, RM are the class bounds)
+    if (total < mid_floor) return;
     const int64_t u0 = total * blockIdx.x / gridDim.x, u1 = total * (blockIdx.x + 1) / gridDim.x;
     if (u0 >= u1) return;  // the whole workgroup
 
@@ -1562,8 +1590,9 @@ static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, i
 
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
-                               const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots, float *out,
-                               hipStream_t stream) {
+                               const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
+                               int64_t max_per_expert, float *out, hipStream_t stream) {
+    if (max_per_expert > max_slots) max_per_expert = max_slots;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
@@ -1573,7 +1602,11 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         // experts with 17..128 slots: one weight pass per 64 rows when the K slicing
         // fits (at least two slices; activation offsets below 2^32)
         const bool mid = G % kMidSlice == 0 && G >= 2 * kMidSlice && (int64_t)R * K < (1ll << 32);
-        const int small_max = mid ? 16 : (int)kSmallRows;
+        const int small_max = mid ? kMidMin : (int)kSmallRows;
+        // the weight-streaming loop runs if some expert can be in its class; the decode
+        // loop takes that class when it has too few units to keep a quarter of the CUs
+        // busy (a lone mid-size expert): re-reading it per 16 rows is then cheaper
+        const int64_t mid_floor = (mid && max_per_expert > kMidMin) ? cus / 4 : 0;
 #define W4A8_GDEC(UU, SS)                                                                                           \
     do {                                                                                                            \
         const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + dec_red_bytes(SS));                 \
@@ -1581,7 +1614,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)               \
             return hipGetLastError();                                                                               \
         hipLaunchKernelGGL((grouped_decode_kernel<UU, SS>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,  \
-                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max);                  \
+                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max, mid_floor);       \
     } while (0)
         // four K parts per tile when no workgroup can get more than four tiles (an upper
         // bound of the work: each expert's last chunk may be partial)
@@ -1597,25 +1630,29 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
 #undef W4A8_GDEC
         hipError_t derr = hipGetLastError();
         if (derr != hipSuccess) return derr;
-        if (!mid) return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
-                                              max_slots, out, kSmallRows, cus, stream);
+        if (!mid) return max_per_expert <= kSmallRows ? hipSuccess
+                                                      : launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets,
+                                                                             E, K, packed, scale, zp, N, max_slots, out,
+                                                                             kSmallRows, cus, stream);
         // the other loops only when some expert can have that many slots
 #define W4A8_GMID(MF, CMIN, CMAX)                                                                                       \
     do {                                                                                                            \
-        if (max_slots > (CMIN)) {                                                                                   \
+        if (max_per_expert > (CMIN)) {                                                                              \
             if (hipFuncSetAttribute((const void *)grouped_mid_kernel<MF, 4>,                                        \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes(MF)) != hipSuccess) \
                 return hipGetLastError();                                                                           \
             hipLaunchKernelGGL((grouped_mid_kernel<MF, 4>), dim3((uint32_t)cus), dim3(kMidThreads),                \
                                (size_t)mid_lds_bytes(MF), stream, qa, a_scale, R, row_index, expert_offsets, E, K,   \
-                               packed, scale, zp, N, max_slots, out, (int64_t)(CMIN), (int64_t)(CMAX));             \
+                               packed, scale, zp, N, max_slots, out, (int64_t)(CMIN), (int64_t)(CMAX), mid_floor);  \
             if ((derr = hipGetLastError()) != hipSuccess) return derr;                                              \
         }                                                                                                           \
     } while (0)
-        W4A8_GMID(2, 16, 128);  // 65..128 slots: two row blocks, the weights read twice
+        static_assert(kMidRows == 64, "the weight-streaming loop stages 64 rows (MF = 2)");
+        W4A8_GMID(2, kMidMin, kMidMax);  // 65..128 slots: two row blocks, the weights read twice
 #undef W4A8_GMID
+        if (max_per_expert <= kMidMax) return hipSuccess;
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, 128, cus, stream);
+                                    out, kMidMax, cus, stream);
     }
     const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
@@ -1629,7 +1666,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         hipLaunchKernelGGL(grouped_stream_kernel<1>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
                            expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || max_per_expert <= kSmallRows) return err;
     return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
                                 kSmallRows, cus, stream);
 }

@@ -10,7 +10,8 @@
 //
 //  * route_topk: one wave per token; each lane keeps E/64 logits in registers,
 //    k rounds of a wave-wide (value, -id) arg-max pick the experts in
-//    descending order (ties -> lower id), then a softmax over the k picks.
+//    descending order (ties -> lower id), then a softmax over the k picks, all
+//    without divergent branches.
 //  * bucket: one workgroup; per-expert counts with LDS integer atomics, an
 //    exclusive scan, then a stable placement: pairs are taken in chunks of 1024
 //    in increasing pair index; inside a wave, lanes with the same expert are
@@ -28,63 +29,73 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 8;
 constexpr int kPerLane = kMaxE / kWave;  // 16
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
 constexpr int kRouteThreads = 256;
+// One wave per token.  Lane l holds logits l, l + 64, ... (up to kPerLane of them) and
+// a bitmask of the ones already picked; each of the k rounds takes the lane-local best
+// candidate with selects (no branches), then a wave-wide (value, -id) arg-max.  Every
+// lane ends up with all k picks; lane j writes pick j.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
                                                                    int32_t E, int32_t k, int32_t *__restrict__ ids,
                                                                    float *__restrict__ w) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x >> 6);
-    if (t >= T) return;
+    if (t >= T) return;  // whole waves
+    const int per = (E + kWave - 1) / kWave;  // logits per lane (wave-uniform)
+    const float *row = logits + t * E;
     float v[kPerLane];
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
+        if (i >= per) break;
         const int e = i * kWave + lane;
-        v[i] = e < E ? logits[t * E + e] : -INFINITY;
+        const float x = row[e < E ? e : E - 1];
+        v[i] = e < E ? x : -INFINITY;
     }
-    bool taken[kPerLane];
+    uint32_t taken = 0;  // bit i: logit i * 64 + lane already picked (or past E)
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) taken[i] = (i * kWave + lane) >= E;
+    for (int i = 0; i < kPerLane; ++i)
+        if (i * kWave + lane >= E) taken |= 1u << i;
     float sel_v[kMaxK];
     int sel_i[kMaxK];
-    for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
         float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
+        int bi = 0x7FFFFFFF;  // none yet
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
+            if (i >= per) break;
             const int e = i * kWave + lane;
-            if (!taken[i] && (bi == 0x7FFFFFFF || better(v[i], e, bv, bi))) {
-                bv = v[i];
-                bi = e;
-            }
+            // bitwise, not short-circuit, operators: no branches
+            const bool take = !((taken >> i) & 1u) & ((bi == 0x7FFFFFFF) | (v[i] > bv) | ((v[i] == bv) & (e < bi)));
+            bv = take ? v[i] : bv;
+            bi = take ? e : bi;
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             const float ov = __shfl_xor(bv, off, kWave);
             const int oi = __shfl_xor(bi, off, kWave);
-            if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-            }
+            const bool take = (oi != 0x7FFFFFFF) & ((bi == 0x7FFFFFFF) | (ov > bv) | ((ov == bv) & (oi < bi)));
+            bv = take ? ov : bv;
+            bi = take ? oi : bi;
         }
         sel_v[j] = bv;
         sel_i[j] = bi;
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i)
-            if (i * kWave + lane == bi) taken[i] = true;
+        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     }
-    if (lane == 0) {
-        const float top = sel_v[0];
-        float denom = 0.0f;
-        float ex[kMaxK];
-        for (int j = 0; j < k; ++j) {
-            ex[j] = expf(sel_v[j] - top);
-            denom += ex[j];
-        }
-        for (int j = 0; j < k; ++j) {
+    // softmax over the picks, in pick order (the same sum on every lane)
+    const float top = sel_v[0];
+    float ex[kMaxK];
+    float denom = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        ex[j] = expf(sel_v[j] - top);
+        denom += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        if (lane == j) {
             ids[t * k + j] = sel_i[j];
             w[t * k + j] = ex[j] / denom;
         }

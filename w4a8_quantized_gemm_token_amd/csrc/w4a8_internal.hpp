@@ -31,11 +31,14 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
                        const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
                        int64_t N, int path, float *out, int32_t *isums, hipStream_t stream);
 
+// max_per_expert: a bound on any one expert's slot count known to the caller (the
+// MoE layer knows no expert gets more than T); loops for larger experts are not
+// launched.  max_slots when nothing better is known.
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R,
                                const int32_t *row_index, const int32_t *expert_offsets, int32_t E,
                                int64_t K, const uint8_t *packed, const uint16_t *scale,
-                               const uint16_t *zp, int64_t N, int64_t max_slots, float *out,
-                               hipStream_t stream);
+                               const uint16_t *zp, int64_t N, int64_t max_slots, int64_t max_per_expert,
+                               float *out, hipStream_t stream);
 
 hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared,
                             int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *slot_row,
