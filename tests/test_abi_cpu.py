@@ -61,6 +61,7 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_gemm(f, f, -1, 256, f, f, f, 128, 128, f, None) == EINVAL
     # bad path
     assert lib.w4a8_gemm_path(f, f, 4, 256, f, f, f, 128, 128, 7, f, None) == EINVAL
+    assert lib.w4a8_gemm_path(f, f, 4, 256, f, f, f, 128, 128, -1, f, None) == EINVAL
     # streaming path with too many rows
     assert lib.w4a8_gemm_path(f, f, 65, 256, f, f, f, 128, 128, 1, f, None) == EINVAL
     # M == 0 is a no-op that launches nothing
