@@ -142,6 +142,40 @@ def summarize_stats(stats_csv, cmd, top=12):
     return "\n".join(out)
 
 
+def summarize_counters(csvs, kernel, cmd):
+    """Text summary of rocprofv3 --pmc runs (SQ_* / GRBM_* counters) for one kernel: the mean of
+    each counter over that kernel's dispatches, then a few ratios derived from them."""
+    vals, n = {}, {}
+    for path in csvs:
+        for r in _counter_rows(path):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel} in {csvs}")
+    avg = {k: float(np.mean(v)) for k, v in vals.items()}
+    out = [f"# hardware counters of {kernel}, mean per dispatch",
+           "# commands (run from /tmp with TMPDIR=/tmp; <repo> = the repository root):"]
+    for c in cmd:
+        out.append("#   " + c)
+    out.append(f"kernel_sources_sha256: {kernel_digest()}")
+    for k in sorted(avg):
+        out.append(f"{k}: {avg[k]:.0f}   ({len(vals[k])} dispatches)")
+
+    def ratio(name, a, b, scale=1.0):
+        if a in avg and b in avg and avg[b] > 0:
+            out.append(f"{name}: {scale * avg[a] / avg[b]:.3f}")
+
+    out.append("# derived")
+    ratio("valu_insts_per_mfma_inst", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")
+    ratio("lds_insts_per_mfma_inst", "SQ_INSTS_LDS", "SQ_INSTS_MFMA")
+    ratio("wave_cycles_waiting_on_loads_frac", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")
+    ratio("wave_cycles_waiting_any_frac", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+    ratio("coexec_over_mfma_busy", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES")
+    ratio("valu_active_over_wave_cycles", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")
+    return "\n".join(out)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -157,7 +191,13 @@ def parse():
                    help="print the traffic summary of two rocprofv3 --pmc counter_collection.csv files; no GPU")
     p.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                    help="print a short table of a rocprofv3 kernel_stats.csv; no GPU")
+    p.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV",
+                   help="print the mean SQ/GRBM counters of --kernel over rocprofv3 --pmc runs; no GPU")
+    p.add_argument("--kernel", default="gemm_tiled_kernel", help="kernel named by --summarize-counters")
     p.add_argument("--cmd", action="append", default=[], help="command text recorded in a summary")
+    p.add_argument("--only", choices=["prefill"],
+                   help="run one secondary workload alone and print its figures (for counter runs)")
+    p.add_argument("--reps", type=int, default=10, help="timed launches for --only")
     return p.parse_args()
 
 
@@ -258,11 +298,10 @@ def cpu_baseline(synthetic):
                       f"{t_total:.1f} s; weight quantization excluded (offline)"}
 
 
-def secondary(torch, w4, synthetic):
-    """Prefill (M=4096, K=N=8192) TOPS and MoE layer times; context figures."""
+def prefill(torch, w4, synthetic, reps=10):
+    """The prefill-shaped dense GEMM (M=4096, K=N=8192): quantize once, then `reps`
+    back-to-back prepared launches timed with one event pair on the launch stream."""
     dev = torch.device("cuda:0")
-    out = {}
-    # prefill
     M, N, K = 4096, 8192, 8192
     W = torch.empty((N, K), dtype=torch.float32, device=dev)
     synthetic.fill_weights_device(W, 0, synthetic.TAG_W, 0, K, 0, "offset")
@@ -270,23 +309,28 @@ def secondary(torch, w4, synthetic):
     del W
     x = torch.from_numpy(synthetic.activations(0, M, K)).to(dev)
     qa, sc = w4.quantize_act(x)
-    for _ in range(40):  # about 20 ms of warm-up
-        w4.gemm(qa, sc, *layer)
     out_buf = torch.empty((M, N), dtype=torch.float32, device=dev)
     launch = w4.prepare_gemm(qa, sc, *layer, out_buf)
+    for _ in range(40):  # about 20 ms of warm-up
+        launch()
     stream = torch.cuda.current_stream()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
-    for _ in range(10):
+    for _ in range(reps):
         launch()
     e.record(stream)
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / 10
+    ms = s.elapsed_time(e) / reps
     tops = 2 * M * N * K / (ms * 1e-3) / 1e12
-    out["prefill_M4096_K8192_N8192"] = {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1),
-                                        "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
-    del layer, x, qa, sc
+    del layer, x, qa, sc, out_buf
     torch.cuda.empty_cache()
+    return {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+
+
+def secondary(torch, w4, synthetic):
+    """Prefill (M=4096, K=N=8192) TOPS and MoE layer times; context figures."""
+    dev = torch.device("cuda:0")
+    out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic)}
     from tests.gpu_common import device_experts
     # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
     # back-to-back prepared launches that rotate three copies of the 250 MB expert set
@@ -378,6 +422,9 @@ def main():
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.cmd))
         return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.kernel, args.cmd))
+        return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               "(sharding the layer over several GPUs is designed but not implemented)", file=sys.stderr)
@@ -388,6 +435,9 @@ def main():
     import w4a8_quantized_gemm_token_amd as w4
 
     w4.load()
+    if args.only == "prefill":
+        print(json.dumps({"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic, args.reps)}), flush=True)
+        return
     layers, xs = decode_setup(torch, w4, synthetic, args.copies)
     ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m = run_decode(torch, w4, layers, xs, args.steps, args.warmup)
     if args.profile_copy:
