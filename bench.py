@@ -202,6 +202,8 @@ def parse():
 
 
 def decode_setup(torch, w4, synthetic, copies):
+    """`copies` copies of the decode layer in the standard layout and in the tile-major one
+    (converted offline, outside any timed region), and the activations."""
     dev = torch.device("cuda:0")
     W = torch.empty((N_DEC, K_DEC), dtype=torch.float32, device=dev)
     synthetic.fill_weights_device(W, 0, synthetic.TAG_W, 0, K_DEC, 0, "outliers")
@@ -209,20 +211,22 @@ def decode_setup(torch, w4, synthetic, copies):
     for _ in range(copies - 1):
         layers.append(tuple(t.clone() for t in layers[0]))
     del W
+    tms = [w4.weights_to_tm(*layer) for layer in layers]
     x = torch.from_numpy(synthetic.activations_with_outlier_channels(0, 16, K_DEC)).to(dev)
     xs = {M: x[:M].contiguous() for M in M_DEC}
     torch.cuda.synchronize()
-    return layers, xs
+    return layers, tms, xs
 
 
-def run_decode(torch, w4, layers, xs, steps, warmup):
+def run_decode(torch, w4, prep, n_layers, xs, steps, warmup):
     """Times `steps` decode steps, then the GEMM kernel alone.
 
-    Each launch is prepared once (pointers marshalled), so the host stays ahead of the GPU and
-    kernels run back to back.  HIP event records are themselves queue packets that cost a few
-    microseconds each, so none sits between the kernels of a step; the GEMM's launch duration is
-    taken from one event pair around `steps` back-to-back GEMM launches per M (rotating weight
-    copies, activations from the step) on the same stream."""
+    `prep(qa, sc, i, out)` prepares the GEMM over weight copy i.  Each launch is prepared once
+    (pointers marshalled), so the host stays ahead of the GPU and kernels run back to back.
+    HIP event records are themselves queue packets that cost a few microseconds each, so none
+    sits between the kernels of a step; the GEMM's launch duration is taken from one event pair
+    around `steps` back-to-back GEMM launches per M (rotating weight copies, activations from
+    the step) on the same stream."""
     dev = torch.device("cuda:0")
     quant, gemms = {}, {}
     for M in M_DEC:
@@ -230,8 +234,7 @@ def run_decode(torch, w4, layers, xs, steps, warmup):
         sc = torch.empty((M,), dtype=torch.float32, device=dev)
         out = torch.empty((M, N_DEC), dtype=torch.float32, device=dev)
         quant[M] = w4.prepare_quantize_act(xs[M], qa, sc)
-        gemms[M] = [w4.prepare_gemm(qa, sc, *layer, out) for layer in layers]
-    n_layers = len(layers)
+        gemms[M] = [prep(qa, sc, i, out) for i in range(n_layers)]
     stream = torch.cuda.current_stream()
     calls = 0
 
@@ -438,15 +441,21 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic, args.reps)}), flush=True)
         return
-    layers, xs = decode_setup(torch, w4, synthetic, args.copies)
-    ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m = run_decode(torch, w4, layers, xs, args.steps, args.warmup)
+    layers, tms, xs = decode_setup(torch, w4, synthetic, args.copies)
+    ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m = run_decode(
+        torch, w4, lambda qa, sc, i, out: w4.prepare_gemm_tm(qa, sc, tms[i], out), len(tms), xs, args.steps,
+        args.warmup)
+    std_per_m = None
+    if not args.no_secondary:  # the same step over the standard layout, for comparison
+        std_per_m = run_decode(torch, w4, lambda qa, sc, i, out: w4.prepare_gemm(qa, sc, *layers[i], out),
+                               len(layers), xs, args.steps, 200)[4]
     if args.profile_copy:
         a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    del layers
+    del layers, tms
     torch.cuda.empty_cache()
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = read_traffic()
@@ -466,15 +475,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "W4A8 decode linear: per-token INT8 quant + GEMM, K=8192, N=28672, group=128, "
                                "M=1,8,16 per step (0.1% x20 weight outliers, 4 x50 activation channels)",
+                   "weight_layout": "tile-major (offline reorder of the packed codes, scales and zero points)",
                    "weight_copies_rotated": args.copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "gemm_decode_kernel (decode W4A8 GEMM, activations staged in LDS)",
+                     "kernel": "gemm_decode_kernel, tile-major weights (decode W4A8 GEMM, activations staged in LDS)",
                      "bytes_per_launch": gemm_bytes, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "decode_per_M": per_m,
     }
     if not args.no_secondary:
-        result["secondary"] = secondary(torch, w4, synthetic)
+        result["secondary"] = {"decode_standard_layout_per_M": std_per_m, **secondary(torch, w4, synthetic)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synthetic)
     print(json.dumps(result), flush=True)

@@ -72,7 +72,7 @@ typedef enum {
     W4A8_EWORKSPACE = 4     /* the caller's workspace is smaller than the call needs */
 } w4a8_status;
 
-#define W4A8_ABI_VERSION 2
+#define W4A8_ABI_VERSION 3
 #define W4A8_GROUP 128
 
 int w4a8_abi_version(void);
@@ -146,6 +146,42 @@ w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K,
 w4a8_status w4a8_gemm_path(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
                            const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
                            int64_t N, int32_t group, int32_t path, float *out, hipStream_t stream);
+
+/* --------------------------------------------- tile-major weights (decode) */
+
+/* The same codes, scales and zero points as the standard layout, reordered
+ * offline so that the decode GEMM (M <= 16, where the weights are the whole cost:
+ * [p1 §4.3] on decode being bound by the weight stream) reads each weight byte in
+ * one contiguous stream per wave.  This is only a storage order; the arithmetic
+ * is that of w4a8_gemm.  For N % 16 == 0 and K % 256 == 0, with G = K/128:
+ *     tm  u8  [N/16][G/2][2176]   block (t, w) for columns 16t..16t+15 and groups
+ *                                 2w, 2w+1:
+ *       bytes [1024h, 1024h + 1024), h = 0, 1: group 2w+h; byte 16l + b (l = 0..63,
+ *           b = 0..15) = packed[16t + (l & 15)][(2w+h)*64 + 16*(l >> 4) + b]
+ *       bytes [2048, 2176): 64 fp16 words; word 4c + j = scale[2w + j][16t + c]
+ *           for j = 0, 1 and zp[2w + j - 2][16t + c] for j = 2, 3 (c = 0..15)
+ * Total size: N*K/2 + 4*N*(K/128) bytes, the same as packed + scale + zp. */
+
+/* Bytes of the tile-major array for an N x K weight (0 if N % 16 or K % 256). */
+size_t w4a8_tm_bytes(int64_t N, int64_t K);
+
+/* Device, asynchronous.  Writes the tile-major array `tm` (device, 16-byte
+ * aligned, w4a8_tm_bytes(N, K) bytes) from standard-layout device weights.
+ * Errors: W4A8_EINVAL (null, N % 16 != 0, K % 256 != 0, misalignment),
+ * W4A8_EUNSUPPORTED (group != 128). */
+w4a8_status w4a8_weights_to_tm(const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
+                               int64_t N, int64_t K, int32_t group, uint8_t *tm,
+                               hipStream_t stream);
+
+/* Device.  out[M][N] as w4a8_gemm, with the weights in the tile-major array, for
+ * the decode sizes 1 <= M <= 16.  Output bytes are identical to w4a8_gemm's for
+ * the same weights.  Besides w4a8_gemm's conditions it needs K % 256 == 0,
+ * M * (K + 16) <= 143360 (the staged activation rows) and a tile-major array
+ * below 4 GiB; anything else is W4A8_EINVAL (use w4a8_gemm for larger M).
+ * M == 0 is a no-op. */
+w4a8_status w4a8_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
+                         const uint8_t *tm, int64_t N, int32_t group, float *out,
+                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------- MoE */
 

@@ -86,6 +86,21 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_moe_combine(f, f, f, None, 4, 0, 128, f, None) == EINVAL
     # device packer sizes
     assert lib.w4a8_pack_weights_device(f, 128, 200, 128, f, f, f, None) == EINVAL
+    # tile-major weights: size query, conversion and GEMM
+    assert lib.w4a8_tm_bytes(28672, 8192) == 28672 * 8192 // 2 + 4 * 28672 * 64
+    assert lib.w4a8_tm_bytes(24, 256) == 0 and lib.w4a8_tm_bytes(16, 384) == 0
+    assert lib.w4a8_weights_to_tm(f, f, f, 128, 384, 128, f, None) == EINVAL
+    assert lib.w4a8_weights_to_tm(f, f, f, 120, 256, 128, f, None) == EINVAL
+    assert lib.w4a8_weights_to_tm(f, f, f, 128, 256, 64, f, None) == EUNSUPPORTED
+    assert lib.w4a8_weights_to_tm(f, f, f, 128, 256, 128, _fake(4104), None) == EINVAL
+    assert lib.w4a8_gemm_tm(f, f, 17, 256, f, 128, 128, f, None) == EINVAL
+    assert b"1 <= M <= 16" in lib.w4a8_last_error()
+    assert lib.w4a8_gemm_tm(f, f, 4, 384, f, 128, 128, f, None) == EINVAL
+    assert lib.w4a8_gemm_tm(f, f, 16, 9216, f, 128, 128, f, None) == EINVAL  # staged rows past the LDS
+    assert lib.w4a8_gemm_tm(f, f, 4, 256, f, 120, 128, f, None) == EINVAL
+    assert lib.w4a8_gemm_tm(f, f, 4, 256, f, 128, 256, f, None) == EUNSUPPORTED
+    assert lib.w4a8_gemm_tm(None, f, 4, 256, f, 128, 128, f, None) == EINVAL
+    assert lib.w4a8_gemm_tm(f, f, 0, 256, f, 128, 128, f, None) == 0
     # MoE FFN layer: sizes, workspace alignment and size
     need = lib.w4a8_moe_ffn_workspace_size(64, 7168, 2048, 384, 8)
     assert need > 0

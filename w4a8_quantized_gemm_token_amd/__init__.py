@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 GROUP = 128
-ABI_VERSION = 2          # W4A8_ABI_VERSION of the header this binding follows
+ABI_VERSION = 3          # W4A8_ABI_VERSION of the header this binding follows
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
@@ -25,6 +25,7 @@ EXPORTS = (
     "w4a8_abi_version", "w4a8_status_str", "w4a8_last_error",
     "w4a8_pack_weights", "w4a8_pack_weights_device", "w4a8_unpack_weights",
     "w4a8_quantize_act", "w4a8_gemm", "w4a8_gemm_debug_isums", "w4a8_gemm_path",
+    "w4a8_tm_bytes", "w4a8_weights_to_tm", "w4a8_gemm_tm",
     "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_silu_mul_quantize", "w4a8_moe_combine",
     "w4a8_moe_ffn_workspace_size", "w4a8_moe_ffn_workspace_layout", "w4a8_moe_ffn",
 )
@@ -62,6 +63,9 @@ def load() -> ctypes.CDLL:
         "w4a8_gemm": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, p, p]),
         "w4a8_gemm_debug_isums": (ctypes.c_int, [p, i64, i64, p, p, i64, i32, i32, p, p]),
         "w4a8_gemm_path": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, i32, p, p]),
+        "w4a8_tm_bytes": (sz, [i64, i64]),
+        "w4a8_weights_to_tm": (ctypes.c_int, [p, p, p, i64, i64, i32, p, p]),
+        "w4a8_gemm_tm": (ctypes.c_int, [p, p, i64, i64, p, i64, i32, p, p]),
         "w4a8_moe_route": (ctypes.c_int, [p, i64, i32, i32, i32, p, p, p, p, p, p, p]),
         "w4a8_moe_grouped_gemm": (ctypes.c_int, [p, p, i64, p, p, i32, i64, p, p, p, i64, i32, i64, p, p]),
         "w4a8_silu_mul_quantize": (ctypes.c_int, [p, i64, i64, p, p, p, p]),
@@ -239,6 +243,48 @@ def gemm_debug_isums(qa, packed, zp, path: int = 0, group: int = GROUP):
     _call("w4a8_gemm_debug_isums", _dev_ptr(qa), M, K, _dev_ptr(packed), _dev_ptr(zp), N, group, path,
           _dev_ptr(isums), _stream(qa.device))
     return isums
+
+
+def tm_bytes(N: int, K: int) -> int:
+    """Bytes of the tile-major weight array for an N x K weight (0 if the shape has none)."""
+    return int(load().w4a8_tm_bytes(N, K))
+
+
+def weights_to_tm(packed, scale, zp, group: int = GROUP, out=None):
+    """Tile-major copy (uint8 [N/16][K/256][2176]) of standard-layout device weights."""
+    torch = _torch()
+    N = packed.shape[0]
+    K = 2 * packed.shape[1]
+    if out is None:
+        out = _empty((N // 16, K // 256, 2176), torch.uint8, packed)
+    _call("w4a8_weights_to_tm", _dev_ptr(packed), _dev_ptr(scale), _dev_ptr(zp), N, K, group, _dev_ptr(out),
+          _stream(packed.device))
+    return out
+
+
+def _tm_n(tm) -> int:
+    return 16 * tm.shape[0]
+
+
+def gemm_tm(qa, a_scale, tm, out=None, group: int = GROUP):
+    """out float32 [M][N] (M <= 16) from tile-major weights; the same bytes as gemm()."""
+    torch = _torch()
+    M, K = qa.shape
+    N = _tm_n(tm)
+    if out is None:
+        out = _empty((M, N), torch.float32, qa)
+    _call("w4a8_gemm_tm", _dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(tm), N, group, _dev_ptr(out),
+          _stream(qa.device))
+    return out
+
+
+def prepare_gemm_tm(qa, a_scale, tm, out, group: int = GROUP) -> Launch:
+    """Prepared w4a8_gemm_tm writing into a preallocated out float32 [M][N]."""
+    M, K = qa.shape
+    N = _tm_n(tm)
+    assert tuple(out.shape) == (M, N)
+    return Launch("w4a8_gemm_tm", (_dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(tm), N, group, _dev_ptr(out),
+                                   _stream(qa.device)), (qa, a_scale, tm, out))
 
 
 def linear(x, packed, scale, zp, path: int = 0):

@@ -238,6 +238,40 @@ w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K, const 
     return gemm_common(qa, nullptr, M, K, packed, nullptr, zp, N, group, path, nullptr, isums, stream);
 }
 
+size_t w4a8_tm_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || N % 16 != 0 || K % (2 * W4A8_GROUP) != 0) return 0;
+    return (size_t)tm_bytes(N, K);
+}
+
+w4a8_status w4a8_weights_to_tm(const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t K,
+                               int32_t group, uint8_t *tm, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(packed && scale && zp && tm, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(N > 0 && N % 16 == 0, W4A8_EINVAL, "N=%lld must be a positive multiple of 16", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(K % (2 * W4A8_GROUP) == 0, W4A8_EINVAL, "K=%lld must be a multiple of 256", (long long)K);
+    W4A8_REQUIRE(aligned16(packed) && aligned16(tm), W4A8_EINVAL, "packed and tm must be 16-byte aligned");
+    W4A8_REQUIRE((N / 16) * (K / 256) < (1ll << 31), W4A8_EINVAL, "weight too large");
+    return hip_status(launch_weights_to_tm(packed, scale, zp, N, K, tm, stream), "weights_to_tm launch");
+}
+
+w4a8_status w4a8_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *tm, int64_t N,
+                         int32_t group, float *out, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(qa && a_scale && tm && out, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(M >= 0, W4A8_EINVAL, "M=%lld must be >= 0", (long long)M);
+    W4A8_REQUIRE(N > 0 && N % 16 == 0, W4A8_EINVAL, "N=%lld must be a positive multiple of 16", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(aligned16(qa) && aligned16(tm) && aligned16(out), W4A8_EINVAL,
+                 "qa, tm and out must be 16-byte aligned");
+    if (M == 0) return W4A8_OK;
+    W4A8_REQUIRE(gemm_tm_supported(M, K, N), W4A8_EINVAL,
+                 "the tile-major GEMM takes 1 <= M <= 16, K %% 256 == 0, M*(K+16) <= 143360 and a tile-major "
+                 "array below 4 GiB (M=%lld K=%lld N=%lld)",
+                 (long long)M, (long long)K, (long long)N);
+    return hip_status(launch_gemm_tm(qa, a_scale, M, K, tm, N, out, stream), "gemm_tm launch");
+}
+
 w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared,
                            int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *perm,
                            int32_t *slot_row, int32_t *slot_of_pair, hipStream_t stream) {

@@ -462,7 +462,17 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
 // `stage(0)` runs before the first weight windows are issued and may start loading the
 // rows; `stage(1)` runs after them (so their latency overlaps it) and is followed by a
 // workgroup barrier: it fills `rows` when they change.
-template <int U, int SPLIT, bool ISUMS, typename Stage, typename Store>
+// Tile-major weights (TM): for 16-column tile t and two-group window w, block
+// (t * G/2 + w) of kTmBlock bytes holds the first group's codes (byte 16 l + b: column
+// 16 t + (l & 15), packed byte 16 (l >> 4) + b of that column's group, l = 0..63), the
+// second group's the same way, then for each column c = 0..15 four fp16 words at byte
+// 2048 + 8 c: scale of group 2 w, scale of group 2 w + 1, zero point of group 2 w, zero
+// point of group 2 w + 1.  A wave's windows are then one contiguous stream, lane l's
+// 16-byte loads land directly in the 16x16x64 MFMA operand layout, and one 8-byte load
+// gives a lane all four words of its column (no cross-lane moves at all).
+constexpr int64_t kTmBlock = 2 * 1024 + 128;
+
+template <int U, int SPLIT, bool ISUMS, bool TM, typename Stage, typename Store>
 __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M, int64_t K,
                                           const uint8_t *__restrict__ wpk, const uint16_t *__restrict__ wsc,
                                           const uint16_t *__restrict__ wzp, int64_t N, int64_t t0, int64_t t1,
@@ -487,17 +497,41 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
     // Codes are read through a range-checked buffer over the N x K/2 packed bytes (its
     // size is below 2^32, which the launcher checks): 32-bit offsets, and an offset past
     // the end reads zeros without touching memory.
+    // (TM: the buffer covers the whole tile-major array, codes and scales)
+    const int64_t wbytes = TM ? (N / 16) * (G / 2) * kTmBlock : N * (K / 2);
     const __amdgpu_buffer_rsrc_t wrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wpk), (short)0, (int)(N * (K / 2)), 0x00020000);
-    const uint32_t colbyte = (uint32_t)((lane & 7) * (K / 2) + lchunk);
-    const uint16_t *szbase = ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wpk), (short)0, (int)(uint32_t)wbytes, 0x00020000);
+    const uint32_t colbyte = TM ? (uint32_t)(16 * lane) : (uint32_t)((lane & 7) * (K / 2) + lchunk);
+    const uint32_t szbyte = 2048u + 8u * (uint32_t)(lane & 15);  // TM: this lane's column's words
+    const uint16_t *szbase = TM ? nullptr : ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
     v4u rb0[U], rb1[U];
-    uint32_t rsz[U];
+    uint32_t rsz[U];   // standard layout: one fp16 word per lane (spread with ds_bpermute)
+    v2u rsz2[U];       // tile-major: the four words of this lane's column
+    // first byte of window w of tile `tile`, less this lane's part
+    // TM: 32-bit arithmetic (every offset is below the buffer size), with the product
+    // kept apart from the add: fused into a 64-bit multiply-add, its unused high half has
+    // been paired with a register that a staging load was still filling, so the first
+    // weight loads waited for the staged rows.
+    auto window_base = [&](int64_t tile, int64_t w) -> uint32_t {
+        if constexpr (TM) {
+            uint32_t p = (uint32_t)tile * (uint32_t)(G / 2);
+            __asm__("" : "+v"(p));
+            return (p + (uint32_t)w) * (uint32_t)kTmBlock;
+        } else {
+            return (uint32_t)(tile * 16 * (K / 2)) + (uint32_t)w * 128;
+        }
+    };
     auto load_window = [&](int u, int64_t tile, int64_t w) {
-        const uint32_t o = (uint32_t)(tile * 16 * (K / 2)) + colbyte + (uint32_t)w * 128;
-        rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
-        rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o + (uint32_t)(8 * (K / 2)), 0, 2);
-        rsz[u] = szbase[tile * 16 + 2 * w * N];
+        const uint32_t o = window_base(tile, w) + colbyte;
+        if constexpr (TM) {
+            rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
+            rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o + 1024u, 0, 2);
+            rsz2[u] = __builtin_amdgcn_raw_buffer_load_b64(wrs, o - colbyte + szbyte, 0, 2);
+        } else {
+            rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
+            rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o + (uint32_t)(8 * (K / 2)), 0, 2);
+            rsz[u] = szbase[tile * 16 + 2 * w * N];
+        }
     };
     stage(0);  // issue the staging loads (older than the ring's, so waiting for them does not wait for the weights)
     {
@@ -509,11 +543,17 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             __builtin_amdgcn_sched_barrier(0);
-            const uint32_t o = has ? (uint32_t)(tile * 16 * (K / 2)) + colbyte + (uint32_t)(win0 + u) * 128 : 0xFFFFFFF0u;
-            const uint32_t o1 = has ? o + (uint32_t)(8 * (K / 2)) : 0xFFFFFFF0u;
-            rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
-            rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, 2);
-            rsz[u] = szbase[tile * 16 + 2 * (win0 + u) * N];
+            const uint32_t o = window_base(tile, win0 + u) + colbyte;
+            if constexpr (TM) {
+                rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o : 0xFFFFFFF0u, 0, 2);
+                rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o + 1024u : 0xFFFFFFF0u, 0, 2);
+                rsz2[u] = __builtin_amdgcn_raw_buffer_load_b64(wrs, has ? o - colbyte + szbyte : 0xFFFFFFF0u, 0, 2);
+            } else {
+                rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o : 0xFFFFFFF0u, 0, 2);
+                rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o + (uint32_t)(8 * (K / 2)) : 0xFFFFFFF0u, 0,
+                                                              2);
+                rsz[u] = szbase[tile * 16 + 2 * (win0 + u) * N];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -537,16 +577,28 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                         const uint32_t r1[4] = {rb1[u].x, rb1[u].y, rb1[u].z, rb1[u].w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const uint32_t t1v = dpp_ror8(r1[i]);
-                            const uint32_t t0v = dpp_ror8(r0[i]);
-                            xy[0][i] = hi8 ? t1v : r0[i];
-                            xy[1][i] = hi8 ? r1[i] : t0v;
+                            if constexpr (TM) {
+                                xy[0][i] = r0[i];
+                                xy[1][i] = r1[i];
+                            } else {
+                                const uint32_t t1v = dpp_ror8(r1[i]);
+                                const uint32_t t0v = dpp_ror8(r0[i]);
+                                xy[0][i] = hi8 ? t1v : r0[i];
+                                xy[1][i] = hi8 ? r1[i] : t0v;
+                            }
                         }
                     }
                     uint32_t sz[4];  // scale g0, scale g1, zp g0, zp g1 of this lane's column
+                    if constexpr (TM) {
+                        sz[0] = rsz2[u][0] & 0xFFFFu;
+                        sz[1] = rsz2[u][0] >> 16;
+                        sz[2] = rsz2[u][1] & 0xFFFFu;
+                        sz[3] = rsz2[u][1] >> 16;
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sz[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)rsz[u]);
+                        for (int i = 0; i < 4; ++i)
+                            sz[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)rsz[u]);
+                    }
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int64_t g = 2 * w + h;
@@ -619,7 +671,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
     }
 }
 
-template <int U, int SPLIT, bool ISUMS, int SB>
+template <int U, int SPLIT, bool ISUMS, int SB, bool TM>
 __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *__restrict__ qa,
                                                                  const float *__restrict__ a_scale, int64_t M,
                                                                  int64_t K, const uint8_t *__restrict__ wpk,
@@ -638,7 +690,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
     const bool batched = M * K <= (int64_t)kStageBatch * kDecThreads * 16;
     v4u stg[kStageBatch];
     float asc = 0.0f;
-    dec_tiles<U, SPLIT, ISUMS>(
+    dec_tiles<U, SPLIT, ISUMS, TM>(
         dsm, red, (int)M, K, wpk, wsc, wzp, N, t0, t1,
         [&](int phase) {  // qa[M][K] -> LDS, 16-byte pieces through registers
             if (phase == 0) {
@@ -1121,7 +1173,7 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
         auto store = [&](int m, int64_t col, float v) {
             if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
         };
-        dec_tiles<U, SPLIT, false>(dsm, red, rows, K, wpk, wsc, wzp, N, t0, t1, stage, store, nullptr);
+        dec_tiles<U, SPLIT, false, false>(dsm, red, rows, K, wpk, wsc, wzp, N, t0, t1, stage, store, nullptr);
     }
 }
 
@@ -1453,9 +1505,10 @@ hipError_t launch_tiled(const int8_t *qa, const float *a_scale, int64_t M, int64
     return hipGetLastError();
 }
 
+// tm: `packed` is the tile-major array (scale and zp unused; no isums)
 hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                          const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
-                         hipStream_t stream) {
+                         bool tm, hipStream_t stream) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
@@ -1471,20 +1524,43 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
     const dim3 grid((uint32_t)nwg), block(kDecThreads);
     // rows staged with one load per thread when they fit, else eight at a time
     const bool one = M * K <= (int64_t)kDecThreads * 16;
-#define W4A8_DEC1(UU, SS, IS, SB)                                                                                   \
+#define W4A8_DEC1(UU, SS, IS, SB, TT)                                                                               \
     do {                                                                                                            \
-        if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, IS, SB>,                                   \
+        if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, IS, SB, TT>,                               \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)                \
             return hipGetLastError();                                                                               \
-        hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, IS, SB>), grid, block, lds, stream, qa, a_scale, M, K,       \
+        hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, IS, SB, TT>), grid, block, lds, stream, qa, a_scale, M, K,   \
                            packed, scale, zp, N, tpw, out, isums);                                                  \
     } while (0)
 #define W4A8_DEC(UU, SS)                                                                                            \
     do {                                                                                                            \
-        if (isums) W4A8_DEC1(UU, SS, true, 8);                                                                      \
-        else if (one) W4A8_DEC1(UU, SS, false, 1);                                                                  \
-        else W4A8_DEC1(UU, SS, false, 8);                                                                           \
+        if (isums) W4A8_DEC1(UU, SS, true, 8, false);                                                               \
+        else if (one) W4A8_DEC1(UU, SS, false, 1, false);                                                           \
+        else W4A8_DEC1(UU, SS, false, 8, false);                                                                    \
     } while (0)
+    // tile-major weights: contiguous streams take a deeper ring (four windows in flight)
+#define W4A8_DEC_TM(UU, SS)                                                                                         \
+    do {                                                                                                            \
+        if (one) W4A8_DEC1(UU, SS, false, 1, true);                                                                 \
+        else W4A8_DEC1(UU, SS, false, 8, true);                                                                     \
+    } while (0)
+    if (tm) {
+        if (split == 4) {
+            if (nwin % 4 == 0) W4A8_DEC_TM(4, 4);
+            else if (nwin % 2 == 0) W4A8_DEC_TM(2, 4);
+            else W4A8_DEC_TM(1, 4);
+        } else if (split == 2) {
+            if (nwin % 4 == 0) W4A8_DEC_TM(4, 2);
+            else if (nwin % 2 == 0) W4A8_DEC_TM(2, 2);
+            else W4A8_DEC_TM(1, 2);
+        } else {
+            if (nwin % 4 == 0) W4A8_DEC_TM(4, 1);
+            else if (nwin % 2 == 0) W4A8_DEC_TM(2, 1);
+            else W4A8_DEC_TM(1, 1);
+        }
+        return hipGetLastError();
+    }
+#undef W4A8_DEC_TM
     if (split == 4) {
         if (nwin % 2 == 0) W4A8_DEC(2, 4);
         else W4A8_DEC(1, 4);
@@ -1516,7 +1592,7 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
         const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
         // (the decode loop addresses the packed codes with 32-bit buffer offsets)
         if (G % 2 == 0 && M <= 16 && dec_lds_bytes(M, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax)
-            return launch_decode(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+            return launch_decode(qa, a_scale, M, K, packed, scale, zp, N, out, isums, false, stream);
         if (G % 2 == 0) {
             // line-wide loop: two-group windows, K split over two waves when it divides
             const int split = (G % 4 == 0) ? 2 : 1;
@@ -1553,6 +1629,50 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
             return launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
         return launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     }
+    return hipGetLastError();
+}
+
+int64_t tm_bytes(int64_t N, int64_t K) { return (N / 16) * (K / G128 / 2) * kTmBlock; }
+
+bool gemm_tm_supported(int64_t M, int64_t K, int64_t N) {
+    return M >= 1 && M <= 16 && K % (2 * G128) == 0 && N % 16 == 0 && dec_lds_bytes(M, K) <= kDecLdsMax &&
+           tm_bytes(N, K) < kDecCodesMax;
+}
+
+hipError_t launch_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *tm, int64_t N,
+                          float *out, hipStream_t stream) {
+    return launch_decode(qa, a_scale, M, K, tm, nullptr, nullptr, N, out, nullptr, true, stream);
+}
+
+// Standard layout -> tile-major: thread i of workgroup b (b = t * G/2 + w) writes the
+// 16 code bytes of lane i & 63 for group 2 w + (i >> 6) (i < 128), or fp16 word
+// i - 128 of the block's scales and zero points (column (i - 128) / 4).
+__global__ __launch_bounds__(192) void weights_to_tm_kernel(const uint8_t *__restrict__ packed,
+                                                            const uint16_t *__restrict__ scale,
+                                                            const uint16_t *__restrict__ zp, int64_t N, int64_t K,
+                                                            uint8_t *__restrict__ tm) {
+    const int64_t G = K / G128, W = G / 2;
+    const int64_t b = (int64_t)blockIdx.x;
+    if (b >= (N / 16) * W) return;
+    const int64_t t = b / W, w = b % W;
+    uint8_t *dst = tm + b * kTmBlock;
+    const int i = threadIdx.x;
+    if (i < 128) {
+        const int l = i & 63, h = i >> 6;
+        const int64_t col = 16 * t + (l & 15);
+        const v4u v = *reinterpret_cast<const v4u *>(packed + col * (K / 2) + (2 * w + h) * (G128 / 2) + 16 * (l >> 4));
+        *reinterpret_cast<v4u *>(dst + h * 1024 + 16 * l) = v;
+    } else {
+        const int l = i - 128, c = l >> 2, j = l & 3;
+        const uint16_t *src = (j < 2) ? scale : zp;
+        reinterpret_cast<uint16_t *>(dst + 2048)[l] = src[(2 * w + (j & 1)) * N + 16 * t + c];
+    }
+}
+
+hipError_t launch_weights_to_tm(const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t K,
+                                uint8_t *tm, hipStream_t stream) {
+    const int64_t blocks = (N / 16) * (K / G128 / 2);
+    hipLaunchKernelGGL(weights_to_tm_kernel, dim3((uint32_t)blocks), dim3(192), 0, stream, packed, scale, zp, N, K, tm);
     return hipGetLastError();
 }
 

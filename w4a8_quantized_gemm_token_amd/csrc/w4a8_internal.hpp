@@ -40,6 +40,15 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
                                const uint16_t *zp, int64_t N, int64_t max_slots, int64_t max_per_expert,
                                float *out, hipStream_t stream);
 
+// Tile-major weights for the decode loop (M <= 16): bytes of the array, whether a
+// shape is served, the GEMM over it, and the conversion from the standard layout.
+int64_t tm_bytes(int64_t N, int64_t K);
+bool gemm_tm_supported(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *tm, int64_t N,
+                          float *out, hipStream_t stream);
+hipError_t launch_weights_to_tm(const uint8_t *packed, const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t K,
+                                uint8_t *tm, hipStream_t stream);
+
 hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared,
                             int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *slot_row,
                             int32_t *slot_of_pair, hipStream_t stream);
@@ -60,6 +69,7 @@ namespace w4a8dev {
 constexpr int kWave = 64;
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
