@@ -156,10 +156,13 @@ w4a8_status w4a8_gemm_path(const int8_t *qa, const float *a_scale, int64_t M, in
  * is that of w4a8_gemm.  For N % 16 == 0 and K % 256 == 0, with G = K/128:
  *     tm  u8  [N/16][G/2][2176]   block (t, w) for columns 16t..16t+15 and groups
  *                                 2w, 2w+1:
- *       bytes [1024h, 1024h + 1024), h = 0, 1: group 2w+h; byte 16l + b (l = 0..63,
- *           b = 0..15) = packed[16t + (l & 15)][(2w+h)*64 + 16*(l >> 4) + b]
- *       bytes [2048, 2176): 64 fp16 words; word 4c + j = scale[2w + j][16t + c]
- *           for j = 0, 1 and zp[2w + j - 2][16t + c] for j = 2, 3 (c = 0..15)
+ *       bytes [1024h, 1024h + 1024), h = 0, 1: group 2w+h; the 16 bytes at 16l
+ *           (l = 0..63) hold the codes k = 32*(l >> 4) + [0, 32) of that group for
+ *           column 16t + (l & 15), each run of 8 codes c0..c7 (in k order) as the
+ *           4 bytes c_b | c_(b+4) << 4, b = 0..3
+ *       bytes [2048, 2176): 8 bytes per column c = 0..15 at 2048 + 8c: the fp16
+ *           scale[2w][16t + c] and scale[2w + 1][16t + c], then the bytes -zp
+ *           (two's complement int8) of groups 2w and 2w + 1, then two zero bytes
  * Total size: N*K/2 + 4*N*(K/128) bytes, the same as packed + scale + zp. */
 
 /* Bytes of the tile-major array for an N x K weight (0 if N % 16 or K % 256). */

@@ -35,10 +35,11 @@ def w4mod():
     return w4
 
 
-def tm_expected(packed: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """Tile-major bytes written out from the definition, one block at a time."""
-    N, KB = packed.shape
-    G = 2 * KB // 128
+def tm_expected(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Tile-major bytes written out from the definition, one block at a time, from the
+    4-bit codes q[N][K] and the fp16 bits of the scales and zero points [G][N]."""
+    N, K = q.shape
+    G = K // 128
     out = np.zeros((N // 16, G // 2, 2176), np.uint8)
     for t in range(N // 16):
         for w in range(G // 2):
@@ -47,14 +48,17 @@ def tm_expected(packed: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
                 g = 2 * w + h
                 for lane in range(64):
                     col, quarter = 16 * t + (lane & 15), lane >> 4
-                    blk[1024 * h + 16 * lane:1024 * h + 16 * lane + 16] = \
-                        packed[col, 64 * g + 16 * quarter:64 * g + 16 * quarter + 16]
-            words = np.zeros(64, np.uint16)
+                    codes = q[col, 128 * g + 32 * quarter:128 * g + 32 * quarter + 32].reshape(4, 8)
+                    chunk = codes[:, :4] | (codes[:, 4:] << 4)
+                    blk[1024 * h + 16 * lane:1024 * h + 16 * lane + 16] = chunk.reshape(16)
+            zint = z.view(np.float16).astype(np.int64)      # zero points are integers 0..15
             for c in range(16):
-                for j in range(4):
-                    src = s if j < 2 else z
-                    words[4 * c + j] = src[2 * w + (j & 1), 16 * t + c]
-            blk[2048:] = words.view(np.uint8)
+                col = 16 * t + c
+                area = blk[2048 + 8 * c:2048 + 8 * c + 8]
+                area[0:4] = s[2 * w:2 * w + 2, col].astype(np.uint16).view(np.uint8)
+                area[4] = (-zint[2 * w, col]) & 0xFF
+                area[5] = (-zint[2 * w + 1, col]) & 0xFF
+                area[6:8] = 0
     return out
 
 
@@ -67,7 +71,7 @@ def test_weights_to_tm_bytes(orc, N, K):
     packed = orc.pack_nibbles(q)
     tm = w4.weights_to_tm(to_dev(packed), to_dev(s.view(np.int16)), to_dev(z.view(np.int16)))
     assert tm.numel() == w4.tm_bytes(N, K) == N * K // 2 + 4 * N * (K // 128)
-    assert np.array_equal(to_host(tm), tm_expected(packed, s, z))
+    assert np.array_equal(to_host(tm), tm_expected(q.astype(np.uint8), s, z))
 
 
 # (M, N, K): ring depth 4 with two and four K parts per tile, depth 2 and 1, one K

@@ -463,13 +463,16 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
 // rows; `stage(1)` runs after them (so their latency overlaps it) and is followed by a
 // workgroup barrier: it fills `rows` when they change.
 // Tile-major weights (TM): for 16-column tile t and two-group window w, block
-// (t * G/2 + w) of kTmBlock bytes holds the first group's codes (byte 16 l + b: column
-// 16 t + (l & 15), packed byte 16 (l >> 4) + b of that column's group, l = 0..63), the
-// second group's the same way, then for each column c = 0..15 four fp16 words at byte
-// 2048 + 8 c: scale of group 2 w, scale of group 2 w + 1, zero point of group 2 w, zero
-// point of group 2 w + 1.  A wave's windows are then one contiguous stream, lane l's
-// 16-byte loads land directly in the 16x16x64 MFMA operand layout, and one 8-byte load
-// gives a lane all four words of its column (no cross-lane moves at all).
+// (t * G/2 + w) of kTmBlock bytes holds the first group's codes (the 16 bytes at 16 l:
+// column 16 t + (l & 15), codes 32 (l >> 4) + [0, 32) of that column's group, l = 0..63,
+// each run of 8 codes c0..c7 as 4 bytes c_b | c_{b+4} << 4), the second group's the same
+// way, then for each column c = 0..15 eight bytes at 2048 + 8 c: the fp16 scales of
+// groups 2 w and 2 w + 1, then the bytes -zp of the two groups (two's complement), then
+// two zero bytes.  A wave's windows are then one contiguous stream, lane l's 16-byte
+// loads land directly in the 16x16x64 MFMA operand layout, a dword's low and high
+// nibbles are codes 0-3 and 4-7 in order (a mask and a shift, no byte permutes), one
+// 8-byte load gives a lane its column's scales and zero points (no cross-lane moves),
+// and the -zp operand of the zero-point MFMA is one byte replicated (one v_perm).
 constexpr int64_t kTmBlock = 2 * 1024 + 128;
 
 template <int U, int SPLIT, bool ISUMS, bool TM, typename Stage, typename Store>
@@ -606,11 +609,23 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                         const v4i a1 = *reinterpret_cast<const v4i *>(abase + g * G128 + 16);
                         uint32_t q[8];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) spread8(xy[h][i], q[2 * i], q[2 * i + 1]);
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (TM) {
+                                q[2 * i] = xy[h][i] & 0x0F0F0F0Fu;
+                                q[2 * i + 1] = (xy[h][i] >> 4) & 0x0F0F0F0Fu;
+                            } else {
+                                spread8(xy[h][i], q[2 * i], q[2 * i + 1]);
+                            }
+                        }
                         const v4i bq0 = {(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
                         const v4i bq1 = {(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
-                        const int zneg = -(int)half_bits_to_float((uint16_t)sz[2 + h]);
-                        const int z4 = (int)((uint32_t)(zneg & 0xFF) * 0x01010101u);
+                        int z4;
+                        if constexpr (TM) {
+                            z4 = (int)__builtin_amdgcn_perm(0u, rsz2[u][1], h ? 0x01010101u : 0u);
+                        } else {
+                            const int zneg = -(int)half_bits_to_float((uint16_t)sz[2 + h]);
+                            z4 = (int)((uint32_t)(zneg & 0xFF) * 0x01010101u);
+                        }
                         const v4i bz = {z4, z4, z4, z4};
                         v4i d = {0, 0, 0, 0};
                         d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
@@ -1646,7 +1661,7 @@ hipError_t launch_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int
 
 // Standard layout -> tile-major: thread i of workgroup b (b = t * G/2 + w) writes the
 // 16 code bytes of lane i & 63 for group 2 w + (i >> 6) (i < 128), or fp16 word
-// i - 128 of the block's scales and zero points (column (i - 128) / 4).
+// i - 128 of the block's scale and zero-point area (column (i - 128) / 4).
 __global__ __launch_bounds__(192) void weights_to_tm_kernel(const uint8_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scale,
                                                             const uint16_t *__restrict__ zp, int64_t N, int64_t K,
@@ -1661,11 +1676,28 @@ __global__ __launch_bounds__(192) void weights_to_tm_kernel(const uint8_t *__res
         const int l = i & 63, h = i >> 6;
         const int64_t col = 16 * t + (l & 15);
         const v4u v = *reinterpret_cast<const v4u *>(packed + col * (K / 2) + (2 * w + h) * (G128 / 2) + 16 * (l >> 4));
-        *reinterpret_cast<v4u *>(dst + h * 1024 + 16 * l) = v;
+        // standard bytes hold codes (2j, 2j + 1); re-pair each run of 8 as (b, b + 4)
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t c03, c47;
+            spread8(d[j], c03, c47);
+            o[j] = c03 | (c47 << 4);
+        }
+        *reinterpret_cast<v4u *>(dst + h * 1024 + 16 * l) = v4u{o[0], o[1], o[2], o[3]};
     } else {
         const int l = i - 128, c = l >> 2, j = l & 3;
-        const uint16_t *src = (j < 2) ? scale : zp;
-        reinterpret_cast<uint16_t *>(dst + 2048)[l] = src[(2 * w + (j & 1)) * N + 16 * t + c];
+        const int64_t col = 16 * t + c;
+        uint16_t word = 0;
+        if (j < 2) {
+            word = scale[(2 * w + j) * N + col];
+        } else if (j == 2) {
+            const uint32_t z0 = (uint32_t)(-(int)half_bits_to_float(zp[(2 * w) * N + col])) & 0xFFu;
+            const uint32_t z1 = (uint32_t)(-(int)half_bits_to_float(zp[(2 * w + 1) * N + col])) & 0xFFu;
+            word = (uint16_t)(z0 | (z1 << 8));
+        }
+        reinterpret_cast<uint16_t *>(dst + 2048)[l] = word;
     }
 }
 
