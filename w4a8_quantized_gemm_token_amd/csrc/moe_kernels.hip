@@ -9,9 +9,9 @@
 // storage bill"): the toy top-1 router over 8 experts.
 //
 //  * route_topk: one wave per token; each lane keeps E/64 logits in registers,
-//    k rounds of a wave-wide (value, -id) arg-max pick the experts in
-//    descending order (ties -> lower id), then a softmax over the k picks, all
-//    without divergent branches.
+//    k rounds of a wave-wide (value, -id) arg-max (DPP within rows, scalar reads
+//    across them) pick the experts in descending order (ties -> lower id), then a
+//    softmax over the k picks, all without divergent branches.
 //  * bucket: one workgroup; per-expert counts with LDS integer atomics, an
 //    exclusive scan, then a stable placement: pairs are taken in chunks of 1024
 //    in increasing pair index; inside a wave, lanes with the same expert are
@@ -30,30 +30,45 @@ constexpr int kMaxK = 8;
 constexpr int kPerLane = kMaxE / kWave;  // 16
 
 constexpr int kRouteThreads = 256;
-// One wave per token.  Lane l holds logits l, l + 64, ... (up to kPerLane of them) and
+
+// (v, i) beats (bv, bi): larger value, then lower id.  A lane with no candidate holds
+// (-inf, INT_MAX), which every real candidate beats (non-NaN logits).
+__device__ __forceinline__ void better_of(float ov, int oi, float &bv, int &bi) {
+    const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+    bv = take ? ov : bv;
+    bi = take ? oi : bi;
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float &bv, int &bi) {
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), CTRL, 0xF,
+                                                                           0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+    better_of(ov, oi, bv, bi);
+}
+
+// One wave per token.  Lane l holds logits l, l + 64, ... (PER of them, PER * 64 >= E) and
 // a bitmask of the ones already picked; each of the k rounds takes the lane-local best
-// candidate with selects (no branches), then a wave-wide (value, -id) arg-max.  Every
-// lane ends up with all k picks; lane j writes pick j.
+// candidate with selects, then a wave-wide arg-max: DPP steps inside each 16-lane row
+// (swap neighbours, swap pairs, rotate by 4 and by 8), then the four row winners read
+// as scalars -- no LDS round trips, no branches.  Every lane ends up with all k picks;
+// lane j writes pick j.
+template <int PER>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
                                                                    int32_t E, int32_t k, int32_t *__restrict__ ids,
                                                                    float *__restrict__ w) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x >> 6);
     if (t >= T) return;  // whole waves
-    const int per = (E + kWave - 1) / kWave;  // logits per lane (wave-uniform)
     const float *row = logits + t * E;
-    float v[kPerLane];
+    float v[PER];
+    uint32_t taken = 0;  // bit i: logit i * 64 + lane already picked (or past E)
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        if (i >= per) break;
+    for (int i = 0; i < PER; ++i) {
         const int e = i * kWave + lane;
         const float x = row[e < E ? e : E - 1];
         v[i] = e < E ? x : -INFINITY;
+        taken |= (e < E ? 0u : 1u) << i;
     }
-    uint32_t taken = 0;  // bit i: logit i * 64 + lane already picked (or past E)
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i)
-        if (i * kWave + lane >= E) taken |= 1u << i;
     float sel_v[kMaxK];
     int sel_i[kMaxK];
 #pragma unroll
@@ -62,25 +77,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;  // none yet
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            if (i >= per) break;
+        for (int i = 0; i < PER; ++i) {
             const int e = i * kWave + lane;
-            // bitwise, not short-circuit, operators: no branches
-            const bool take = !((taken >> i) & 1u) & ((bi == 0x7FFFFFFF) | (v[i] > bv) | ((v[i] == bv) & (e < bi)));
+            const bool take = !((taken >> i) & 1u) & ((v[i] > bv) | ((v[i] == bv) & (e < bi)));
             bv = take ? v[i] : bv;
             bi = take ? e : bi;
         }
+        argmax_step<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
+        argmax_step<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
+        argmax_step<0x124>(bv, bi);  // row_ror:4
+        argmax_step<0x128>(bv, bi);  // row_ror:8
+        const int ib = __builtin_bit_cast(int, bv);
+        float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ib, 0));
+        int ri = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            const bool take = (oi != 0x7FFFFFFF) & ((bi == 0x7FFFFFFF) | (ov > bv) | ((ov == bv) & (oi < bi)));
-            bv = take ? ov : bv;
-            bi = take ? oi : bi;
-        }
-        sel_v[j] = bv;
-        sel_i[j] = bi;
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        for (int r = 1; r < 4; ++r)
+            better_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(ib, 16 * r)),
+                      __builtin_amdgcn_readlane(bi, 16 * r), rv, ri);
+        sel_v[j] = rv;
+        sel_i[j] = ri;
+        taken |= ((ri & (kWave - 1)) == lane ? 1u : 0u) << ((ri / kWave) & 31);
     }
     // softmax over the picks, in pick order (the same sum on every lane)
     const float top = sel_v[0];
@@ -223,9 +239,13 @@ hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t t
                             float *w, int32_t *offsets, int32_t *perm, int32_t *slot_row, int32_t *slot_of_pair,
                             hipStream_t stream) {
     if (T > 0) {
-        const int64_t per = kRouteThreads / kWave;
-        hipLaunchKernelGGL(route_topk_kernel, dim3((uint32_t)((T + per - 1) / per)), dim3(kRouteThreads), 0, stream,
-                           logits, T, E, topk, ids, w);
+        const dim3 grid((uint32_t)((T + kRouteThreads / kWave - 1) / (kRouteThreads / kWave))), block(kRouteThreads);
+        const int per = (E + kWave - 1) / kWave;  // logits per lane, rounded up to a power of two
+        if (per <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, stream, logits, T, E, topk, ids, w);
+        else if (per <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, stream, logits, T, E, topk, ids, w);
+        else if (per <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, stream, logits, T, E, topk, ids, w);
+        else if (per <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, stream, logits, T, E, topk, ids, w);
+        else hipLaunchKernelGGL(route_topk_kernel<kPerLane>, grid, block, 0, stream, logits, T, E, topk, ids, w);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
