@@ -12,12 +12,12 @@
 //    k rounds of a wave-wide (value, -id) arg-max (DPP within rows, scalar reads
 //    across them) pick the experts in descending order (ties -> lower id), then a
 //    softmax over the k picks, all without divergent branches.
-//  * bucket: one workgroup; per-expert counts with LDS integer atomics, an
-//    exclusive scan, then a stable placement: pairs are taken in chunks of 1024
-//    in increasing pair index; inside a wave, lanes with the same expert are
-//    found with ballots over the expert id bits, and per-wave counts in LDS
-//    give each pair its rank among equal experts -- deterministic, no atomics
-//    on positions.
+//  * bucket: one workgroup; each wave counts the experts of its contiguous range
+//    of pairs (LDS integer atomics), an exclusive scan over experts gives the
+//    offsets and each wave's first slot per expert, then every wave places its
+//    own pairs in increasing pair index (ballots over the expert id bits rank
+//    lanes with the same expert) -- stable, deterministic, no atomics on
+//    positions.
 //  * combine: out[t] = sum_j w[t][j] * y[slot(t, j)] + y_shared[t], float4 wide.
 #include "w4a8_internal.hpp"
 
@@ -123,79 +123,108 @@ constexpr int kBucketWaves = kBucketThreads / kWave;
 
 // shared_T > 0 appends a shared expert (index E) whose T slots follow the routed
 // ones: offsets[E+1] = P + T, and slot P + t reads activation row t.
+//
+// Wave w owns the contiguous pair range [w C, (w + 1) C), C = ceil(P / 16):
+//  1. per-wave expert counts in LDS (integer atomics: the totals are exact);
+//  2. offsets[e] = exclusive scan of the totals (wave scans, then the wave totals),
+//     and the first slot of wave w's pairs of expert e = offsets[e] + the counts of
+//     waves before w;
+//  3. each wave walks its range 64 pairs at a time in increasing pair index: lanes
+//     holding the same expert are found with ballots over the expert id bits, a lane's
+//     slot is its expert's running slot plus its rank among those lanes, and the
+//     lowest of them advances the running slot.
+// Slots are therefore ordered by expert, then by pair index (stable), with no
+// atomics on positions; four barriers in all.
+// kBatch 64-pair chunks have their expert ids loaded together (their latencies overlap).
+template <int kBatch>
 __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *__restrict__ ids, int64_t P, int32_t E,
                                                                 int32_t k, int64_t shared_T,
                                                                 int32_t *__restrict__ offsets,
                                                                 int32_t *__restrict__ perm,
                                                                 int32_t *__restrict__ slot_row,
                                                                 int32_t *__restrict__ slot_of_pair) {
-    __shared__ int32_t count[kMaxE];
-    __shared__ int32_t base[kMaxE];      // offsets[e] + pairs of e already placed
-    __shared__ int32_t scan[kBucketThreads];
-    __shared__ uint8_t wave_cnt[kBucketWaves][kMaxE];  // <= 64 per wave
+    __shared__ int32_t hist[kBucketWaves][kMaxE];  // counts, then each wave's running slot
+    __shared__ int32_t wave_sum[kBucketWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t C = (P + kBucketWaves - 1) / kBucketWaves;
+    const int64_t p0 = wave * C, p1 = (p0 + C < P) ? p0 + C : P;
 
-    for (int e = tid; e < E; e += kBucketThreads) count[e] = 0;
-    for (int i = tid; i < kBucketWaves * kMaxE; i += kBucketThreads) (&wave_cnt[0][0])[i] = 0;
+    for (int i = tid; i < kBucketWaves * kMaxE; i += kBucketThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int64_t p = tid; p < P; p += kBucketThreads) atomicAdd(&count[ids[p]], 1);
-    __syncthreads();
-
-    // exclusive scan of count[0..E) (E <= 1024 = one entry per thread)
-    scan[tid] = tid < E ? count[tid] : 0;
-    __syncthreads();
-    for (int off = 1; off < kBucketThreads; off <<= 1) {
-        const int32_t v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    for (int64_t c0 = p0; c0 < p1; c0 += kBatch * kWave) {
+        int e[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t p = c0 + j * kWave + lane;
+            e[j] = p < p1 ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (e[j] >= 0) atomicAdd(&hist[wave][e[j]], 1);
     }
+    __syncthreads();
+
+    // exclusive scan over experts of the totals (one expert per thread, E <= 1024)
+    int32_t total = 0;
+    if (tid < E)
+        for (int w2 = 0; w2 < kBucketWaves; ++w2) total += hist[w2][tid];
+    int32_t incl = total;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wave_sum[wave] = incl;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w2 = 0; w2 < wave; ++w2) before += wave_sum[w2];
     if (tid < E) {
-        const int32_t excl = scan[tid] - count[tid];
-        base[tid] = excl;
-        offsets[tid] = excl;
+        int32_t run = before + incl - total;  // offsets[tid]
+        offsets[tid] = run;
+        for (int w2 = 0; w2 < kBucketWaves; ++w2) {
+            const int32_t c = hist[w2][tid];
+            hist[w2][tid] = run;
+            run += c;
+        }
     }
-    if (tid == 0) {
-        offsets[E] = scan[kBucketThreads - 1];
-        if (shared_T > 0) offsets[E + 1] = scan[kBucketThreads - 1] + (int32_t)shared_T;
+    if (tid == kBucketThreads - 1) {
+        const int32_t all = before + incl;  // the last thread's inclusive sum covers every expert
+        offsets[E] = all;
+        if (shared_T > 0) offsets[E + 1] = all + (int32_t)shared_T;
     }
     __syncthreads();
 
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-    for (int64_t c0 = 0; c0 < P; c0 += kBucketThreads) {
-        const int64_t p = c0 + tid;
-        const bool valid = p < P;
-        const int e = valid ? ids[p] : -1;
-        // lanes of this wave holding the same expert
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const uint64_t bit = __ballot(valid && ((e >> b) & 1));
-            peers &= ((e >> b) & 1) ? bit : ~bit;
+    for (int64_t b0 = p0; b0 < p1; b0 += kBatch * kWave) {
+        int eb[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t p = b0 + j * kWave + lane;
+            eb[j] = p < p1 ? ids[p] : 0;
         }
-        const int rank_in_wave = __popcll(peers & lt_mask);
-        const bool leader = valid && rank_in_wave == 0;
-        if (leader) wave_cnt[wave][e] = (uint8_t)__popcll(peers);
-        __syncthreads();
-        if (valid) {
-            int32_t before = base[e];
-            for (int w2 = 0; w2 < wave; ++w2) before += wave_cnt[w2][e];
-            const int32_t slot = before + rank_in_wave;
-            perm[slot] = (int32_t)p;
-            slot_of_pair[p] = slot;
-            if (slot_row) slot_row[slot] = (int32_t)(p / k);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (b0 + j * kWave >= p1) break;  // wave-uniform: no pairs left in this range
+            const int64_t p = b0 + j * kWave + lane;
+            const bool valid = p < p1;
+            const int e = eb[j];
+            uint64_t peers = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const uint64_t bit = __ballot(valid && ((e >> b) & 1));
+                peers &= ((e >> b) & 1) ? bit : ~bit;
+            }
+            const int rank = __popcll(peers & lt_mask);
+            const int32_t start = valid ? hist[wave][e] : 0;  // all lanes read before any lane writes
+            if (valid) {
+                const int32_t slot = start + rank;
+                perm[slot] = (int32_t)p;
+                slot_of_pair[p] = slot;
+                if (slot_row) slot_row[slot] = (int32_t)(p / k);
+            }
+            if (valid && rank == 0) hist[wave][e] = start + __popcll(peers);
         }
-        __syncthreads();
-        if (tid < E) {
-            int32_t add = 0;
-            for (int w2 = 0; w2 < kBucketWaves; ++w2) add += wave_cnt[w2][tid];
-            base[tid] += add;
-        }
-        __syncthreads();
-        if (leader) wave_cnt[wave][e] = 0;
-        __syncthreads();
     }
     if (slot_row)
         for (int64_t t = tid; t < shared_T; t += kBucketThreads) slot_row[P + t] = (int32_t)t;
@@ -249,8 +278,14 @@ hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t t
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, T * topk, E, topk,
-                       with_shared ? T : (int64_t)0, offsets, perm, slot_row, slot_of_pair);
+    // one chunk per wave for small batches, eight chunks' ids in flight for large ones
+    const int64_t P = T * topk, shared = with_shared ? T : (int64_t)0;
+    if (P <= (int64_t)kBucketThreads)
+        hipLaunchKernelGGL(bucket_kernel<1>, dim3(1), dim3(kBucketThreads), 0, stream, ids, P, E, topk, shared, offsets,
+                           perm, slot_row, slot_of_pair);
+    else
+        hipLaunchKernelGGL(bucket_kernel<8>, dim3(1), dim3(kBucketThreads), 0, stream, ids, P, E, topk, shared, offsets,
+                           perm, slot_row, slot_of_pair);
     return hipGetLastError();
 }
 
