@@ -822,6 +822,15 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
     const int arow_l = tid / S::A_TPR, apart = tid % S::A_TPR;
     int64_t arow = -1;
     if (arow_l < rows.rows) arow = row_index ? (int64_t)row_index[rows.slot0 + arow_l] : rows.slot0 + arow_l;
+    // row scales for the epilogue, read now (they arrive during the group loop instead
+    // of stalling the stores at the end); the first barrier below publishes them
+    __shared__ float row_as[S::BM];
+    __shared__ int8_t row_ok[S::BM];
+    if (!ISUMS && apart == 0) {
+        const bool ok = arow >= 0 && arow < R;
+        row_as[arow_l] = ok ? a_scale[arow] : 0.0f;
+        row_ok[arow_l] = ok ? 1 : 0;
+    }
     if (arow < 0 || arow >= R) arow = 0;
     const v4u *aglob = reinterpret_cast<const v4u *>(qa + arow * K + apart * S::A_BYTES);
     const int bcol_l = tid / S::B_TPC, bpart = tid % S::B_TPC;
@@ -969,15 +978,12 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < rows.rows) {
+                if (m < rows.rows && row_ok[m]) {
                     const int64_t slot = rows.slot0 + m;
-                    const int64_t row = row_index ? (int64_t)row_index[slot] : slot;
-                    if (row >= 0 && row < R) {
-                        const float as = a_scale[row];
+                    const float as = row_as[m];
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
-                    }
+                    for (int j = 0; j < 2; ++j)
+                        if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
                 }
             }
     }
