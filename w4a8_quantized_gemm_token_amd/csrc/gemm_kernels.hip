@@ -1451,7 +1451,13 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
         return (c > cmin && c <= cmax) ? ((c + S::BM - 1) / S::BM) * ntn : 0;
     });
     const int64_t G = K / G128;
-    for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+    // Round r hands each XCD (workgroup b runs on XCD b % 8) a contiguous run of units,
+    // row tiles fastest: the workgroups of one XCD then share their experts' weight
+    // columns and activation rows in that XCD's L2.
+    const int64_t nb = gridDim.x;
+    const bool by_xcd = nb % 8 == 0;
+    const int64_t lane_u = by_xcd ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    for (int64_t u = lane_u; u < total; u += nb) {
         const int e = find_expert(pfx, E, u);
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
         const int64_t mt = (c + S::BM - 1) / S::BM;
