@@ -707,8 +707,21 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
     float asc = 0.0f;
     dec_tiles<U, SPLIT, ISUMS, TM>(
         dsm, red, (int)M, K, wpk, wsc, wzp, N, t0, t1,
-        [&](int phase) {  // qa[M][K] -> LDS, 16-byte pieces through registers
-            if (phase == 0) {
+        [&](int phase) {  // qa[M][K] -> LDS
+            if constexpr (TM) {
+                // straight from memory to LDS (no registers, no LDS write instructions);
+                // the first U weight windows (three loads each) are issued between the
+                // two phases, so waiting for all but 3 U loads covers exactly the rows
+                if (phase == 0) {
+                    stage_rows_dma(dsm, lda, qa, K, (int)M, [](int r) { return (int64_t)r; });
+                    if (threadIdx.x < M) asc = a_scale[threadIdx.x];
+                    return;
+                }
+                __builtin_amdgcn_s_waitcnt(t3_waitcnt(3 * U, 15));
+                if (threadIdx.x < M) sasc[threadIdx.x] = asc;
+                return;
+            }
+            if (phase == 0) {  // 16-byte pieces through registers
                 // up to eight pieces per thread in flight at once; pieces past the end
                 // read as zeros (buffer range check) and are not stored
                 if (batched) {
