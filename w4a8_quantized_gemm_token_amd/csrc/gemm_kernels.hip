@@ -1578,12 +1578,9 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
         else if (one) W4A8_DEC1(UU, SS, false, 1, false);                                                           \
         else W4A8_DEC1(UU, SS, false, 8, false);                                                                    \
     } while (0)
-    // tile-major weights: contiguous streams take a deeper ring (four windows in flight)
-#define W4A8_DEC_TM(UU, SS)                                                                                         \
-    do {                                                                                                            \
-        if (one) W4A8_DEC1(UU, SS, false, 1, true);                                                                 \
-        else W4A8_DEC1(UU, SS, false, 8, true);                                                                     \
-    } while (0)
+    // tile-major weights: contiguous streams take a deeper ring (four windows in flight);
+    // the rows are staged by direct-to-LDS loads, so the staging batch does not apply
+#define W4A8_DEC_TM(UU, SS) W4A8_DEC1(UU, SS, false, 1, true)
     if (tm) {
         if (split == 4) {
             if (nwin % 4 == 0) W4A8_DEC_TM(4, 4);
