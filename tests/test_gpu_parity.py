@@ -295,11 +295,12 @@ def test_route_ties_go_to_lower_expert():
 
 
 # ------------------------------------------------------------------ grouped GEMM
-@pytest.mark.parametrize("K", [384, 1024])
+@pytest.mark.parametrize("K", [384, 1024, 8192, 8704])
 def test_grouped_gemm_mixed_bucket_sizes(orc, K):
-    """Experts with 0, 1, 17, 64, 65 and 200 slots: both loops (K=1024 takes the
-    decode-style loop for the small experts, K=384 the streaming one), an empty
-    expert, ragged tails, gathered rows; every output element checked."""
+    """Experts with 0, 1, 17, 64, 65 and 200 slots: both loops (K=1024, 8192 and 8704
+    take the decode-style loop for the small experts, the last with its staged rows
+    near the LDS limit; K=384 the streaming one), an empty expert, ragged tails,
+    gathered rows; every output element checked."""
     w4 = w4mod()
     counts = [0, 1, 17, 64, 65, 200]
     E, N = len(counts), 160
