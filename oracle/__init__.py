@@ -67,6 +67,14 @@ class Oracle:
         lib.orc_dequantize_weights.argtypes = [p, p, p, i64, i64, i64, p]
         lib.orc_pack_nibbles.restype = ctypes.c_int
         lib.orc_pack_nibbles.argtypes = [p, i64, i64, p]
+        lib.orc_channel_absmax.restype = None
+        lib.orc_channel_absmax.argtypes = [p, i64, i64, p]
+        lib.orc_smooth_factors.restype = None
+        lib.orc_smooth_factors.argtypes = [p, p, i64, ctypes.c_double, p, p]
+        lib.orc_smooth_weights.restype = None
+        lib.orc_smooth_weights.argtypes = [p, i64, i64, p, p]
+        lib.orc_quantize_act_smooth.restype = None
+        lib.orc_quantize_act_smooth.argtypes = [p, i64, i64, i64, p, p, p]
         lib.orc_unpack_nibbles.restype = None
         lib.orc_unpack_nibbles.argtypes = [p, i64, i64, p]
         lib.orc_quantize_act.restype = None
@@ -164,6 +172,42 @@ class Oracle:
         lib.orc_quantize_act(_ptr(x), M, K, K, _ptr(qa), _ptr(sc))
         return qa, sc
 
+
+    # --------------------------------------------------------------------------- O8
+    def channel_absmax(self, A: np.ndarray) -> np.ndarray:
+        """max over rows of |A[r][k]| (fp32 [K])."""
+        A = _c(A, np.float32)
+        rows, K = A.shape
+        out = np.empty((K,), np.float32)
+        self.lib.orc_channel_absmax(_ptr(A), rows, K, _ptr(out))
+        return out
+
+    def smooth_factors(self, ax, aw, alpha: float = 0.5):
+        """[p3 §3.4] per-channel smoothing factors s and 1/s (fp32 [K] each)."""
+        ax = _c(ax, np.float32)
+        aw = _c(aw, np.float32)
+        K = ax.shape[0]
+        s = np.empty((K,), np.float32)
+        inv = np.empty((K,), np.float32)
+        self.lib.orc_smooth_factors(_ptr(ax), _ptr(aw), K, float(alpha), _ptr(s), _ptr(inv))
+        return s, inv
+
+    def smooth_weights(self, W, s) -> np.ndarray:
+        """W[n][k] * s[k] (fp32)."""
+        W = _c(W, np.float32)
+        N, K = W.shape
+        out = np.empty((N, K), np.float32)
+        self.lib.orc_smooth_weights(_ptr(W), N, K, _ptr(_c(s, np.float32)), _ptr(out))
+        return out
+
+    def quantize_act_smooth(self, x, inv_s):
+        """Per-token INT8 of x[m][k] * inv_s[k]: (qa int8 [M][K], a_scale fp32 [M])."""
+        x = _c(x, np.float32)
+        M, K = x.shape
+        qa = np.empty((M, K), np.int8)
+        sc = np.empty((M,), np.float32)
+        self.lib.orc_quantize_act_smooth(_ptr(x), M, K, K, _ptr(_c(inv_s, np.float32)), _ptr(qa), _ptr(sc))
+        return qa, sc
 
     # --------------------------------------------------------------------------- O3/O4
     def group_isums(self, qa, q, zp16, group: int = 128) -> np.ndarray:

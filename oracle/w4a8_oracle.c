@@ -29,6 +29,10 @@
  *   - An activation row whose scale is 0 (all-zero row, or max|x|/127 underflows
  *     in fp32) has codes 0.
  *   - A group whose scale exceeds the largest finite fp16 is an error.
+ *   - Smoothing (O8): s_k = ax_k^alpha / aw_k^(1-alpha) from the channel maxima
+ *     of calibration activations and of the weights (1 where either is 0),
+ *     rounded to fp32; inv_s_k = fp32(1 / s_k); weights multiplied by s and
+ *     activations by inv_s, one fp32 product each, before the quantizers.
  *
  * Parity pins: see tests/test_oracle_pins.py.  Every function here is pinned
  * by at least one test against values the pages print, closed forms, brute
@@ -225,6 +229,63 @@ void orc_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t 
             qa[m * K + k] = (int8_t)v;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O8: per-channel activation smoothing [p3 §3.4]: a factor per input        */
+/* channel moves part of the activations' outlier range into the weights,    */
+/* so that both fall in a range the quantizers handle.  The page gives the   */
+/* idea, not a formula; the reading used here (listed in the design notes):  */
+/*   ax_k = max_m |x_cal[m][k]| over calibration rows,                        */
+/*   aw_k = max_n |W[n][k]|,                                                  */
+/*   s_k  = ax_k^alpha / aw_k^(1 - alpha)   (double, then fp32),              */
+/*          1 where ax_k or aw_k is 0,                                        */
+/*   inv_s_k = 1 / s_k                      (double, then fp32),              */
+/* the weights become W[n][k] * s_k (one fp32 product) before the group      */
+/* quantization, and at run time every activation is multiplied by inv_s_k  */
+/* (one fp32 product) before the per-token quantizer O2.                     */
+/* ------------------------------------------------------------------------ */
+void orc_channel_absmax(const float *A, int64_t rows, int64_t K, float *out)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        float m = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) {
+            float a = fabsf(A[r * K + k]);
+            if (a > m)
+                m = a;
+        }
+        out[k] = m;
+    }
+}
+
+void orc_smooth_factors(const float *ax, const float *aw, int64_t K, double alpha, float *s, float *inv_s)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        double f = 1.0;
+        if (ax[k] > 0.0f && aw[k] > 0.0f)
+            f = pow((double)ax[k], alpha) / pow((double)aw[k], 1.0 - alpha);
+        s[k] = (float)f;
+        inv_s[k] = (float)(1.0 / (double)s[k]);
+    }
+}
+
+void orc_smooth_weights(const float *W, int64_t N, int64_t K, const float *s, float *out)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = W[n * K + k] * s[k];
+}
+
+/* O2 applied to the smoothed activations x[m][k] * inv_s[k] (fp32 products). */
+void orc_quantize_act_smooth(const float *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s, int8_t *qa,
+                             float *a_scale)
+{
+    float *y = (float *)malloc((size_t)(M * K) * sizeof(float));
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            y[m * K + k] = x[m * ldx + k] * inv_s[k];
+    orc_quantize_act(y, M, K, K, qa, a_scale);
+    free(y);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -354,4 +354,72 @@ def pin_silu_mul_and_combine(orc):
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ smoothing [p3 §3.4]
+def pin_smoothing_factor_closed_forms(orc):
+    """alpha = 0 gives s = 1/aw, alpha = 1 gives s = ax, alpha = 0.5 gives sqrt(ax/aw),
+    which leaves both operands with the same channel maximum sqrt(ax*aw); a zero maximum on
+    either side gives 1; inv_s is the fp32 rounding of 1/s for the stored fp32 s."""
+    ax = np.array([4.0, 0.0, 9.0, 2.0, 1e-3, 50.0], np.float32)
+    aw = np.array([1.0, 2.0, 0.25, 0.0, 3.0, 0.02], np.float32)
+    live = (ax > 0) & (aw > 0)
+    axd, awd = ax.astype(np.float64), aw.astype(np.float64)
+    aws = np.where(live, awd, 1.0)
+    for alpha, closed in ((0.0, 1.0 / aws), (1.0, axd), (0.5, np.sqrt(axd / aws))):
+        s, inv = orc.smooth_factors(ax, aw, alpha)
+        want = np.where(live, closed, 1.0)
+        assert np.allclose(s, want, rtol=2.0 ** -23, atol=0), (alpha, s, want)
+        assert np.array_equal(inv, (1.0 / s.astype(np.float64)).astype(np.float32))
+    s, _ = orc.smooth_factors(ax, aw, 0.5)
+    sd = s.astype(np.float64)
+    assert np.allclose((axd / sd)[live], (awd * sd)[live], rtol=3e-7)
+    assert np.allclose((axd / sd)[live], np.sqrt(axd * awd)[live], rtol=3e-7)
+    rng = np.random.default_rng(21)
+    ax = np.exp(rng.uniform(-8, 8, 4096)).astype(np.float32)
+    aw = np.exp(rng.uniform(-8, 8, 4096)).astype(np.float32)
+    s, inv = orc.smooth_factors(ax, aw, 0.37)
+    want = ax.astype(np.float64) ** 0.37 / aw.astype(np.float64) ** 0.63
+    assert np.allclose(s, want, rtol=2.0 ** -23, atol=0)
+    assert np.array_equal(inv, (1.0 / s.astype(np.float64)).astype(np.float32))
+
+
+def pin_smoothing_absmax_and_product(orc):
+    """Channel maxima against numpy on a signed, non-square matrix; smoothing leaves the
+    unquantized product unchanged up to the three fp32 roundings of each term."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((7, 300)).astype(np.float32) * np.exp(rng.uniform(-3, 3, 300)).astype(np.float32)
+    x[:, 5] = -np.abs(x[:, 5]) * 40
+    W = rng.standard_normal((11, 300)).astype(np.float32)
+    W[:, 9] = 0.0
+    ax, aw = orc.channel_absmax(x), orc.channel_absmax(W)
+    assert np.array_equal(ax, np.abs(x).max(0)) and np.array_equal(aw, np.abs(W).max(0))
+    s, inv = orc.smooth_factors(ax, aw, 0.5)
+    assert s[9] == 1.0
+    Ws = orc.smooth_weights(W, s)
+    xd, Wd = x.astype(np.float64), W.astype(np.float64)
+    xs = (xd * inv.astype(np.float64)).astype(np.float32)      # the product the quantizer sees
+    ref = xd @ Wd.T
+    got = xs.astype(np.float64) @ Ws.astype(np.float64).T
+    bound = 4 * 2.0 ** -24 * (np.abs(xd) @ np.abs(Wd).T) + 1e-30
+    assert np.all(np.abs(got - ref) <= bound)
+    assert np.array_equal(Ws, (Wd * s.astype(np.float64)).astype(np.float32))
+
+
+def pin_smoothing_quantizer_special_cases(orc):
+    """inv_s = 1 is the plain per-token quantizer; alpha = 1 calibrated on the row itself
+    divides each entry by its own magnitude, so every nonzero code is +-127 and the row
+    scale is 1/127 (up to one ulp of the fp32 quotient x * (1/|x|))."""
+    x = np.random.default_rng(23).standard_normal((5, 256)).astype(np.float32) * 3
+    x[2, :7] = 0.0
+    q0, s0 = orc.quantize_act(x)
+    q1, s1 = orc.quantize_act_smooth(x, np.ones(256, np.float32))
+    assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
+    for r in range(5):
+        ax = orc.channel_absmax(x[r:r + 1])
+        s, inv = orc.smooth_factors(ax, np.ones(256, np.float32), 1.0)
+        q, sc = orc.quantize_act_smooth(x[r:r + 1], inv)
+        want = np.where(x[r] > 0, 127, np.where(x[r] < 0, -127, 0))
+        assert np.array_equal(q[0], want), r
+        assert abs(float(sc[0]) - 1.0 / 127.0) <= 2.0 ** -23 / 127.0, sc
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

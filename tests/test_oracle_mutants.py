@@ -49,6 +49,14 @@ MUTANTS = [
     ("bucket_offsets_inclusive", "offsets[ids[p] + 1] += 1;", "offsets[ids[p]] += 1;"),
     ("silu_uses_plus", "h[p * I + i] = g / (1.0 + exp(-g)) * u;", "h[p * I + i] = g / (1.0 + exp(g)) * u;"),
     ("combine_drops_shared", "acc += (double)y_shared[t * H + c];", "acc += 0.0;"),
+    ("smooth_alpha_swapped", "pow((double)ax[k], alpha) / pow((double)aw[k], 1.0 - alpha)",
+     "pow((double)ax[k], 1.0 - alpha) / pow((double)aw[k], alpha)"),
+    ("smooth_zero_guard_either", "if (ax[k] > 0.0f && aw[k] > 0.0f)", "if (ax[k] > 0.0f || aw[k] > 0.0f)"),
+    ("smooth_inv_from_unrounded", "inv_s[k] = (float)(1.0 / (double)s[k]);", "inv_s[k] = (float)(1.0 / f);"),
+    ("smooth_weights_divide", "out[n * K + k] = W[n * K + k] * s[k];", "out[n * K + k] = W[n * K + k] / s[k];"),
+    ("smooth_act_divides", "y[m * K + k] = x[m * ldx + k] * inv_s[k];", "y[m * K + k] = x[m * ldx + k] / inv_s[k];"),
+    ("absmax_signed", "float a = fabsf(A[r * K + k]);", "float a = A[r * K + k];"),
+    ("absmax_transposed", "float a = fabsf(A[r * K + k]);", "float a = fabsf(A[k * rows + r]);"),
 ]
 
 
