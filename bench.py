@@ -330,10 +330,56 @@ def prefill(torch, w4, synthetic, reps=10):
     return {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
-def secondary(torch, w4, synthetic):
-    """Prefill (M=4096, K=N=8192) TOPS and MoE layer times; context figures."""
+def smoothing(torch, w4, synthetic):
+    """Per-channel smoothing on the decode workload (K=8192, 0.1% x20 weight outliers, 4 x50
+    activation channels): the first 4096 output columns, factors from 48 calibration tokens
+    (rows 16..63 of the activation draw), error of 16 other tokens against the fp64
+    unquantized product, plain vs smoothed; and the quantizer's time with and without
+    the per-channel factor (M=16)."""
     dev = torch.device("cuda:0")
-    out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic)}
+    N, K, M = 4096, 8192, 16
+    W = torch.empty((N, K), dtype=torch.float32, device=dev)
+    synthetic.fill_weights_device(W, 0, synthetic.TAG_W, 0, K, 0, "outliers")
+    x = torch.from_numpy(synthetic.activations_with_outlier_channels(0, 64, K)).to(dev)
+    xe, xcal = x[:M].contiguous(), x[M:].contiguous()
+    exact = xe.double() @ W.double().T
+    aw = w4.channel_absmax(W).cpu().numpy()
+    ax = w4.channel_absmax(xcal).cpu().numpy()
+
+    def rel_err(qa, sc, packed, scale, zp):
+        y = w4.gemm(qa, sc, packed, scale, zp).double()
+        return float(torch.linalg.norm(y - exact) / torch.linalg.norm(exact))
+
+    res = {"rel_err_plain": round(rel_err(*w4.quantize_act(xe), *w4.pack_weights_device(W)), 4)}
+    for alpha in (0.25, 0.5, 0.75):
+        s, inv = w4.smooth_factors(ax, aw, alpha)
+        s_d, inv_d = torch.from_numpy(s).to(dev), torch.from_numpy(inv).to(dev)
+        res[f"rel_err_alpha{alpha}"] = round(rel_err(*w4.quantize_act_smooth(xe, inv_d),
+                                                     *w4.pack_weights_device_smooth(W, s_d)), 4)
+    qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sc = torch.empty((M,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for name, launch in (("quantize_us_plain", w4.prepare_quantize_act(xe, qa, sc)),
+                         ("quantize_us_smoothed", w4.prepare_quantize_act_smooth(xe, inv_d, qa, sc))):
+        for _ in range(50):
+            launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(500):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(a.elapsed_time(b) / 500 * 1e3, 2)
+    del W, exact
+    torch.cuda.empty_cache()
+    return res
+
+
+def secondary(torch, w4, synthetic):
+    """Prefill (M=4096, K=N=8192) TOPS, MoE layer times and the smoothing figures; context."""
+    dev = torch.device("cuda:0")
+    out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
+           "smoothing_K8192_N4096_M16": smoothing(torch, w4, synthetic)}
     from tests.gpu_common import device_experts
     # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
     # back-to-back prepared launches that rotate three copies of the 250 MB expert set

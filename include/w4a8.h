@@ -72,7 +72,7 @@ typedef enum {
     W4A8_EWORKSPACE = 4     /* the caller's workspace is smaller than the call needs */
 } w4a8_status;
 
-#define W4A8_ABI_VERSION 3
+#define W4A8_ABI_VERSION 4
 #define W4A8_GROUP 128
 
 int w4a8_abi_version(void);
@@ -116,6 +116,47 @@ w4a8_status w4a8_unpack_weights(const uint8_t *packed, const uint16_t *scale, co
  * 16-byte aligned, or K % 16 != 0.  M == 0 is a no-op. */
 w4a8_status w4a8_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
                               int8_t *qa, float *a_scale, hipStream_t stream);
+
+/* ------------------------------------------------- per-channel smoothing
+ * [p3 §3.4] (quantization-friendly transforms): a positive factor s_k per input
+ * channel moves part of the activations' outlier range into the weights; the
+ * layer's product is unchanged because x_k * W[n][k] = (x_k / s_k) * (W[n][k] * s_k).
+ * The page names the idea without a formula; this library reads it as
+ *   ax_k = max over calibration rows of |x[r][k]|,  aw_k = max over n of |W[n][k]|,
+ *   s_k  = ax_k^alpha / aw_k^(1 - alpha)  (double, rounded to fp32; 1 where
+ *          ax_k or aw_k is 0),  inv_s_k = fp32(1 / s_k),
+ * weights quantized as fp32(W[n][k] * s_k) and activations as fp32(x[m][k] * inv_s_k).
+ * The GEMM entry points take the results unchanged. */
+
+/* Device, asynchronous.  out[k] = max over r < rows of |A[r][k]| for a row-major
+ * A (row stride lda >= K floats); rows == 0 gives 0 (A may then be NULL).  Exact
+ * (a maximum has no rounding) and deterministic.  Device memory.  Errors:
+ * W4A8_EINVAL for null pointers, rows < 0, K <= 0 or lda < K. */
+w4a8_status w4a8_channel_absmax(const float *A, int64_t rows, int64_t K, int64_t lda, float *out,
+                                hipStream_t stream);
+
+/* Host, synchronous.  s[K] and inv_s[K] from the channel maxima ax[K] (activations)
+ * and aw[K] (weights) with migration strength alpha in [0, 1], as stated above.
+ * Host memory owned by the caller.  Errors: W4A8_EINVAL for null pointers, K <= 0,
+ * alpha outside [0, 1], a negative or non-finite maximum, or a factor that is not
+ * a positive finite fp32 (extreme ratios of the two maxima). */
+w4a8_status w4a8_smooth_factors(const float *ax, const float *aw, int64_t K, double alpha,
+                                float *s, float *inv_s);
+
+/* Device, asynchronous.  w4a8_pack_weights_device of the smoothed weights
+ * fp32(W[n][k] * s[k]) (s: device fp32 [K]); the smoothed matrix is not stored.
+ * W and s 8-byte aligned.  Errors as w4a8_pack_weights_device. */
+w4a8_status w4a8_pack_weights_device_smooth(const float *W, int64_t N, int64_t K, int32_t group,
+                                            const float *s, uint8_t *packed, uint16_t *scale,
+                                            uint16_t *zp, hipStream_t stream);
+
+/* Device, asynchronous.  w4a8_quantize_act of the smoothed rows fp32(x[m][k] *
+ * inv_s[k]) (inv_s: device fp32 [K]); the row maximum and the codes are taken of
+ * those products and the scaled rows are never written out.  Errors as
+ * w4a8_quantize_act, plus a null inv_s. */
+w4a8_status w4a8_quantize_act_smooth(const float *x, int64_t M, int64_t K, int64_t ldx,
+                                     const float *inv_s, int8_t *qa, float *a_scale,
+                                     hipStream_t stream);
 
 /* --------------------------------------------------------------------- GEMM */
 

@@ -101,6 +101,14 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_gemm_tm(f, f, 4, 256, f, 128, 256, f, None) == EUNSUPPORTED
     assert lib.w4a8_gemm_tm(None, f, 4, 256, f, 128, 128, f, None) == EINVAL
     assert lib.w4a8_gemm_tm(f, f, 0, 256, f, 128, 128, f, None) == 0
+    # smoothing entry points
+    assert lib.w4a8_channel_absmax(f, 4, 256, 200, f, None) == EINVAL
+    assert lib.w4a8_channel_absmax(None, 4, 256, 256, f, None) == EINVAL
+    assert lib.w4a8_quantize_act_smooth(f, 4, 256, 256, None, f, f, None) == EINVAL
+    assert lib.w4a8_quantize_act_smooth(f, 4, 200, 256, f, f, f, None) == EINVAL
+    assert lib.w4a8_quantize_act_smooth(f, 0, 256, 256, f, f, f, None) == 0
+    assert lib.w4a8_pack_weights_device_smooth(f, 16, 256, 128, _fake(4100), f, f, f, None) == EINVAL
+    assert lib.w4a8_pack_weights_device_smooth(f, 16, 256, 64, f, f, f, f, None) == EUNSUPPORTED
     # MoE FFN layer: sizes, workspace alignment and size
     need = lib.w4a8_moe_ffn_workspace_size(64, 7168, 2048, 384, 8)
     assert need > 0
@@ -180,3 +188,28 @@ def test_host_packer_bit_exact_vs_oracle(orc, case):
         W[7, ::2] = 0.5                  # ties in w / s
         W[8] = W[8] * 1000               # large range
     _packer_matches_oracle(orc, W)
+
+
+def test_smooth_factors_bit_exact_vs_oracle_and_rejects(orc):
+    """The host factor routine gives the oracle's fp32 factors bit for bit (both take
+    the power in double, round once to fp32, and invert the stored fp32 factor)."""
+    K = 8192
+    x = synthetic.activations_with_outlier_channels(0, 64, K)
+    W = synthetic.weights(7, synthetic.TAG_W, 0, 96, K)
+    ax, aw = orc.channel_absmax(x[16:]), orc.channel_absmax(W)
+    ax[:5] = 0.0
+    aw[5:9] = 0.0
+    for alpha in (0.0, 0.25, 0.5, 0.8, 1.0):
+        s, inv = w4.smooth_factors(ax, aw, alpha)
+        so, invo = orc.smooth_factors(ax, aw, alpha)
+        assert np.array_equal(s.view(np.uint32), so.view(np.uint32)), alpha
+        assert np.array_equal(inv.view(np.uint32), invo.view(np.uint32)), alpha
+    for bad_alpha in (-0.1, 1.5, float("nan")):
+        with pytest.raises(w4.W4A8Error):
+            w4.smooth_factors(ax, aw, bad_alpha)
+    neg = ax.copy()
+    neg[3] = -1.0
+    with pytest.raises(w4.W4A8Error):
+        w4.smooth_factors(neg, aw, 0.5)
+    with pytest.raises(w4.W4A8Error):      # 1 / 1e-45 overflows fp32
+        w4.smooth_factors(np.ones(4, np.float32), np.full(4, 1e-45, np.float32), 0.0)

@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 GROUP = 128
-ABI_VERSION = 3          # W4A8_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4          # W4A8_ABI_VERSION of the header this binding follows
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
@@ -26,6 +26,7 @@ EXPORTS = (
     "w4a8_pack_weights", "w4a8_pack_weights_device", "w4a8_unpack_weights",
     "w4a8_quantize_act", "w4a8_gemm", "w4a8_gemm_debug_isums", "w4a8_gemm_path",
     "w4a8_tm_bytes", "w4a8_weights_to_tm", "w4a8_gemm_tm",
+    "w4a8_channel_absmax", "w4a8_smooth_factors", "w4a8_pack_weights_device_smooth", "w4a8_quantize_act_smooth",
     "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_silu_mul_quantize", "w4a8_moe_combine",
     "w4a8_moe_ffn_workspace_size", "w4a8_moe_ffn_workspace_layout", "w4a8_moe_ffn",
 )
@@ -63,6 +64,10 @@ def load() -> ctypes.CDLL:
         "w4a8_gemm": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, p, p]),
         "w4a8_gemm_debug_isums": (ctypes.c_int, [p, i64, i64, p, p, i64, i32, i32, p, p]),
         "w4a8_gemm_path": (ctypes.c_int, [p, p, i64, i64, p, p, p, i64, i32, i32, p, p]),
+        "w4a8_channel_absmax": (ctypes.c_int, [p, i64, i64, i64, p, p]),
+        "w4a8_smooth_factors": (ctypes.c_int, [p, p, i64, ctypes.c_double, p, p]),
+        "w4a8_pack_weights_device_smooth": (ctypes.c_int, [p, i64, i64, i32, p, p, p, p, p]),
+        "w4a8_quantize_act_smooth": (ctypes.c_int, [p, i64, i64, i64, p, p, p, p]),
         "w4a8_tm_bytes": (sz, [i64, i64]),
         "w4a8_weights_to_tm": (ctypes.c_int, [p, p, p, i64, i64, i32, p, p]),
         "w4a8_gemm_tm": (ctypes.c_int, [p, p, i64, i64, p, i64, i32, p, p]),
@@ -134,7 +139,7 @@ def _dev_rows_ptr(t):
     """Device pointer of a 2-D tensor whose rows may be strided (unit stride inside a row)."""
     torch = _torch()
     assert isinstance(t, torch.Tensor) and t.is_cuda and t.dim() == 2, "2-D device tensor expected"
-    assert t.stride(1) == 1 or t.shape[1] <= 1, "rows must be contiguous"
+    assert t.stride(1) == 1 or t.shape[1] <= 1 or t.shape[0] == 0, "rows must be contiguous"
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -214,6 +219,63 @@ def gemm(qa, a_scale, packed, scale, zp, path: int = 0, out=None, group: int = G
     _call("w4a8_gemm_path", _dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(packed), _dev_ptr(scale),
           _dev_ptr(zp), N, group, path, _dev_ptr(out), _stream(qa.device))
     return out
+
+
+# ----------------------------------------------------------------- smoothing [p3 §3.4]
+def channel_absmax(A):
+    """A float32 [rows][K] (device, unit column stride) -> max over rows of |A| (float32 [K], device)."""
+    torch = _torch()
+    rows, K = A.shape
+    out = _empty((K,), torch.float32, A)
+    _call("w4a8_channel_absmax", _dev_rows_ptr(A), rows, K, A.stride(0) if rows else K, _dev_ptr(out),
+          _stream(A.device))
+    return out
+
+
+def smooth_factors(ax: np.ndarray, aw: np.ndarray, alpha: float = 0.5):
+    """Host: (s, inv_s) float32 [K] from the activation and weight channel maxima."""
+    ax = np.ascontiguousarray(ax, np.float32)
+    aw = np.ascontiguousarray(aw, np.float32)
+    K = ax.shape[0]
+    assert aw.shape == (K,)
+    s = np.empty((K,), np.float32)
+    inv = np.empty((K,), np.float32)
+    vp = ctypes.c_void_p
+    _call("w4a8_smooth_factors", ax.ctypes.data_as(vp), aw.ctypes.data_as(vp), K, float(alpha),
+          s.ctypes.data_as(vp), inv.ctypes.data_as(vp))
+    return s, inv
+
+
+def pack_weights_device_smooth(W, s, group: int = GROUP):
+    """Device packer of the smoothed weights W[n][k] * s[k] (W float32 [N][K], s float32 [K], device)."""
+    torch = _torch()
+    N, K = W.shape
+    assert tuple(s.shape) == (K,) and s.is_contiguous()
+    out = (_empty((N, K // 2), torch.uint8, W), _empty((K // group, N), torch.int16, W),
+           _empty((K // group, N), torch.int16, W))
+    _call("w4a8_pack_weights_device_smooth", _dev_ptr(W), N, K, group, _dev_ptr(s), _dev_ptr(out[0]),
+          _dev_ptr(out[1]), _dev_ptr(out[2]), _stream(W.device))
+    return out
+
+
+def quantize_act_smooth(x, inv_s):
+    """Per-token INT8 of x[m][k] * inv_s[k] (device): (qa int8 [M][K], a_scale float32 [M])."""
+    torch = _torch()
+    M, K = x.shape
+    assert tuple(inv_s.shape) == (K,) and inv_s.is_contiguous()
+    qa = _empty((M, K), torch.int8, x)
+    sc = _empty((M,), torch.float32, x)
+    _call("w4a8_quantize_act_smooth", _dev_rows_ptr(x), M, K, x.stride(0), _dev_ptr(inv_s), _dev_ptr(qa),
+          _dev_ptr(sc), _stream(x.device))
+    return qa, sc
+
+
+def prepare_quantize_act_smooth(x, inv_s, qa, a_scale) -> Launch:
+    """Prepared w4a8_quantize_act_smooth writing into preallocated qa and a_scale."""
+    M, K = x.shape
+    assert tuple(qa.shape) == (M, K) and tuple(a_scale.shape) == (M,) and tuple(inv_s.shape) == (K,)
+    return Launch("w4a8_quantize_act_smooth", (_dev_rows_ptr(x), M, K, x.stride(0), _dev_ptr(inv_s), _dev_ptr(qa),
+                                               _dev_ptr(a_scale), _stream(x.device)), (x, inv_s, qa, a_scale))
 
 
 def prepare_quantize_act(x, qa, a_scale) -> Launch:

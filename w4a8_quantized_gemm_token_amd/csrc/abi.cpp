@@ -177,7 +177,48 @@ w4a8_status w4a8_pack_weights_device(const float *W, int64_t N, int64_t K, int32
     W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
     if (w4a8_status st = check_group(group, K)) return st;
     W4A8_REQUIRE(((uintptr_t)W & 7u) == 0, W4A8_EINVAL, "W must be 8-byte aligned");
-    return hip_status(launch_pack_weights(W, N, K, packed, scale, zp, stream), "pack_weights_device launch");
+    return hip_status(launch_pack_weights(W, N, K, nullptr, packed, scale, zp, stream), "pack_weights_device launch");
+}
+
+w4a8_status w4a8_pack_weights_device_smooth(const float *W, int64_t N, int64_t K, int32_t group, const float *s,
+                                            uint8_t *packed, uint16_t *scale, uint16_t *zp, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(W && s && packed && scale && zp, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
+    if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(((uintptr_t)W & 7u) == 0 && ((uintptr_t)s & 7u) == 0, W4A8_EINVAL, "W and s must be 8-byte aligned");
+    return hip_status(launch_pack_weights(W, N, K, s, packed, scale, zp, stream), "pack_weights_device_smooth launch");
+}
+
+w4a8_status w4a8_channel_absmax(const float *A, int64_t rows, int64_t K, int64_t lda, float *out, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE((A || rows == 0) && out, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(rows >= 0 && K > 0 && lda >= K, W4A8_EINVAL, "bad sizes rows=%lld K=%lld lda=%lld", (long long)rows,
+                 (long long)K, (long long)lda);
+    W4A8_REQUIRE((K + 63) / 64 < (1ll << 31), W4A8_EINVAL, "K too large");
+    return hip_status(launch_channel_absmax(A, rows, K, lda, out, stream), "channel_absmax launch");
+}
+
+w4a8_status w4a8_smooth_factors(const float *ax, const float *aw, int64_t K, double alpha, float *s, float *inv_s) {
+    clear_error();
+    W4A8_REQUIRE(ax && aw && s && inv_s, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(K > 0, W4A8_EINVAL, "K=%lld must be positive", (long long)K);
+    W4A8_REQUIRE(alpha >= 0.0 && alpha <= 1.0, W4A8_EINVAL, "alpha=%g must lie in [0, 1]", alpha);
+    for (int64_t k = 0; k < K; ++k)
+        W4A8_REQUIRE(std::isfinite(ax[k]) && ax[k] >= 0.0f && std::isfinite(aw[k]) && aw[k] >= 0.0f, W4A8_EINVAL,
+                     "channel maxima must be finite and non-negative (channel %lld)", (long long)k);
+    for (int64_t k = 0; k < K; ++k) {
+        // migration strength alpha: activation range ax^alpha over weight range aw^(1-alpha)
+        const double f = (ax[k] > 0.0f && aw[k] > 0.0f) ? std::pow((double)ax[k], alpha) /
+                                                                std::pow((double)aw[k], 1.0 - alpha)
+                                                          : 1.0;
+        const float sf = (float)f;
+        W4A8_REQUIRE(std::isfinite(sf) && sf > 0.0f, W4A8_EINVAL,
+                     "smoothing factor of channel %lld is not a positive finite fp32", (long long)k);
+        s[k] = sf;
+        inv_s[k] = (float)(1.0 / (double)sf);
+    }
+    return W4A8_OK;
 }
 
 w4a8_status w4a8_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa, float *a_scale,
@@ -190,7 +231,20 @@ w4a8_status w4a8_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
     W4A8_REQUIRE(aligned16(qa), W4A8_EINVAL, "qa must be 16-byte aligned");
     W4A8_REQUIRE(M < (1ll << 31), W4A8_EINVAL, "M too large");
     if (M == 0) return W4A8_OK;
-    return hip_status(launch_quantize_act(x, M, K, ldx, qa, a_scale, stream), "quantize_act launch");
+    return hip_status(launch_quantize_act(x, M, K, ldx, nullptr, qa, a_scale, stream), "quantize_act launch");
+}
+
+w4a8_status w4a8_quantize_act_smooth(const float *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s, int8_t *qa,
+                                     float *a_scale, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(x && inv_s && qa && a_scale, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(M >= 0 && K > 0 && ldx >= K, W4A8_EINVAL, "bad sizes M=%lld K=%lld ldx=%lld", (long long)M,
+                 (long long)K, (long long)ldx);
+    W4A8_REQUIRE(K % 16 == 0, W4A8_EINVAL, "K=%lld must be a multiple of 16", (long long)K);
+    W4A8_REQUIRE(aligned16(qa), W4A8_EINVAL, "qa must be 16-byte aligned");
+    W4A8_REQUIRE(M < (1ll << 31), W4A8_EINVAL, "M too large");
+    if (M == 0) return W4A8_OK;
+    return hip_status(launch_quantize_act(x, M, K, ldx, inv_s, qa, a_scale, stream), "quantize_act_smooth launch");
 }
 
 static w4a8_status check_gemm(const int8_t *qa, int64_t M, int64_t K, const uint8_t *packed, const uint16_t *scale,
@@ -420,7 +474,7 @@ w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t
     hipError_t err = launch_moe_route(logits, T, E, topk, 1, ids, w, offsets, perm, slot_row, sop, stream);
     if (err != hipSuccess) return hip_status(err, "moe_ffn: route");
     if (T == 0) return W4A8_OK;
-    if ((err = launch_quantize_act(x, T, H, H, qa, a_scale, stream)) != hipSuccess)
+    if ((err = launch_quantize_act(x, T, H, H, nullptr, qa, a_scale, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: quantize");
     // top-k picks distinct experts per token, so no expert (the shared one included) gets more than T slots
     if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S, T,

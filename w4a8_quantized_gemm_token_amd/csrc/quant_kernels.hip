@@ -4,10 +4,16 @@
 //    computed in the kernel at forward time; [p3 §2.1]: q = round(x/s),
 //    s = max|x| / 127).  One workgroup per row; the row maximum is a wave64
 //    shuffle reduction followed by a cross-wave LDS step.
+//    With a per-channel factor inv_s (smoothing, [p3 §3.4]) each entry is first
+//    multiplied by inv_s[k] in fp32; the maximum and the codes are taken of that
+//    product, so the scaled row is never written out.
 //  * silu_mul_quantize: the MoE expert activation silu(gate) * up followed by the
 //    same per-row quantizer (the INT8 input of the down projection).
 //  * pack_weights: group-wise asymmetric 4-bit weight quantization and nibble
-//    packing ([p2 §2.1, §2.2]), one wave per (output feature, group of 128).
+//    packing ([p2 §2.1, §2.2]), one wave per (output feature, group of 128),
+//    optionally of the smoothed weights W[n][k] * s[k].
+//  * channel_absmax: per-channel maxima of |A| over rows, the statistic the
+//    smoothing factors are computed from.
 //
 // Page keys: [p1] hotelren.com/news/5173946 "Kimi 2.7 MoE: from 4-bit storage to
 // INT8 compute"; [p2] pptc.cn/news/121597 "Kimi 2.7 MoE, 4-bit storage to INT8,
@@ -40,11 +46,28 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xFF) << 24);
 }
 
+// Four consecutive columns of a row, times the smoothing factors when SMOOTH
+// (one fp32 product per entry).  VEC: row and inv_s are 16-byte aligned.
+template <bool VEC, bool SMOOTH>
+__device__ __forceinline__ float4 load4(const float *row, const float *inv_s, int64_t c) {
+    float4 v;
+    if (VEC) v = reinterpret_cast<const float4 *>(row)[c];
+    else v = make_float4(row[4 * c], row[4 * c + 1], row[4 * c + 2], row[4 * c + 3]);
+    if (SMOOTH) {
+        float4 f;
+        if (VEC) f = reinterpret_cast<const float4 *>(inv_s)[c];
+        else f = make_float4(inv_s[4 * c], inv_s[4 * c + 1], inv_s[4 * c + 2], inv_s[4 * c + 3]);
+        v = make_float4(v.x * f.x, v.y * f.y, v.z * f.z, v.w * f.w);
+    }
+    return v;
+}
+
 // x rows of K floats (stride ldx); each thread owns groups of 4 consecutive
-// columns.  VEC: x rows are 16-byte aligned, so float4 loads are used.
-template <bool VEC>
+// columns.  VEC: x rows (and inv_s) are 16-byte aligned, so float4 loads are used.
+template <bool VEC, bool SMOOTH>
 __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const float *__restrict__ x, int64_t K,
-                                                                   int64_t ldx, int8_t *__restrict__ qa,
+                                                                   int64_t ldx, const float *__restrict__ inv_s,
+                                                                   int8_t *__restrict__ qa,
                                                                    float *__restrict__ a_scale) {
     __shared__ float red[kActWaves];
     const int64_t m = blockIdx.x;
@@ -52,9 +75,7 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const float *
     const int64_t K4 = K / 4;
     float amax = 0.0f;
     for (int64_t c = threadIdx.x; c < K4; c += kActThreads) {
-        float4 v;
-        if (VEC) v = reinterpret_cast<const float4 *>(row)[c];
-        else v = make_float4(row[4 * c], row[4 * c + 1], row[4 * c + 2], row[4 * c + 3]);
+        const float4 v = load4<VEC, SMOOTH>(row, inv_s, c);
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     amax = block_max(amax, red);
@@ -62,9 +83,7 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const float *
     if (threadIdx.x == 0) a_scale[m] = s;
     uint32_t *out = reinterpret_cast<uint32_t *>(qa + m * K);
     for (int64_t c = threadIdx.x; c < K4; c += kActThreads) {
-        float4 v;
-        if (VEC) v = reinterpret_cast<const float4 *>(row)[c];
-        else v = make_float4(row[4 * c], row[4 * c + 1], row[4 * c + 2], row[4 * c + 3]);
+        const float4 v = load4<VEC, SMOOTH>(row, inv_s, c);
         out[c] = pack4_i8(quantize_i8(v.x, s), quantize_i8(v.y, s), quantize_i8(v.z, s), quantize_i8(v.w, s));
     }
 }
@@ -73,20 +92,21 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const float *
 // per row keeps the row in registers between the maximum and the quantization, so
 // the row is read from memory once (this is the latency-critical small-M case).
 constexpr int kRowThreads = 1024;
-template <int VPT4>
+template <int VPT4, bool SMOOTH>
 __global__ __launch_bounds__(kRowThreads) void quantize_act_row_kernel(const float *__restrict__ x, int64_t K,
-                                                                       int64_t ldx, int8_t *__restrict__ qa,
+                                                                       int64_t ldx, const float *__restrict__ inv_s,
+                                                                       int8_t *__restrict__ qa,
                                                                        float *__restrict__ a_scale) {
     __shared__ float red[kRowThreads / kWave];
     const int64_t m = blockIdx.x;
-    const float4 *row = reinterpret_cast<const float4 *>(x + m * ldx);
+    const float *row = x + m * ldx;
     const int64_t K4 = K / 4;
     float4 v[VPT4];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT4; ++i) {
         const int64_t c = threadIdx.x + (int64_t)i * kRowThreads;
-        v[i] = c < K4 ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[i] = c < K4 ? load4<true, SMOOTH>(row, inv_s, c) : make_float4(0.f, 0.f, 0.f, 0.f);
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     }
     amax = wave_max(amax);
@@ -170,9 +190,13 @@ __global__ __launch_bounds__(kActThreads) void silu_mul_quantize_long_kernel(con
 
 // One wave per (output feature n, group g); lane l owns weights 2l and 2l+1 of
 // the group, i.e. exactly packed byte l of the group.
+// SMOOTH: each weight is first multiplied by its channel's smoothing factor
+// s[k] (one fp32 product), so the smoothed matrix is never written out.
 constexpr int kPackThreads = 256;
+template <bool SMOOTH>
 __global__ __launch_bounds__(kPackThreads) void pack_weights_kernel(const float *__restrict__ W, int64_t N,
-                                                                    int64_t K, uint8_t *__restrict__ packed,
+                                                                    int64_t K, const float *__restrict__ sf,
+                                                                    uint8_t *__restrict__ packed,
                                                                     uint16_t *__restrict__ scale,
                                                                     uint16_t *__restrict__ zp) {
     const int64_t G = K / W4A8_GROUP;
@@ -180,7 +204,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_weights_kernel(const float 
     if (unit >= N * G) return;
     const int64_t n = unit / G, g = unit % G;
     const int lane = threadIdx.x % kWave;
-    const float2 w = reinterpret_cast<const float2 *>(W + n * K + g * W4A8_GROUP)[lane];
+    float2 w = reinterpret_cast<const float2 *>(W + n * K + g * W4A8_GROUP)[lane];
+    if (SMOOTH) {
+        const float2 f = reinterpret_cast<const float2 *>(sf + g * W4A8_GROUP)[lane];
+        w = make_float2(w.x * f.x, w.y * f.y);
+    }
     // the range always contains 0: zp in [0, 15], (q - zp) in [-15, 15]
     const float lo = wave_min(fminf(fminf(w.x, w.y), 0.0f));
     const float hi = wave_max(fmaxf(fmaxf(w.x, w.y), 0.0f));
@@ -200,30 +228,63 @@ __global__ __launch_bounds__(kPackThreads) void pack_weights_kernel(const float 
     }
 }
 
+// Channel maxima out[k] = max_r |A[r][k]| (calibration for smoothing): a workgroup
+// owns 64 columns, each of its 16 waves a residue class of rows, read one coalesced
+// 256-byte row slice at a time; the 16 partial maxima meet in LDS.  The maximum
+// does not depend on the order, so the result is exact and deterministic.
+constexpr int kAbsThreads = 1024;
+__global__ __launch_bounds__(kAbsThreads) void channel_absmax_kernel(const float *__restrict__ A, int64_t rows,
+                                                                     int64_t K, int64_t lda, float *__restrict__ out) {
+    __shared__ float part[kAbsThreads / kWave][kWave];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int64_t k = (int64_t)blockIdx.x * kWave + lane;
+    float m = 0.0f;
+    if (k < K)
+        for (int64_t r = wave; r < rows; r += kAbsThreads / kWave) m = fmaxf(m, fabsf(A[r * lda + k]));
+    part[wave][lane] = m;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 1; i < kAbsThreads / kWave; ++i) m = fmaxf(m, part[i][lane]);
+        if (k < K) out[k] = m;
+    }
+}
+
 }  // namespace
 
 namespace w4a8 {
 
-hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa, float *a_scale,
-                               hipStream_t stream) {
-    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
-    if (vec && K <= 4 * 2 * kRowThreads) {
-        hipLaunchKernelGGL(quantize_act_row_kernel<2>, dim3((uint32_t)M), dim3(kRowThreads), 0, stream, x, K, ldx, qa,
-                           a_scale);
-        return hipGetLastError();
-    }
-    if (vec && K <= 4 * 4 * kRowThreads) {
-        hipLaunchKernelGGL(quantize_act_row_kernel<4>, dim3((uint32_t)M), dim3(kRowThreads), 0, stream, x, K, ldx, qa,
-                           a_scale);
-        return hipGetLastError();
-    }
-    if (vec)
-        hipLaunchKernelGGL(quantize_act_kernel<true>, dim3((uint32_t)M), dim3(kActThreads), 0, stream, x, K, ldx, qa,
-                           a_scale);
+hipError_t launch_channel_absmax(const float *A, int64_t rows, int64_t K, int64_t lda, float *out,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(channel_absmax_kernel, dim3((uint32_t)((K + kWave - 1) / kWave)), dim3(kAbsThreads), 0, stream,
+                       A, rows, K, lda, out);
+    return hipGetLastError();
+}
+
+template <bool SMOOTH>
+static hipError_t quantize_act_forms(const float *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
+                                     int8_t *qa, float *a_scale, hipStream_t stream) {
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0) && (!SMOOTH || (uintptr_t)inv_s % 16 == 0);
+    const dim3 grid((uint32_t)M);
+    if (vec && K <= 4 * 2 * kRowThreads)
+        hipLaunchKernelGGL((quantize_act_row_kernel<2, SMOOTH>), grid, dim3(kRowThreads), 0, stream, x, K, ldx, inv_s,
+                           qa, a_scale);
+    else if (vec && K <= 4 * 4 * kRowThreads)
+        hipLaunchKernelGGL((quantize_act_row_kernel<4, SMOOTH>), grid, dim3(kRowThreads), 0, stream, x, K, ldx, inv_s,
+                           qa, a_scale);
+    else if (vec)
+        hipLaunchKernelGGL((quantize_act_kernel<true, SMOOTH>), grid, dim3(kActThreads), 0, stream, x, K, ldx, inv_s,
+                           qa, a_scale);
     else
-        hipLaunchKernelGGL(quantize_act_kernel<false>, dim3((uint32_t)M), dim3(kActThreads), 0, stream, x, K, ldx,
+        hipLaunchKernelGGL((quantize_act_kernel<false, SMOOTH>), grid, dim3(kActThreads), 0, stream, x, K, ldx, inv_s,
                            qa, a_scale);
     return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s, int8_t *qa,
+                               float *a_scale, hipStream_t stream) {
+    return inv_s ? quantize_act_forms<true>(x, M, K, ldx, inv_s, qa, a_scale, stream)
+                 : quantize_act_forms<false>(x, M, K, ldx, nullptr, qa, a_scale, stream);
 }
 
 hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh, float *h_scale, float *h_out,
@@ -242,13 +303,17 @@ hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_
     return hipGetLastError();
 }
 
-hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *packed, uint16_t *scale, uint16_t *zp,
-                               hipStream_t stream) {
+hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, const float *s, uint8_t *packed, uint16_t *scale,
+                               uint16_t *zp, hipStream_t stream) {
     const int64_t units = N * (K / W4A8_GROUP);
     const int64_t per_block = kPackThreads / kWave;
-    const int64_t blocks = (units + per_block - 1) / per_block;
-    hipLaunchKernelGGL(pack_weights_kernel, dim3((uint32_t)blocks), dim3(kPackThreads), 0, stream, W, N, K, packed,
-                       scale, zp);
+    const dim3 grid((uint32_t)((units + per_block - 1) / per_block));
+    if (s)
+        hipLaunchKernelGGL(pack_weights_kernel<true>, grid, dim3(kPackThreads), 0, stream, W, N, K, s, packed, scale,
+                           zp);
+    else
+        hipLaunchKernelGGL(pack_weights_kernel<false>, grid, dim3(kPackThreads), 0, stream, W, N, K, s, packed, scale,
+                           zp);
     return hipGetLastError();
 }
 

@@ -18,12 +18,16 @@ w4a8_status hip_status(hipError_t err, const char *what);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
-hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *qa,
+// inv_s: per-channel smoothing factors [K] (nullptr: none).
+hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s, int8_t *qa,
                                float *a_scale, hipStream_t stream);
 hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh,
                                     float *h_scale, float *h_out, hipStream_t stream);
-hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *packed,
+// s: per-channel smoothing factors [K] applied before quantization (nullptr: none).
+hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, const float *s, uint8_t *packed,
                                uint16_t *scale, uint16_t *zp, hipStream_t stream);
+hipError_t launch_channel_absmax(const float *A, int64_t rows, int64_t K, int64_t lda, float *out,
+                                 hipStream_t stream);
 
 // Dense GEMM.  path: 1 = streaming (M <= 64), 2 = tiled.  isums != nullptr selects
 // the debug epilogue that stores the per-group int32 sums instead of `out`.
