@@ -67,6 +67,12 @@ class Oracle:
         lib.orc_dequantize_weights.argtypes = [p, p, p, i64, i64, i64, p]
         lib.orc_pack_nibbles.restype = ctypes.c_int
         lib.orc_pack_nibbles.argtypes = [p, i64, i64, p]
+        lib.orc_quantize_weights_sym.restype = ctypes.c_int
+        lib.orc_quantize_weights_sym.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.orc_percentile.restype = ctypes.c_double
+        lib.orc_percentile.argtypes = [p, i64, ctypes.c_double]
+        lib.orc_clip_rows.restype = None
+        lib.orc_clip_rows.argtypes = [p, i64, i64, ctypes.c_double, p]
         lib.orc_channel_absmax.restype = None
         lib.orc_channel_absmax.argtypes = [p, i64, i64, p]
         lib.orc_smooth_factors.restype = None
@@ -172,6 +178,32 @@ class Oracle:
         lib.orc_quantize_act(_ptr(x), M, K, K, _ptr(qa), _ptr(sc))
         return qa, sc
 
+
+    # --------------------------------------------------------------------------- O9/O10
+    def quantize_weights_sym(self, W, group: int = 128):
+        """[p3 §2.1] symmetric 4-bit: (codes q+8 uint8 [N][K], scale fp16 bits [G][N], zp fp16 bits = 8)."""
+        W = _c(W, np.float32)
+        N, K = W.shape
+        q = np.empty((N, K), np.uint8)
+        sc = np.empty((K // group, N), np.uint16)
+        zp = np.empty((K // group, N), np.uint16)
+        rc = self.lib.orc_quantize_weights_sym(_ptr(W), N, K, group, _ptr(q), _ptr(sc), _ptr(zp))
+        if rc != 0:
+            raise ValueError("orc_quantize_weights_sym rejected the input")
+        return q, sc, zp
+
+    def percentile(self, v, pct: float) -> float:
+        """Linear-interpolation percentile of a float32 vector, in double."""
+        v = _c(v, np.float32)
+        return self.lib.orc_percentile(_ptr(v), v.shape[0], float(pct))
+
+    def clip_rows(self, W, pct: float) -> np.ndarray:
+        """[p2 §2.2, §5.1] each row clamped to its [100-pct, pct] percentiles (fp32)."""
+        W = _c(W, np.float32)
+        N, K = W.shape
+        out = np.empty((N, K), np.float32)
+        self.lib.orc_clip_rows(_ptr(W), N, K, float(pct), _ptr(out))
+        return out
 
     # --------------------------------------------------------------------------- O8
     def channel_absmax(self, A: np.ndarray) -> np.ndarray:

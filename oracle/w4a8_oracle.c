@@ -29,6 +29,9 @@
  *   - An activation row whose scale is 0 (all-zero row, or max|x|/127 underflows
  *     in fp32) has codes 0.
  *   - A group whose scale exceeds the largest finite fp16 is an error.
+ *   - Symmetric weights (O9) keep the stored format: code q + 8 with zp 8.
+ *   - Percentile clipping (O10) is per output column over its K weights,
+ *     linear interpolation between order statistics, both tails.
  *   - Smoothing (O8): s_k = ax_k^alpha / aw_k^(1-alpha) from the channel maxima
  *     of calibration activations and of the weights (1 where either is 0),
  *     rounded to fp32; inv_s_k = fp32(1 / s_k); weights multiplied by s and
@@ -152,6 +155,95 @@ int orc_quantize_weights(const float *W, int64_t N, int64_t K, int64_t group,
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O9: symmetric 4-bit weights [p3 §2.1] (zero point fixed at 0; scale =    */
+/* max|w| / (2^(b-1) - 1) = max|w| / 7; q = round(w / scale) in [-7, 7]),   */
+/* [p2 §2.1] names it as the simpler alternative.  Stored in the same       */
+/* format as O1 so that every GEMM serves it: code = q + 8, zp = 8, so that  */
+/* code - zp = q.  fp16 scale rules as O1 (codes use the stored scale; a     */
+/* scale that rounds to 0 stores 1.0; an fp16 overflow is an error).         */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_weights_sym(const float *W, int64_t N, int64_t K, int64_t group,
+                             uint8_t *q, uint16_t *scale16, uint16_t *zp16)
+{
+    if (N <= 0 || K <= 0 || group <= 0 || K % group != 0)
+        return -1;
+    int64_t G = K / group;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float *w = W + n * K + g * group;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < group; ++i) {
+                if (!isfinite(w[i]))
+                    return -1;
+                if (fabsf(w[i]) > amax)
+                    amax = fabsf(w[i]);
+            }
+            uint16_t sh = orc_f32_to_f16(amax / 7.0f);
+            if ((sh & 0x7FFFu) == 0x7C00u)
+                return -1;
+            float s = orc_f16_to_f32(sh);
+            if (s == 0.0f) {
+                sh = 0x3C00u;
+                s = 1.0f;
+            }
+            scale16[n + g * N] = sh;
+            zp16[n + g * N] = orc_f32_to_f16(8.0f);
+            for (int64_t i = 0; i < group; ++i) {
+                float r = rintf(w[i] / s);
+                if (r < -7.0f)
+                    r = -7.0f;
+                if (r > 7.0f)
+                    r = 7.0f;
+                q[n * K + g * group + i] = (uint8_t)((int)r + 8);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O10: percentile range clipping [p2 §2.2, §5.1]: the range is taken from   */
+/* percentiles instead of the minimum and maximum, and weights beyond the    */
+/* percentile are cut back to it.  Reading: per output column n, over its K  */
+/* weights, the p-th and (100-p)-th percentiles with linear interpolation    */
+/* between order statistics (position h = (K-1) * pct / 100,                 */
+/* v[floor h] + (h - floor h) * (v[floor h + 1] - v[floor h]), in double),   */
+/* rounded to fp32; every weight is clamped to [lo, hi] before O1 or O9.     */
+/* p = 100 gives [min, max]: no change.                                      */
+/* ------------------------------------------------------------------------ */
+static int orc_cmp_float(const void *a, const void *b)
+{
+    float x = *(const float *)a, y = *(const float *)b;
+    return (x > y) - (x < y);
+}
+
+double orc_percentile(const float *v, int64_t n, double pct)
+{
+    float *t = (float *)malloc((size_t)n * sizeof(float));
+    memcpy(t, v, (size_t)n * sizeof(float));
+    qsort(t, (size_t)n, sizeof(float), orc_cmp_float);
+    double h = (double)(n - 1) * pct / 100.0;
+    int64_t i = (int64_t)floor(h);
+    double r = (double)t[i];
+    if (i + 1 < n)
+        r += (h - (double)i) * ((double)t[i + 1] - (double)t[i]);
+    free(t);
+    return r;
+}
+
+void orc_clip_rows(const float *W, int64_t N, int64_t K, double pct, float *out)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float lo = (float)orc_percentile(W + n * K, K, 100.0 - pct);
+        float hi = (float)orc_percentile(W + n * K, K, pct);
+        for (int64_t k = 0; k < K; ++k) {
+            float w = W[n * K + k];
+            out[n * K + k] = w < lo ? lo : (w > hi ? hi : w);
+        }
+    }
 }
 
 /* Dequantized weight w_hat = (q - zp) * scale  [p2 §2.1, §2.2]. */

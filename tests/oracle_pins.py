@@ -354,6 +354,69 @@ def pin_silu_mul_and_combine(orc):
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ packer variants
+def pin_symmetric_weights_closed_forms(orc):
+    """[p3 §2.1] b-bit symmetric: scale = max|w| / (2^(b-1) - 1) = max|w| / 7 for 4 bits,
+    q = round(w / scale).  On an exact lattice j * step (j = -7..7, both ends present) the
+    scale is step and the stored codes are j + 8 with zp 8; range [-1, 1] gives scale
+    fp16(1/7) and 0.2 -> code 9; an all-zero group stores scale 1.0 and code 8."""
+    rng = np.random.default_rng(31)
+    N, K = 6, 512
+    steps = np.array([2.0 ** -6, 0.375, 2.0 ** -10, 0.0625, 1.5, 2.0 ** -4], np.float32)
+    j = rng.integers(-7, 8, (N, K))
+    j[:, ::128] = 7
+    j[:, 1::128] = -7
+    W = (j * steps[:, None]).astype(np.float32)
+    q, sc, zp = orc.quantize_weights_sym(W)
+    assert np.array_equal(q.astype(np.int64), j + 8)
+    assert np.array_equal(sc, np.tile(np.float16(steps).view(np.uint16), (K // 128, 1)))
+    assert np.all(zp == np.float16(8.0).view(np.uint16))
+    Wr = np.full((1, 128), 0.0, np.float32)
+    Wr[0, 0], Wr[0, 1], Wr[0, 2] = -1.0, 1.0, 0.2
+    q, sc, zp = orc.quantize_weights_sym(Wr)
+    assert sc[0, 0] == np.float16(np.float32(1.0) / np.float32(7.0)).view(np.uint16)
+    assert (q[0, 0], q[0, 1], q[0, 2], q[0, 3]) == (1, 15, 9, 8)
+    q, sc, _ = orc.quantize_weights_sym(np.zeros((2, 128), np.float32))
+    assert np.all(q == 8) and np.all(sc == 0x3C00)
+    # reconstruction bound on random data: |w - (q - 8) * s| <= s / 2 (+ fp32 slack)
+    W = rng.standard_normal((16, 1024)).astype(np.float32) * 0.02
+    q, sc, _ = orc.quantize_weights_sym(W)
+    s = np.repeat(np.float16(sc.view(np.float16)).astype(np.float64).T, 128, axis=1)
+    err = np.abs(W - (q.astype(np.float64) - 8) * s)
+    assert np.all(err <= s * (0.5 + 2.0 ** -19)) and q.min() >= 1 and q.max() <= 15
+
+
+def pin_percentile_against_numpy(orc):
+    """Linear-interpolation percentiles equal numpy's default method (computed in double);
+    0 and 100 give the minimum and the maximum exactly."""
+    rng = np.random.default_rng(32)
+    for n in (1, 2, 7, 128, 1000, 8192):
+        v = (rng.standard_normal(n) * np.exp(rng.uniform(-3, 3, n))).astype(np.float32)
+        for pct in (0.0, 0.1, 12.5, 50.0, 99.9, 100.0):
+            want = np.percentile(v.astype(np.float64), pct)
+            # numpy forms the position as (n-1) * (pct/100), the oracle as (n-1) * pct / 100:
+            # the two doubles differ by an ulp or so, which moves the result by ~1e-13 relative
+            assert np.isclose(orc.percentile(v, pct), want, rtol=1e-12, atol=0), (n, pct)
+        assert orc.percentile(v, 0.0) == v.min() and orc.percentile(v, 100.0) == v.max()
+
+
+def pin_clip_rows(orc):
+    """[p2 §2.2, §5.1] each row is clamped to its own [100-p, p] percentiles, rounded to
+    fp32; p = 100 changes nothing; at 99.9 on a row with eight x20 outliers among 8192
+    weights, only the tails move."""
+    rng = np.random.default_rng(33)
+    W = (rng.standard_normal((3, 8192)) * 0.02).astype(np.float32)
+    W[0, rng.choice(8192, 8, replace=False)] *= 20
+    assert np.array_equal(orc.clip_rows(W, 100.0), W)
+    C = orc.clip_rows(W, 99.9)
+    for n in range(3):
+        lo = np.float32(np.percentile(W[n].astype(np.float64), 0.1))
+        hi = np.float32(np.percentile(W[n].astype(np.float64), 99.9))
+        assert np.array_equal(C[n], np.clip(W[n], lo, hi))
+        assert (C[n] != W[n]).sum() <= 2 * 10
+    assert np.abs(C[0]).max() < np.abs(W[0]).max() / 5
+
+
 # ------------------------------------------------------------------ smoothing [p3 §3.4]
 def pin_smoothing_factor_closed_forms(orc):
     """alpha = 0 gives s = 1/aw, alpha = 1 gives s = ax, alpha = 0.5 gives sqrt(ax/aw),

@@ -49,6 +49,15 @@ MUTANTS = [
     ("bucket_offsets_inclusive", "offsets[ids[p] + 1] += 1;", "offsets[ids[p]] += 1;"),
     ("silu_uses_plus", "h[p * I + i] = g / (1.0 + exp(-g)) * u;", "h[p * I + i] = g / (1.0 + exp(g)) * u;"),
     ("combine_drops_shared", "acc += (double)y_shared[t * H + c];", "acc += 0.0;"),
+    ("sym_divides_by_8", "orc_f32_to_f16(amax / 7.0f)", "orc_f32_to_f16(amax / 8.0f)"),
+    ("sym_scale_transposed", "scale16[n + g * N] = sh;", "scale16[n * G + g] = sh;"),
+    ("sym_code_offset_7", "(uint8_t)((int)r + 8)", "(uint8_t)((int)r + 7)"),
+    ("sym_uses_signed_max", "if (fabsf(w[i]) > amax)\n                    amax = fabsf(w[i]);",
+     "if (w[i] > amax)\n                    amax = w[i];"),
+    ("percentile_no_interpolation", "r += (h - (double)i) * ((double)t[i + 1] - (double)t[i]);",
+     "r += 0.0 * ((double)t[i + 1] - (double)t[i]);"),
+    ("percentile_index_over_n", "double h = (double)(n - 1) * pct / 100.0;", "double h = (double)n * pct / 100.0;"),
+    ("clip_upper_only", "out[n * K + k] = w < lo ? lo : (w > hi ? hi : w);", "out[n * K + k] = w > hi ? hi : w;"),
     ("smooth_alpha_swapped", "pow((double)ax[k], alpha) / pow((double)aw[k], 1.0 - alpha)",
      "pow((double)ax[k], 1.0 - alpha) / pow((double)aw[k], alpha)"),
     ("smooth_zero_guard_either", "if (ax[k] > 0.0f && aw[k] > 0.0f)", "if (ax[k] > 0.0f || aw[k] > 0.0f)"),
