@@ -331,7 +331,7 @@ def prefill(torch, w4, synthetic, reps=10):
 
 
 def smoothing(torch, w4, synthetic):
-    """Per-channel smoothing on the decode workload (K=8192, 0.1% x20 weight outliers, 4 x50
+    """Packer variants and per-channel smoothing on the decode workload (K=8192, 0.1% x20 weight outliers, 4 x50
     activation channels): the first 4096 output columns, factors from 48 calibration tokens
     (rows 16..63 of the activation draw), error of 16 other tokens against the fp64
     unquantized product, plain vs smoothed; and the quantizer's time with and without
@@ -351,6 +351,14 @@ def smoothing(torch, w4, synthetic):
         return float(torch.linalg.norm(y - exact) / torch.linalg.norm(exact))
 
     res = {"rel_err_plain": round(rel_err(*w4.quantize_act(xe), *w4.pack_weights_device(W)), 4)}
+    # host packer variants on the same columns: symmetric codes, 99.9-percentile clipping
+    Wh = W.cpu().numpy()
+    for name, kw in (("rel_err_symmetric", {"symmetric": True}), ("rel_err_clip99.9", {"clip_percent": 99.9})):
+        packed, scale, zp = w4.pack_weights(Wh, **kw)
+        res[name] = round(rel_err(*w4.quantize_act(xe), torch.from_numpy(packed).to(dev),
+                                  torch.from_numpy(scale.view(np.int16)).to(dev),
+                                  torch.from_numpy(zp.view(np.int16)).to(dev)), 4)
+    del Wh
     for alpha in (0.25, 0.5, 0.75):
         s, inv = w4.smooth_factors(ax, aw, alpha)
         s_d, inv_d = torch.from_numpy(s).to(dev), torch.from_numpy(inv).to(dev)
@@ -379,7 +387,7 @@ def secondary(torch, w4, synthetic):
     """Prefill (M=4096, K=N=8192) TOPS, MoE layer times and the smoothing figures; context."""
     dev = torch.device("cuda:0")
     out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
-           "smoothing_K8192_N4096_M16": smoothing(torch, w4, synthetic)}
+           "quant_variants_K8192_N4096_M16": smoothing(torch, w4, synthetic)}
     from tests.gpu_common import device_experts
     # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
     # back-to-back prepared launches that rotate three copies of the 250 MB expert set

@@ -72,7 +72,7 @@ typedef enum {
     W4A8_EWORKSPACE = 4     /* the caller's workspace is smaller than the call needs */
 } w4a8_status;
 
-#define W4A8_ABI_VERSION 4
+#define W4A8_ABI_VERSION 5
 #define W4A8_GROUP 128
 
 int w4a8_abi_version(void);
@@ -89,6 +89,25 @@ const char *w4a8_last_error(void);
  * non-finite weights, or a group scale above the largest finite fp16. */
 w4a8_status w4a8_pack_weights(const float *W, int64_t N, int64_t K, int32_t group,
                               uint8_t *packed, uint16_t *scale, uint16_t *zp);
+
+/* Host, synchronous.  Packer variants in the same stored format, so every GEMM entry
+ * point takes their output unchanged:
+ *   mode W4A8_PACK_ASYMMETRIC: the packer above.
+ *   mode W4A8_PACK_SYMMETRIC: zero point fixed at 0 ([p2 §2.1] names it as the
+ *     simpler choice; [p3 §2.1] gives the b-bit form scale = max|w| / (2^(b-1) - 1)):
+ *     scale = fp16(max|w| / 7) per group, q = clamp(round(w / scale), -7, 7), stored as
+ *     code q + 8 with zp 8, so that (code - zp) = q.
+ *   clip_percent p in [50, 100] ([p2 §2.2, §5.1]: the range comes from percentiles, not
+ *     the extremes, and weights past them are cut back): each output column's K
+ *     weights are clamped to their own [100 - p, p] percentiles (linear interpolation
+ *     between order statistics at position (K - 1) * pct / 100, in double, rounded to
+ *     fp32) before the group quantizer.  p = 100 leaves the weights as they are.
+ * Host memory owned by the caller.  Errors as w4a8_pack_weights, plus W4A8_EINVAL for an
+ * unknown mode or p outside [50, 100]. */
+#define W4A8_PACK_ASYMMETRIC 0
+#define W4A8_PACK_SYMMETRIC 1
+w4a8_status w4a8_pack_weights_ex(const float *W, int64_t N, int64_t K, int32_t group, int32_t mode,
+                                 double clip_percent, uint8_t *packed, uint16_t *scale, uint16_t *zp);
 
 /* Device, asynchronous.  The same quantization as w4a8_pack_weights, run on the
  * GPU for W (device fp32 [N][K]) -- for weight sets too large to convert on the

@@ -213,3 +213,41 @@ def test_smooth_factors_bit_exact_vs_oracle_and_rejects(orc):
         w4.smooth_factors(neg, aw, 0.5)
     with pytest.raises(w4.W4A8Error):      # 1 / 1e-45 overflows fp32
         w4.smooth_factors(np.ones(4, np.float32), np.full(4, 1e-45, np.float32), 0.0)
+
+
+@pytest.mark.parametrize("symmetric,clip", [(True, 100.0), (False, 99.9), (True, 99.9), (False, 90.0), (True, 50.0)])
+@pytest.mark.parametrize("case", ["c2_rows", "c3_rows", "edge"])
+def test_host_packer_variants_bit_exact_vs_oracle(orc, case, symmetric, clip):
+    """Symmetric codes (q + 8, zp 8) and percentile clipping: the host packer's bytes equal
+    the oracle's, on outlier rows, offset rows and hand-made edge rows (zero groups, ties,
+    a constant row, a single spike)."""
+    if case == "c2_rows":
+        W = synthetic.weights_with_outliers(0, 28672, 8192, rows=np.arange(0, 28672, 997))
+    elif case == "c3_rows":
+        W = synthetic.weights_with_offset(0, 8192, 8192, rows=np.arange(0, 8192, 701))
+    else:
+        W = np.zeros((5, 512), np.float32)
+        W[1] = 0.25
+        W[2, :128] = np.arange(128) * 0.5 - 32.0
+        W[3, 300] = 9.0
+        W[4] = np.random.default_rng(5).standard_normal(512).astype(np.float32)
+    src = orc.clip_rows(W, clip) if clip < 100.0 else W
+    q, s, z = (orc.quantize_weights_sym if symmetric else orc.quantize_weights)(src)
+    packed, scale, zp = w4.pack_weights(W, symmetric=symmetric, clip_percent=clip)
+    assert np.array_equal(packed, orc.pack_nibbles(q))
+    assert np.array_equal(scale, s) and np.array_equal(zp, z)
+    if symmetric:
+        assert np.all(zp == np.float16(8.0).view(np.uint16))
+
+
+def test_host_packer_variant_rejects():
+    W = np.zeros((2, 256), np.float32)
+    for kw in ({"clip_percent": 49.0}, {"clip_percent": 100.5}, {"clip_percent": float("nan")}):
+        with pytest.raises(w4.W4A8Error):
+            w4.pack_weights(W, **kw)
+    lib = w4.load()
+    f = _fake()
+    assert lib.w4a8_pack_weights_ex(f, 2, 256, 128, 2, 100.0, f, f, f) == EINVAL
+    W[1, 3] = np.inf
+    with pytest.raises(w4.W4A8Error):
+        w4.pack_weights(W, symmetric=True, clip_percent=99.0)

@@ -1,7 +1,11 @@
-"""GPU parity of per-channel smoothing ([p3 §3.4]): channel maxima, the smoothed weight
-packer and the smoothed per-token quantizer are integer/byte work (bit-exact against the
-oracle), and the layer over their outputs is the unchanged GEMM (oracle tolerance
-1e-5 * sum_g |a_scale * w_scale * isum_g| + 1e-6).
+"""GPU parity of the offline transforms around the layer.
+
+Per-channel smoothing ([p3 §3.4]): channel maxima, the smoothed weight packer and the
+smoothed per-token quantizer are integer/byte work (bit-exact against the oracle), and the
+layer over their outputs is the unchanged GEMM (oracle tolerance
+1e-5 * sum_g |a_scale * w_scale * isum_g| + 1e-6).  The host packer variants (symmetric
+codes, percentile clipping) are checked byte for byte on the CPU; here every GEMM loop runs
+over their output against the oracle's product of the same codes.
 """
 from __future__ import annotations
 
@@ -122,3 +126,25 @@ def test_smoothed_decode_layer_full_size(orc):
     err_s = np.linalg.norm(out[:, cols] - exact) / np.linalg.norm(exact)
     err_p = np.linalg.norm(out0[:, cols] - exact) / np.linalg.norm(exact)
     assert err_s < err_p, (err_s, err_p)
+
+
+@pytest.mark.parametrize("symmetric,clip", [(True, 100.0), (False, 99.9), (True, 99.9)])
+@pytest.mark.parametrize("M", [1, 16, 40, 300])
+def test_gemm_over_packer_variants(orc, symmetric, clip, M):
+    """Decode (M <= 16, standard and tile-major), streaming (M <= 64) and tiled loops over
+    symmetric and clipped packs of outlier weights."""
+    w4 = w4mod()
+    N, K = 272, 2048
+    W = synthetic.weights_with_outliers(0, 28672, K, rows=np.arange(N) * 97)
+    x = synthetic.activations_with_outlier_channels(M, M, K)
+    src = orc.clip_rows(W, clip) if clip < 100.0 else W
+    q, sw, zw = (orc.quantize_weights_sym if symmetric else orc.quantize_weights)(src)
+    qr, sr = orc.quantize_act(x)
+    ref, mag = orc.gemm(qr, sr, q, sw, zw)
+    packed, scale, zp = w4.pack_weights(W, symmetric=symmetric, clip_percent=clip)
+    dp, ds, dz = to_dev(packed), to_dev(scale.view(np.int16)), to_dev(zp.view(np.int16))
+    qa, sc = w4.quantize_act(to_dev(x))
+    check_close(to_host(w4.gemm(qa, sc, dp, ds, dz)), ref, mag, f"variant sym={symmetric} clip={clip} M={M}")
+    if M <= 16:
+        out = to_host(w4.gemm_tm(qa, sc, w4.weights_to_tm(dp, ds, dz)))
+        check_close(out, ref, mag, f"tile-major variant sym={symmetric} clip={clip} M={M}")

@@ -16,14 +16,14 @@ import os
 import numpy as np
 
 GROUP = 128
-ABI_VERSION = 4          # W4A8_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5          # W4A8_ABI_VERSION of the header this binding follows
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
 # names exported by include/w4a8.h (checked by the test suite against the header)
 EXPORTS = (
     "w4a8_abi_version", "w4a8_status_str", "w4a8_last_error",
-    "w4a8_pack_weights", "w4a8_pack_weights_device", "w4a8_unpack_weights",
+    "w4a8_pack_weights", "w4a8_pack_weights_ex", "w4a8_pack_weights_device", "w4a8_unpack_weights",
     "w4a8_quantize_act", "w4a8_gemm", "w4a8_gemm_debug_isums", "w4a8_gemm_path",
     "w4a8_tm_bytes", "w4a8_weights_to_tm", "w4a8_gemm_tm",
     "w4a8_channel_absmax", "w4a8_smooth_factors", "w4a8_pack_weights_device_smooth", "w4a8_quantize_act_smooth",
@@ -58,6 +58,7 @@ def load() -> ctypes.CDLL:
         "w4a8_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "w4a8_last_error": (ctypes.c_char_p, []),
         "w4a8_pack_weights": (ctypes.c_int, [p, i64, i64, i32, p, p, p]),
+        "w4a8_pack_weights_ex": (ctypes.c_int, [p, i64, i64, i32, i32, ctypes.c_double, p, p, p]),
         "w4a8_pack_weights_device": (ctypes.c_int, [p, i64, i64, i32, p, p, p, p]),
         "w4a8_unpack_weights": (ctypes.c_int, [p, p, p, i64, i64, i32, p, p]),
         "w4a8_quantize_act": (ctypes.c_int, [p, i64, i64, i64, p, p, p]),
@@ -154,17 +155,22 @@ def _empty(shape, dtype, like):
 
 
 # ----------------------------------------------------------------- packing
-def pack_weights(W: np.ndarray, group: int = GROUP):
-    """Host packer: W float32 [N][K] (numpy) -> (packed u8 [N][K/2], scale u16 [G][N], zp u16 [G][N])."""
+def pack_weights(W: np.ndarray, group: int = GROUP, symmetric: bool = False, clip_percent: float = 100.0):
+    """Host packer: W float32 [N][K] (numpy) -> (packed u8 [N][K/2], scale u16 [G][N], zp u16 [G][N]).
+    symmetric / clip_percent select the w4a8_pack_weights_ex variants (same stored format)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
     G = K // group if group else 0
     packed = np.empty((N, K // 2), np.uint8)
     scale = np.empty((max(G, 1), N), np.uint16)
     zp = np.empty((max(G, 1), N), np.uint16)
-    _call("w4a8_pack_weights", W.ctypes.data_as(ctypes.c_void_p), N, K, group,
-          packed.ctypes.data_as(ctypes.c_void_p), scale.ctypes.data_as(ctypes.c_void_p),
-          zp.ctypes.data_as(ctypes.c_void_p))
+    vp = ctypes.c_void_p
+    if symmetric or clip_percent != 100.0:
+        _call("w4a8_pack_weights_ex", W.ctypes.data_as(vp), N, K, group, 1 if symmetric else 0, float(clip_percent),
+              packed.ctypes.data_as(vp), scale.ctypes.data_as(vp), zp.ctypes.data_as(vp))
+    else:
+        _call("w4a8_pack_weights", W.ctypes.data_as(vp), N, K, group, packed.ctypes.data_as(vp),
+              scale.ctypes.data_as(vp), zp.ctypes.data_as(vp))
     return packed, scale, zp
 
 

@@ -7,6 +7,7 @@
 // fp16; zp = round(-min/scale); q = clamp(round(w/scale) + zp, 0, 15) with the
 // stored fp16 scale; two codes per byte, first code in the low nibble.  fp16
 // conversion uses the compiler's _Float16 (IEEE binary16, round to nearest even).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -72,36 +73,79 @@ float f16_bits_to_f32(uint16_t b) {
 }
 
 // Quantize columns [n0, n1); returns false on non-finite input or fp16 overflow.
-bool pack_columns(const float *W, int64_t N, int64_t K, int64_t n0, int64_t n1, uint8_t *packed, uint16_t *scale,
-                  uint16_t *zp) {
+// One output column n (its K weights w): group-wise asymmetric 4-bit codes, or with
+// sym the symmetric form stored in the same format (code q + 8, zp 8).
+bool pack_row(const float *w0, int64_t n, int64_t N, int64_t K, bool sym, uint8_t *packed, uint16_t *scale,
+              uint16_t *zp) {
     const int64_t G = K / W4A8_GROUP;
     uint8_t codes[W4A8_GROUP];
-    for (int64_t n = n0; n < n1; ++n) {
-        for (int64_t g = 0; g < G; ++g) {
-            const float *w = W + n * K + g * W4A8_GROUP;
-            float lo = 0.0f, hi = 0.0f;
-            for (int i = 0; i < W4A8_GROUP; ++i) {
-                if (!std::isfinite(w[i])) return false;
-                lo = std::fmin(lo, w[i]);
-                hi = std::fmax(hi, w[i]);
-            }
-            uint16_t sh = f32_to_f16_bits((hi - lo) / 15.0f);
-            if ((sh & 0x7C00u) == 0x7C00u) return false;
-            float s = f16_bits_to_f32(sh);
-            if (s == 0.0f) {
-                sh = 0x3C00u;
-                s = 1.0f;
-            }
-            const int z = (int)std::fmin(std::fmax(std::nearbyint(-lo / s), 0.0f), 15.0f);
-            for (int i = 0; i < W4A8_GROUP; ++i) {
-                const int v = (int)std::nearbyint(w[i] / s) + z;
-                codes[i] = (uint8_t)(v < 0 ? 0 : (v > 15 ? 15 : v));
-            }
-            uint8_t *dst = packed + n * (K / 2) + g * (W4A8_GROUP / 2);
-            for (int j = 0; j < W4A8_GROUP / 2; ++j) dst[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
-            scale[g * N + n] = sh;
-            zp[g * N + n] = f32_to_f16_bits((float)z);
+    for (int64_t g = 0; g < G; ++g) {
+        const float *w = w0 + g * W4A8_GROUP;
+        float lo = 0.0f, hi = 0.0f;
+        for (int i = 0; i < W4A8_GROUP; ++i) {
+            if (!std::isfinite(w[i])) return false;
+            lo = std::fmin(lo, w[i]);
+            hi = std::fmax(hi, w[i]);
         }
+        // asymmetric: (max - min) / (2^4 - 1); symmetric: max|w| / (2^3 - 1)
+        uint16_t sh = f32_to_f16_bits(sym ? std::fmax(-lo, hi) / 7.0f : (hi - lo) / 15.0f);
+        if ((sh & 0x7C00u) == 0x7C00u) return false;
+        float s = f16_bits_to_f32(sh);
+        if (s == 0.0f) {
+            sh = 0x3C00u;
+            s = 1.0f;
+        }
+        const int z = sym ? 8 : (int)std::fmin(std::fmax(std::nearbyint(-lo / s), 0.0f), 15.0f);
+        for (int i = 0; i < W4A8_GROUP; ++i) {
+            int v;
+            if (sym) v = (int)std::fmin(std::fmax(std::nearbyint(w[i] / s), -7.0f), 7.0f) + 8;
+            else v = (int)std::nearbyint(w[i] / s) + z;
+            codes[i] = (uint8_t)(v < 0 ? 0 : (v > 15 ? 15 : v));
+        }
+        uint8_t *dst = packed + n * (K / 2) + g * (W4A8_GROUP / 2);
+        for (int j = 0; j < W4A8_GROUP / 2; ++j) dst[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        scale[g * N + n] = sh;
+        zp[g * N + n] = f32_to_f16_bits((float)z);
+    }
+    return true;
+}
+
+// pct-th percentile of v (linear interpolation between order statistics, position
+// (K - 1) * pct / 100, in double); v is reordered.
+double row_percentile(std::vector<float> &v, double pct) {
+    const int64_t n = (int64_t)v.size();
+    const double h = (double)(n - 1) * pct / 100.0;
+    const int64_t i = (int64_t)std::floor(h);
+    std::nth_element(v.begin(), v.begin() + i, v.end());
+    double r = (double)v[(size_t)i];
+    if (i + 1 < n) {
+        const float next = *std::min_element(v.begin() + i + 1, v.end());
+        r += (h - (double)i) * ((double)next - (double)v[(size_t)i]);
+    }
+    return r;
+}
+
+// Columns [n0, n1).  clip < 100: each column's weights are first clamped to its own
+// [100 - clip, clip] percentiles (rounded to fp32).
+bool pack_columns(const float *W, int64_t N, int64_t K, int64_t n0, int64_t n1, bool sym, double clip,
+                  uint8_t *packed, uint16_t *scale, uint16_t *zp) {
+    std::vector<float> row, work;
+    if (clip < 100.0) {
+        row.resize((size_t)K);
+        work.resize((size_t)K);
+    }
+    for (int64_t n = n0; n < n1; ++n) {
+        const float *w = W + n * K;
+        if (clip < 100.0) {
+            for (int64_t k = 0; k < K; ++k)
+                if (!std::isfinite(w[k])) return false;
+            work.assign(w, w + K);
+            const float lo = (float)row_percentile(work, 100.0 - clip);
+            const float hi = (float)row_percentile(work, clip);
+            for (int64_t k = 0; k < K; ++k) row[(size_t)k] = w[k] < lo ? lo : (w[k] > hi ? hi : w[k]);
+            w = row.data();
+        }
+        if (!pack_row(w, n, N, K, sym, packed, scale, zp)) return false;
     }
     return true;
 }
@@ -127,10 +171,20 @@ const char *w4a8_last_error(void) { return g_err; }
 
 w4a8_status w4a8_pack_weights(const float *W, int64_t N, int64_t K, int32_t group, uint8_t *packed, uint16_t *scale,
                               uint16_t *zp) {
+    return w4a8_pack_weights_ex(W, N, K, group, W4A8_PACK_ASYMMETRIC, 100.0, packed, scale, zp);
+}
+
+w4a8_status w4a8_pack_weights_ex(const float *W, int64_t N, int64_t K, int32_t group, int32_t mode,
+                                 double clip_percent, uint8_t *packed, uint16_t *scale, uint16_t *zp) {
     clear_error();
     W4A8_REQUIRE(W && packed && scale && zp, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
     if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(mode == W4A8_PACK_ASYMMETRIC || mode == W4A8_PACK_SYMMETRIC, W4A8_EINVAL, "mode=%d is not a packer mode",
+                 (int)mode);
+    W4A8_REQUIRE(clip_percent >= 50.0 && clip_percent <= 100.0, W4A8_EINVAL, "clip_percent=%g must lie in [50, 100]",
+                 clip_percent);
+    const bool sym = mode == W4A8_PACK_SYMMETRIC;
     unsigned hw = std::thread::hardware_concurrency();
     int64_t nthreads = hw ? hw : 1;
     if (nthreads > N) nthreads = N;
@@ -141,7 +195,7 @@ w4a8_status w4a8_pack_weights(const float *W, int64_t N, int64_t K, int32_t grou
     for (int64_t t = 0; t < nthreads; ++t) {
         const int64_t n0 = t * per, n1 = std::min(N, n0 + per);
         if (n0 >= n1) continue;
-        pool.emplace_back([=, &ok] { ok[t] = pack_columns(W, N, K, n0, n1, packed, scale, zp); });
+        pool.emplace_back([=, &ok] { ok[t] = pack_columns(W, N, K, n0, n1, sym, clip_percent, packed, scale, zp); });
     }
     for (auto &th : pool) th.join();
     for (char c : ok)
