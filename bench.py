@@ -197,6 +197,8 @@ def parse():
     p.add_argument("--cmd", action="append", default=[], help="command text recorded in a summary")
     p.add_argument("--only", choices=["prefill"],
                    help="run one secondary workload alone and print its figures (for counter runs)")
+    p.add_argument("--group", type=int, default=GROUP, choices=(64, 128, 256),
+                   help="group size of the weights for --only prefill")
     p.add_argument("--reps", type=int, default=10, help="timed launches for --only")
     return p.parse_args()
 
@@ -301,19 +303,25 @@ def cpu_baseline(synthetic):
                       f"{t_total:.1f} s; weight quantization excluded (offline)"}
 
 
-def prefill(torch, w4, synthetic, reps=10):
+def prefill(torch, w4, synthetic, reps=10, group=GROUP):
     """The prefill-shaped dense GEMM (M=4096, K=N=8192): quantize once, then `reps`
-    back-to-back prepared launches timed with one event pair on the launch stream."""
+    back-to-back prepared launches timed with one event pair on the launch stream.
+    Group sizes other than 128 are packed by the host packer (the device packer takes 128)."""
     dev = torch.device("cuda:0")
     M, N, K = 4096, 8192, 8192
     W = torch.empty((N, K), dtype=torch.float32, device=dev)
     synthetic.fill_weights_device(W, 0, synthetic.TAG_W, 0, K, 0, "offset")
-    layer = w4.pack_weights_device(W)
+    if group == GROUP:
+        layer = w4.pack_weights_device(W)
+    else:
+        packed, scale, zp = w4.pack_weights(W.cpu().numpy(), group=group)
+        layer = (torch.from_numpy(packed).to(dev), torch.from_numpy(scale.view(np.int16)).to(dev),
+                 torch.from_numpy(zp.view(np.int16)).to(dev))
     del W
     x = torch.from_numpy(synthetic.activations(0, M, K)).to(dev)
     qa, sc = w4.quantize_act(x)
     out_buf = torch.empty((M, N), dtype=torch.float32, device=dev)
-    launch = w4.prepare_gemm(qa, sc, *layer, out_buf)
+    launch = w4.prepare_gemm(qa, sc, *layer, out_buf, group=group)
     for _ in range(40):  # about 20 ms of warm-up
         launch()
     stream = torch.cuda.current_stream()
@@ -387,6 +395,8 @@ def secondary(torch, w4, synthetic):
     """Prefill (M=4096, K=N=8192) TOPS, MoE layer times and the smoothing figures; context."""
     dev = torch.device("cuda:0")
     out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
+           "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
+           "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
            "quant_variants_K8192_N4096_M16": smoothing(torch, w4, synthetic)}
     from tests.gpu_common import device_experts
     # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
@@ -493,7 +503,8 @@ def main():
 
     w4.load()
     if args.only == "prefill":
-        print(json.dumps({"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic, args.reps)}), flush=True)
+        print(json.dumps({f"prefill_M4096_K8192_N8192_group{args.group}": prefill(torch, w4, synthetic, args.reps,
+                                                                                   args.group)}), flush=True)
         return
     layers, tms, xs = decode_setup(torch, w4, synthetic, args.copies)
     ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m = run_decode(

@@ -223,6 +223,37 @@ def _random_layer(rng, M, N, K):
     return W, x
 
 
+def pin_group_sizes_64_256(orc):
+    """[p2 §4.3] group sizes 64 and 256: the lattice closed form holds per group of that
+    size ([K/group][N] layout), each group's int32 sum is the integer dot product over
+    exactly its k range (brute force), and the dequantize-then-matmul route agrees."""
+    rng = np.random.default_rng(34)
+    for group in (64, 256):
+        N, G = 3, 3
+        steps = rng.choice(np.float32([0.25, 0.5, 2.0 ** -7, 0.125, 1.5]), (N, G))
+        zps = rng.integers(0, 16, (N, G))
+        i = np.arange(group)
+        W = np.concatenate([((i % 16) - zps[:, g:g + 1]) * steps[:, g:g + 1] for g in range(G)], 1).astype(np.float32)
+        q, s, z = orc.quantize_weights(W, group)
+        assert s.shape == (G, N)
+        assert np.array_equal(s, steps.T.astype(np.float16).view(np.uint16))
+        assert np.array_equal(z, zps.T.astype(np.float16).view(np.uint16))
+        assert np.array_equal(q, np.tile(i % 16, (N, G)).astype(np.uint8))
+        M, K = 2, G * group
+        qa = rng.integers(-127, 128, (M, K)).astype(np.int8)
+        isums = orc.group_isums(qa, q, z, group)
+        zf = np.float16(z.view(np.float16)).astype(np.int64)
+        for g in range(G):
+            ks = slice(g * group, (g + 1) * group)
+            want = qa[:, ks].astype(np.int64) @ (q[:, ks].astype(np.int64) - zf[g][:, None]).T
+            assert np.array_equal(isums[g], want), group
+        a_s = np.float32([0.01, 0.003])
+        out, _ = orc.gemm(qa, a_s, q, s, z, group)
+        deq = orc.dequantize_weights(q, s, z, group)
+        ref = (qa.astype(np.float64) * a_s.astype(np.float64)[:, None]) @ deq.T
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
 def pin_integer_special_case(orc):
     """All scales 1, all zero points 0, a_scale 1: the layer is a plain integer matmul."""
     rng = np.random.default_rng(4)

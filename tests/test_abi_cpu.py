@@ -47,9 +47,14 @@ def test_validation_rejects_before_launch():
     f = _fake()
     # null pointers
     assert lib.w4a8_gemm(None, f, 4, 256, f, f, f, 128, 128, f, None) == EINVAL
-    # group size other than 128: unsupported, never a silent fallback
-    assert lib.w4a8_gemm(f, f, 4, 256, f, f, f, 128, 64, f, None) == EUNSUPPORTED
+    # group sizes other than 64, 128, 256: unsupported, never a silent fallback
+    assert lib.w4a8_gemm(f, f, 4, 256, f, f, f, 128, 32, f, None) == EUNSUPPORTED
     assert b"group" in lib.w4a8_last_error()
+    # 64 and 256 run on the tiled loop only; the expert loops and the device packer take 128
+    assert lib.w4a8_gemm_path(f, f, 4, 256, f, f, f, 128, 64, 1, f, None) == EUNSUPPORTED
+    assert lib.w4a8_gemm_path(f, f, 4, 384, f, f, f, 128, 256, 2, f, None) == EINVAL   # K % 256
+    assert lib.w4a8_gemm_path(f, f, 0, 512, f, f, f, 128, 256, 0, f, None) == 0        # M == 0: no launch
+    assert lib.w4a8_pack_weights_device(f, 16, 256, 64, f, f, f, None) == EUNSUPPORTED
     # K not a multiple of 128
     assert lib.w4a8_gemm(f, f, 4, 200, f, f, f, 128, 128, f, None) == EINVAL
     # N not a multiple of 16
@@ -147,8 +152,11 @@ def test_host_packer_rejects_bad_weights():
     with pytest.raises(w4.W4A8Error):
         w4.pack_weights(W)
     with pytest.raises(w4.W4A8Error) as e:
-        w4.pack_weights(np.zeros((2, 256), np.float32), group=64)
+        w4.pack_weights(np.zeros((2, 256), np.float32), group=32)
     assert e.value.status == EUNSUPPORTED
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.pack_weights(np.zeros((2, 384), np.float32), group=256)
+    assert e.value.status == EINVAL
 
 
 def _packer_matches_oracle(orc, W):
@@ -251,3 +259,20 @@ def test_host_packer_variant_rejects():
     W[1, 3] = np.inf
     with pytest.raises(w4.W4A8Error):
         w4.pack_weights(W, symmetric=True, clip_percent=99.0)
+
+
+@pytest.mark.parametrize("group", [64, 256])
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_host_packer_group_sizes_bit_exact_vs_oracle(orc, group, symmetric):
+    """Group sizes 64 and 256 ([p2 §4.3] weighs 64/128/256): bytes, scales and zero points
+    equal the oracle's for the same group size; the unpacker inverts them."""
+    W = synthetic.weights_with_offset(0, 8192, 1536, rows=np.arange(0, 8192, 331))
+    W[3, :group] = 0.0
+    q, s, z = (orc.quantize_weights_sym if symmetric else orc.quantize_weights)(W, group)
+    packed, scale, zp = w4.pack_weights(W, group=group, symmetric=symmetric)
+    assert scale.shape == (1536 // group, W.shape[0])
+    assert np.array_equal(packed, orc.pack_nibbles(q))
+    assert np.array_equal(scale, s) and np.array_equal(zp, z)
+    q2, w_hat = w4.unpack_weights(packed, scale, zp, group=group)
+    assert np.array_equal(q2, q)
+    assert np.allclose(w_hat, orc.dequantize_weights(q, s, z, group), rtol=0, atol=1e-7)

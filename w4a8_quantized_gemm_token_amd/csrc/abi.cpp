@@ -59,6 +59,15 @@ w4a8_status check_group(int32_t group, int64_t K) {
     return W4A8_OK;
 }
 
+// Group sizes of the host packer and the tiled GEMM loop: 64, 128 or 256 along K.
+w4a8_status check_group_any(int32_t group, int64_t K) {
+    W4A8_REQUIRE(group == 64 || group == 128 || group == 256, W4A8_EUNSUPPORTED,
+                 "group size %d is not supported (64, 128 or 256)", (int)group);
+    W4A8_REQUIRE(K > 0 && K % 128 == 0 && K % group == 0, W4A8_EINVAL,
+                 "K=%lld must be a positive multiple of 128 and of the group size", (long long)K);
+    return W4A8_OK;
+}
+
 uint16_t f32_to_f16_bits(float f) {
     const _Float16 h = (_Float16)f;
     uint16_t b;
@@ -75,14 +84,14 @@ float f16_bits_to_f32(uint16_t b) {
 // Quantize columns [n0, n1); returns false on non-finite input or fp16 overflow.
 // One output column n (its K weights w): group-wise asymmetric 4-bit codes, or with
 // sym the symmetric form stored in the same format (code q + 8, zp 8).
-bool pack_row(const float *w0, int64_t n, int64_t N, int64_t K, bool sym, uint8_t *packed, uint16_t *scale,
-              uint16_t *zp) {
-    const int64_t G = K / W4A8_GROUP;
-    uint8_t codes[W4A8_GROUP];
+bool pack_row(const float *w0, int64_t n, int64_t N, int64_t K, int64_t group, bool sym, uint8_t *packed,
+              uint16_t *scale, uint16_t *zp) {
+    const int64_t G = K / group;
+    uint8_t codes[256];
     for (int64_t g = 0; g < G; ++g) {
-        const float *w = w0 + g * W4A8_GROUP;
+        const float *w = w0 + g * group;
         float lo = 0.0f, hi = 0.0f;
-        for (int i = 0; i < W4A8_GROUP; ++i) {
+        for (int i = 0; i < group; ++i) {
             if (!std::isfinite(w[i])) return false;
             lo = std::fmin(lo, w[i]);
             hi = std::fmax(hi, w[i]);
@@ -96,14 +105,14 @@ bool pack_row(const float *w0, int64_t n, int64_t N, int64_t K, bool sym, uint8_
             s = 1.0f;
         }
         const int z = sym ? 8 : (int)std::fmin(std::fmax(std::nearbyint(-lo / s), 0.0f), 15.0f);
-        for (int i = 0; i < W4A8_GROUP; ++i) {
+        for (int i = 0; i < group; ++i) {
             int v;
             if (sym) v = (int)std::fmin(std::fmax(std::nearbyint(w[i] / s), -7.0f), 7.0f) + 8;
             else v = (int)std::nearbyint(w[i] / s) + z;
             codes[i] = (uint8_t)(v < 0 ? 0 : (v > 15 ? 15 : v));
         }
-        uint8_t *dst = packed + n * (K / 2) + g * (W4A8_GROUP / 2);
-        for (int j = 0; j < W4A8_GROUP / 2; ++j) dst[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        uint8_t *dst = packed + n * (K / 2) + g * (group / 2);
+        for (int j = 0; j < group / 2; ++j) dst[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
         scale[g * N + n] = sh;
         zp[g * N + n] = f32_to_f16_bits((float)z);
     }
@@ -127,7 +136,7 @@ double row_percentile(std::vector<float> &v, double pct) {
 
 // Columns [n0, n1).  clip < 100: each column's weights are first clamped to its own
 // [100 - clip, clip] percentiles (rounded to fp32).
-bool pack_columns(const float *W, int64_t N, int64_t K, int64_t n0, int64_t n1, bool sym, double clip,
+bool pack_columns(const float *W, int64_t N, int64_t K, int64_t group, int64_t n0, int64_t n1, bool sym, double clip,
                   uint8_t *packed, uint16_t *scale, uint16_t *zp) {
     std::vector<float> row, work;
     if (clip < 100.0) {
@@ -145,7 +154,7 @@ bool pack_columns(const float *W, int64_t N, int64_t K, int64_t n0, int64_t n1, 
             for (int64_t k = 0; k < K; ++k) row[(size_t)k] = w[k] < lo ? lo : (w[k] > hi ? hi : w[k]);
             w = row.data();
         }
-        if (!pack_row(w, n, N, K, sym, packed, scale, zp)) return false;
+        if (!pack_row(w, n, N, K, group, sym, packed, scale, zp)) return false;
     }
     return true;
 }
@@ -179,7 +188,7 @@ w4a8_status w4a8_pack_weights_ex(const float *W, int64_t N, int64_t K, int32_t g
     clear_error();
     W4A8_REQUIRE(W && packed && scale && zp, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
-    if (w4a8_status st = check_group(group, K)) return st;
+    if (w4a8_status st = check_group_any(group, K)) return st;
     W4A8_REQUIRE(mode == W4A8_PACK_ASYMMETRIC || mode == W4A8_PACK_SYMMETRIC, W4A8_EINVAL, "mode=%d is not a packer mode",
                  (int)mode);
     W4A8_REQUIRE(clip_percent >= 50.0 && clip_percent <= 100.0, W4A8_EINVAL, "clip_percent=%g must lie in [50, 100]",
@@ -195,7 +204,8 @@ w4a8_status w4a8_pack_weights_ex(const float *W, int64_t N, int64_t K, int32_t g
     for (int64_t t = 0; t < nthreads; ++t) {
         const int64_t n0 = t * per, n1 = std::min(N, n0 + per);
         if (n0 >= n1) continue;
-        pool.emplace_back([=, &ok] { ok[t] = pack_columns(W, N, K, n0, n1, sym, clip_percent, packed, scale, zp); });
+        pool.emplace_back(
+            [=, &ok] { ok[t] = pack_columns(W, N, K, group, n0, n1, sym, clip_percent, packed, scale, zp); });
     }
     for (auto &th : pool) th.join();
     for (char c : ok)
@@ -208,14 +218,14 @@ w4a8_status w4a8_unpack_weights(const uint8_t *packed, const uint16_t *scale, co
     clear_error();
     W4A8_REQUIRE(packed && scale && zp, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
-    if (w4a8_status st = check_group(group, K)) return st;
+    if (w4a8_status st = check_group_any(group, K)) return st;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
             const uint8_t b = packed[n * (K / 2) + k / 2];
             const uint8_t q = (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
             if (q_out) q_out[n * K + k] = q;
             if (w_hat) {
-                const int64_t g = k / W4A8_GROUP;
+                const int64_t g = k / group;
                 const float s = f16_bits_to_f32(scale[g * N + n]);
                 const float z = f16_bits_to_f32(zp[g * N + n]);
                 w_hat[n * K + k] = ((float)q - z) * s;
@@ -307,7 +317,7 @@ static w4a8_status check_gemm(const int8_t *qa, int64_t M, int64_t K, const uint
     (void)scale;
     W4A8_REQUIRE(M >= 0, W4A8_EINVAL, "M=%lld must be >= 0", (long long)M);
     W4A8_REQUIRE(N > 0 && N % 16 == 0, W4A8_EINVAL, "N=%lld must be a positive multiple of 16", (long long)N);
-    if (w4a8_status st = check_group(group, K)) return st;
+    if (w4a8_status st = check_group_any(group, K)) return st;
     W4A8_REQUIRE(aligned16(qa) && aligned16(packed) && aligned16(out), W4A8_EINVAL,
                  "qa, packed and out must be 16-byte aligned");
     return W4A8_OK;
@@ -317,6 +327,16 @@ static w4a8_status gemm_common(const int8_t *qa, const float *a_scale, int64_t M
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group, int32_t path,
                                float *out, int32_t *isums, hipStream_t stream) {
     W4A8_REQUIRE(path >= 0 && path <= 4, W4A8_EINVAL, "path=%d must be in [0, 4]", (int)path);
+    if (group != W4A8_GROUP) {
+        // group sizes 64 and 256 run on the tiled loop, for any M
+        if (path == 0) path = 2;
+        W4A8_REQUIRE(path >= 2, W4A8_EUNSUPPORTED, "group size %d runs on the tiled loop only (path 0, 2, 3 or 4)",
+                     (int)group);
+        if (M == 0) return W4A8_OK;
+        return hip_status(launch_gemm_tiled_group(qa, a_scale, M, K, packed, scale, zp, N, group, path, out, isums,
+                                                  stream),
+                          "gemm launch");
+    }
     if (path == 0) path = (M <= kStreamMaxM) ? 1 : 2;
     W4A8_REQUIRE(!(path == 1 && M > kStreamMaxM), W4A8_EINVAL, "the streaming loop takes M <= %lld",
                  (long long)kStreamMaxM);
@@ -402,6 +422,7 @@ w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_
                                   int64_t max_slots, float *out, hipStream_t stream) {
     clear_error();
     if (w4a8_status st = check_gemm(qa, R, K, packed, scale, zp, N, group, out)) return st;
+    if (w4a8_status st = check_group(group, K)) return st;  // the expert loops take 128 only
     W4A8_REQUIRE(a_scale && scale && expert_offsets, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
     W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");

@@ -798,6 +798,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(const int8_
 // Lane l of a 32x32 tile feeds A row (l&31) / B column (l&31) with k bytes
 // ks*32 + (l>>5)*16 + [0,16), and holds accumulator rows 8*(r>>2) + 4*(l>>5) + (r&3),
 // r = 0..15, of column l&31.
+// Group size GS ([p2 §4.3] and the tuning notes of [p1]/[p2] weigh 64, 128 and 256):
+// the LDS stage stays 128 k.  GS = 256 keeps the int32 sums of two stages in the same
+// accumulators and runs the fp32 epilogue once per two stages (half the epilogue work);
+// GS = 64 runs the MFMAs of each stage as two k halves with an epilogue after each
+// (twice the epilogue work), and each thread unpacks its codes with the zero point of
+// the 64-group they lie in.
 constexpr int kLdsStride = G128 + 16;  // padded row: 144 bytes
 
 struct TileRows {
@@ -817,7 +823,7 @@ struct TileShape {
     static_assert(A_BYTES % 16 == 0 && B_PACKED % 16 == 0, "loader granularity");
 };
 
-template <int WM, int WN, bool ISUMS>
+template <int WM, int WN, bool ISUMS, int GS = G128>
 __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restrict__ qa,
                                            const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
                                            int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
@@ -826,10 +832,13 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
                                            int32_t *__restrict__ isums, int64_t M_isums) {
     using S = TileShape<WM, WN>;
     constexpr int NA = S::A_BYTES / 16, NB = S::B_PACKED / 16;
+    static_assert(GS == 64 || GS == 128 || GS == 256, "group size");
+    static_assert(GS != 64 || 2 * S::B_PACKED <= 64, "a thread's codes must lie in one 64-group");
+    constexpr int NSUB = GS == 64 ? 2 : 1;  // groups per 128-k stage
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t G = K / G128;
+    const int64_t G = K / G128;  // 128-k stages
 
     // ---- loader state
     const int arow_l = tid / S::A_TPR, apart = tid % S::A_TPR;
@@ -862,17 +871,29 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
     // zero point, the two scales of this lane's columns)
     struct Slot {
         v4u ra[NA], rb[NB];
-        uint16_t rz, rs[2];
+        uint16_t rz, rs[2][NSUB];
     };
     Slot sa, sb;
+    // the 64-group (of the two in a stage) that this thread's packed bytes fall in
+    const int zsub = GS == 64 ? (bpart * 2 * S::B_PACKED) / 64 : 0;
     auto gload = [&](Slot &sl, int64_t g) {
 #pragma unroll
         for (int i = 0; i < NA; ++i) sl.ra[i] = aglob[g * (G128 / 16) + i];
 #pragma unroll
         for (int i = 0; i < NB; ++i) sl.rb[i] = __builtin_nontemporal_load(bglob + g * (G128 / 2 / 16) + i);
-        sl.rz = zglob[g * N];
-        sl.rs[0] = sglob[0][g * N];
-        sl.rs[1] = sglob[1][g * N];
+        if constexpr (GS == 64) {
+            sl.rz = zglob[(2 * g + zsub) * N];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                sl.rs[j][0] = sglob[j][2 * g * N];
+                sl.rs[j][1] = sglob[j][(2 * g + 1) * N];
+            }
+        } else {
+            const int64_t gg = GS == 256 ? g >> 1 : g;
+            sl.rz = zglob[gg * N];
+            sl.rs[0][0] = sglob[0][gg * N];
+            sl.rs[1][0] = sglob[1][gg * N];
+        }
     };
     auto lstore = [&](const Slot &sl, int buf) {
         uint8_t *A = lds + buf * S::LDS_STAGE;
@@ -901,18 +922,22 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // the 16 MFMAs of one group: 4 independent accumulator chains, k-step outer
-    auto mfma_group = [&](int buf, v16i (&d)[2][2]) {
+    // the MFMAs of k steps [KS0, KS1) of one stage (4 steps = 16 MFMAs): 4 independent
+    // accumulator chains, k-step outer; RESET starts the sums at zero
+    auto mfma_group = [&](auto ks0c, auto ks1c, auto resetc, int buf, v16i (&d)[2][2]) {
+        constexpr int KS0 = decltype(ks0c)::value, KS1 = decltype(ks1c)::value;
         const uint8_t *A = lds + buf * S::LDS_STAGE;
         const uint8_t *B = A + S::LDS_A;
+        if constexpr (decltype(resetc)::value) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) d[i][j][r] = 0;
+                    for (int r = 0; r < 16; ++r) d[i][j][r] = 0;
+        }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = KS0; ks < KS1; ++ks) {
             v4i af[2], bf[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -951,39 +976,62 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
     // of compute to arrive.  Unrolled by two so the slots stay in registers; indices
     // past the end re-load the last group, whose copies are never consumed.
     v16i d[2][2];
-    float sc[2];
+    float sc[NSUB][2];  // this lane's two columns' scales, per group of the stage
+    auto load_scales = [&](const Slot &sl) {
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) {
+            sc[h][0] = half_bits_to_float(sl.rs[0][h]);
+            sc[h][1] = half_bits_to_float(sl.rs[1][h]);
+        }
+    };
     gload(sa, 0);
     __builtin_amdgcn_sched_barrier(0);
     gload(sb, G > 1 ? 1 : 0);
     __builtin_amdgcn_sched_barrier(0);
     lstore(sa, 0);
-    sc[0] = half_bits_to_float(sa.rs[0]);
-    sc[1] = half_bits_to_float(sa.rs[1]);
+    load_scales(sa);
     __syncthreads();
-    auto body = [&](int64_t g, Slot &fill, const Slot &next) {
+    using I0 = std::integral_constant<int, 0>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using T = std::true_type;
+    // PAR: parity of the stage index (known at compile time: the loop is unrolled by two)
+    auto body = [&](auto parc, int64_t g, Slot &fill, const Slot &next) {
+        constexpr int PAR = decltype(parc)::value;
         // compiler fences keep the prefetch where it is written (IR passes would
         // otherwise merge it into the other half of the unrolled loop)
         __asm__ volatile("" ::: "memory");
         gload(fill, g + 2 < G ? g + 2 : G - 1);
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group((int)(g & 1), d);
-        epilogue(g, d, sc);
+        if constexpr (GS == 128) {
+            mfma_group(I0{}, I4{}, T{}, PAR, d);
+            epilogue(g, d, sc[0]);
+        } else if constexpr (GS == 256) {
+            // the two stages of a group add into the same sums; one epilogue per group
+            mfma_group(I0{}, I4{}, std::integral_constant<bool, PAR == 0>{}, PAR, d);
+            if constexpr (PAR == 1) epilogue(g >> 1, d, sc[0]);
+        } else {
+            mfma_group(I0{}, I2{}, T{}, PAR, d);
+            epilogue(2 * g, d, sc[0]);
+            mfma_group(I2{}, I4{}, T{}, PAR, d);
+            epilogue(2 * g + 1, d, sc[1]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        lstore(next, (int)((g + 1) & 1));
-        sc[0] = half_bits_to_float(next.rs[0]);
-        sc[1] = half_bits_to_float(next.rs[1]);
+        lstore(next, PAR ^ 1);
+        load_scales(next);
         // keep the scales as fp32 values: folding the fp16->fp32 conversion into the
         // epilogue (v_fma_mix_f32) measured slower than converting once per group
-        __asm__ volatile("" : "+v"(sc[0]), "+v"(sc[1]));
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) __asm__ volatile("" : "+v"(sc[h][0]), "+v"(sc[h][1]));
         __syncthreads();
     };
     int64_t g = 0;
     for (; g + 1 < G; g += 2) {
-        body(g, sa, sb);                 // group g from LDS; group g+1 (slot b) -> LDS
-        body(g + 1, sb, sa);             // group g+1 from LDS; group g+2 (slot a) -> LDS
+        body(I0{}, g, sa, sb);                                   // stage g from LDS; g+1 (slot b) -> LDS
+        body(std::integral_constant<int, 1>{}, g + 1, sb, sa);   // stage g+1 from LDS; g+2 (slot a) -> LDS
     }
-    if (g < G) body(g, sa, sb);          // odd G: the last group
+    if (g < G) body(I0{}, g, sa, sb);   // odd stage count (GS = 64 or 128): the last stage
 
     if (!ISUMS) {
 #pragma unroll
@@ -1002,7 +1050,7 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
     }
 }
 
-template <int WM, int WN, bool ISUMS>
+template <int WM, int WN, bool ISUMS, int GS>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *__restrict__ qa,
                                                                   const float *__restrict__ a_scale, int64_t M,
                                                                   int64_t K, const uint8_t *__restrict__ packed,
@@ -1017,8 +1065,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *
     panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
     const int64_t m0 = tm * S::BM;
     const int rows = (int)((M - m0) < S::BM ? (M - m0) : S::BM);
-    tile2_unit<WM, WN, ISUMS>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * S::BN,
-                              out, N, isums, M);
+    tile2_unit<WM, WN, ISUMS, GS>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N,
+                                  tn * S::BN, out, N, isums, M);
 }
 
 // ------------------------------------------------------------------ expert-grouped forms
@@ -1521,7 +1569,7 @@ hipError_t launch_stream2(int mt, int u, int split, const int8_t *qa, const floa
     return launch_stream2_s<4, 1>(split, qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int GS = G128>
 hipError_t launch_tiled(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                         const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
                         hipStream_t stream) {
@@ -1530,16 +1578,16 @@ hipError_t launch_tiled(const int8_t *qa, const float *a_scale, int64_t M, int64
     const size_t lds = 2 * S::LDS_STAGE;
     const dim3 grid((uint32_t)tiles), block(S::THREADS);
     if (isums) {
-        if (hipFuncSetAttribute((const void *)gemm_tiled_kernel<WM, WN, true>,
+        if (hipFuncSetAttribute((const void *)gemm_tiled_kernel<WM, WN, true, GS>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipGetLastError();
-        hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, true>), grid, block, lds, stream, qa, a_scale, M, K, packed,
+        hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, true, GS>), grid, block, lds, stream, qa, a_scale, M, K, packed,
                            scale, zp, N, out, isums);
     } else {
-        if (hipFuncSetAttribute((const void *)gemm_tiled_kernel<WM, WN, false>,
+        if (hipFuncSetAttribute((const void *)gemm_tiled_kernel<WM, WN, false, GS>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipGetLastError();
-        hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, false>), grid, block, lds, stream, qa, a_scale, M, K, packed,
+        hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, false, GS>), grid, block, lds, stream, qa, a_scale, M, K, packed,
                            scale, zp, N, out, isums);
     }
     return hipGetLastError();
@@ -1667,6 +1715,21 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
         return launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                                   const uint16_t *scale, const uint16_t *zp, int64_t N, int group, int path, float *out,
+                                   int32_t *isums, hipStream_t stream) {
+    if (!scale) scale = zp;  // debug entry: see launch_gemm
+    const bool wide = path == 4 || (path == 2 && M > 128);
+    if (group == 64)
+        return wide ? launch_tiled<4, 2, 64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
+                    : launch_tiled<2, 2, 64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+    if (group == 256)
+        return wide ? launch_tiled<4, 2, 256>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
+                    : launch_tiled<2, 2, 256>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+    return wide ? launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
+                : launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
 }
 
 int64_t tm_bytes(int64_t N, int64_t K) { return (N / 16) * (K / G128 / 2) * kTmBlock; }

@@ -35,6 +35,12 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
                        const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
                        int64_t N, int path, float *out, int32_t *isums, hipStream_t stream);
 
+// The tiled loop for group size 64, 128 or 256 (K a multiple of 128 and of the group);
+// path 2 or 3 (the 128-row tile unless path 2 has M > 128) or 4 (256-row tiles).
+hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                                   const uint16_t *scale, const uint16_t *zp, int64_t N, int group, int path, float *out,
+                                   int32_t *isums, hipStream_t stream);
+
 // max_per_expert: a bound on any one expert's slot count known to the caller (the
 // MoE layer knows no expert gets more than T); loops for larger experts are not
 // launched.  max_slots when nothing better is known.
