@@ -85,8 +85,11 @@ const char *w4a8_last_error(void);
  * scale/zero point per group, exactly as stated at the top of this file
  * ([p2 §2.1, §2.2]).  All pointers are host memory owned by the caller.
  * A group whose scale rounds to 0 in fp16 stores scale 1.0 and zp 0.
+ * group is 128, or 64 or 256 ([p2 §4.3] weighs the three) for weights that the
+ * tiled GEMM loop will take (scale/zp then [K/group][N]).
  * Errors: W4A8_EINVAL for null pointers, N <= 0, K <= 0, K % 128 != 0,
- * non-finite weights, or a group scale above the largest finite fp16. */
+ * K % group != 0, non-finite weights, or a group scale above the largest finite
+ * fp16; W4A8_EUNSUPPORTED for another group size. */
 w4a8_status w4a8_pack_weights(const float *W, int64_t N, int64_t K, int32_t group,
                               uint8_t *packed, uint16_t *scale, uint16_t *zp);
 
@@ -185,8 +188,12 @@ w4a8_status w4a8_quantize_act_smooth(const float *x, int64_t M, int64_t K, int64
  * are widened to INT8 inside the kernel, never in memory).  Small M takes an
  * HBM-streaming path, large M an LDS-tiled MFMA path; both give the same
  * per-group int32 sums.  The fp32 epilogue adds groups in increasing g.
- * Errors: W4A8_EINVAL (null, M < 0, N <= 0, K <= 0, K % 128, N % 16 != 0,
- * misalignment), W4A8_EUNSUPPORTED (group != 128).  M == 0 is a no-op. */
+ * Group sizes 64 and 256 (weights from the host packer) run on the tiled loop
+ * for every M: 256 keeps one int32 sum over its two 128-k stages, 64 takes two
+ * sums per stage.
+ * Errors: W4A8_EINVAL (null, M < 0, N <= 0, K <= 0, K % 128, K % group,
+ * N % 16 != 0, misalignment), W4A8_EUNSUPPORTED (group not 64, 128 or 256; 64
+ * or 256 with the streaming loop forced).  M == 0 is a no-op. */
 w4a8_status w4a8_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
                       const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
                       int64_t N, int32_t group, float *out, hipStream_t stream);
