@@ -471,9 +471,12 @@ def test_silu_mul_quantize(orc, P, I):
     assert not (diff[~amb] != 0).any(), f"{int((diff[~amb] != 0).sum())} unambiguous codes differ"
 
 
-def test_combine(orc):
+@pytest.mark.parametrize("k", [8, 3, 1, 11])
+def test_combine(orc, k):
+    """Top-k of 1, 3, 8 and 11 rows per token, against the oracle, and bit for bit against
+    a sequential fp32 fma chain in pick order."""
     w4 = w4mod()
-    T, k, H = 33, 8, 7168
+    T, H = 33, 7168
     S = T * k + 5
     y = synthetic.activations(41, S, H)
     ys = synthetic.activations(42, T, H)
@@ -486,3 +489,11 @@ def test_combine(orc):
     assert (np.abs(out - ref) <= 1e-6 * mag + 1e-7).all()
     out2 = to_host(w4.moe_combine(to_dev(y), to_dev(sop.ravel()), to_dev(w)))
     assert np.allclose(out2, orc.combine(y, sop, w), rtol=1e-5, atol=1e-6)
+    # the same fmas in the same order as a plain sequential fp32 chain: identical bits.
+    # fma emulated in x87 extended precision (the product of two fp32 is exact there; the
+    # sum is rounded twice only in cases of probability ~2^-39 per step)
+    ld = np.longdouble
+    chain = np.zeros((T, H), np.float32)
+    for j in range(k):
+        chain = (w[:, j:j + 1].astype(ld) * y[sop[:, j]].astype(ld) + chain.astype(ld)).astype(np.float32)
+    assert np.array_equal(out2, chain)
