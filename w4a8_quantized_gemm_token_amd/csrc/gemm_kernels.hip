@@ -1602,11 +1602,19 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
         return hipGetLastError();
     const int64_t G = K / G128;
     const int64_t ntiles = N / 16;
-    const int64_t tpw = (ntiles + cus - 1) / cus;
-    const int64_t nwg = (ntiles + tpw - 1) / tpw;
+    int64_t tpw = (ntiles + cus - 1) / cus;
     // K parts per tile: two, or four when a workgroup has at most four tiles (so
     // that all 16 waves stream), as far as the groups divide evenly
     const int split = (G % 8 == 0 && tpw <= 4) ? 4 : ((G % 4 == 0) ? 2 : 1);
+    // Tiles per workgroup rounded up to whole rounds of the 16 waves (16 / split tiles a
+    // round) when at least 7/8 of the CUs still get a workgroup: every wave then streams
+    // (K = 8192, N = 28672: 7 -> 8 tiles, 256 -> 224 workgroups, 22.3 -> 22.1 us).
+    {
+        const int64_t per_round = kDecWaves / split;
+        const int64_t up = (tpw + per_round - 1) / per_round * per_round;
+        if (up != tpw && 8 * ((ntiles + up - 1) / up) >= 7 * (int64_t)cus) tpw = up;
+    }
+    const int64_t nwg = (ntiles + tpw - 1) / tpw;
     const size_t lds = (size_t)(((dec_lds_bytes(M, K) + 15) / 16) * 16 + dec_red_bytes(split));
     const int64_t nwin = G / 2 / split;
     const dim3 grid((uint32_t)nwg), block(kDecThreads);
