@@ -76,7 +76,7 @@ def test_weights_to_tm_bytes(orc, N, K):
 
 # (M, N, K): ring depth 4 with two and four K parts per tile, depth 2 and 1, one K
 # part (odd window count), rows staged in a loop, several tiles per workgroup with a
-# ragged last workgroup
+# ragged last workgroup, tiles per workgroup rounded up to whole rounds of the waves
 TM_SHAPES = [
     (1, 16, 256),
     (4, 128, 256),
@@ -87,6 +87,7 @@ TM_SHAPES = [
     (16, 64, 8704),
     (2, 4112, 3072),
     (3, 20496, 8192),
+    (2, 28640, 512),    # 1790 tiles: 8 tiles per workgroup (rounded up from 7), last workgroup 6
 ]
 
 
