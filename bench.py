@@ -338,7 +338,7 @@ def prefill(torch, w4, synthetic, reps=10, group=GROUP):
     return {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
-def smoothing(torch, w4, synthetic):
+def quant_variants(torch, w4, synthetic):
     """Packer variants and per-channel smoothing on the decode workload (K=8192, 0.1% x20 weight outliers, 4 x50
     activation channels): the first 4096 output columns, factors from 48 calibration tokens
     (rows 16..63 of the activation draw), error of 16 other tokens against the fp64
@@ -397,7 +397,7 @@ def secondary(torch, w4, synthetic):
     out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
            "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
            "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
-           "quant_variants_K8192_N4096_M16": smoothing(torch, w4, synthetic)}
+           "quant_variants_K8192_N4096_M16": quant_variants(torch, w4, synthetic)}
     from tests.gpu_common import device_experts
     # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
     # back-to-back prepared launches that rotate three copies of the 250 MB expert set
