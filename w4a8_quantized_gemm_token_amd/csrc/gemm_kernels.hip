@@ -1210,7 +1210,23 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int64_t G = K / G128;
     const int64_t lda = K + 16;
     float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(16, K) + 15) / 16) * 16);
-    const int64_t u0 = total * blockIdx.x / gridDim.x, u1 = total * (blockIdx.x + 1) / gridDim.x;
+    // Contiguous unit ranges of one length, rounded up to whole rounds of the 16 waves
+    // (16 / SPLIT tiles), when at least 7/8 of the workgroups still get units: every
+    // wave streams, as in the dense decode launch (an even split would leave some
+    // workgroups a tile short of a round); else the even split.
+    int64_t u0, u1;
+    {
+        const int64_t nb = gridDim.x, per_round = kDecWaves / SPLIT;
+        const int64_t span = (total + nb - 1) / nb;
+        const int64_t up = (span + per_round - 1) / per_round * per_round;
+        if (span > 0 && 8 * ((total + up - 1) / up) >= 7 * nb) {
+            u0 = (int64_t)blockIdx.x * up < total ? (int64_t)blockIdx.x * up : total;
+            u1 = u0 + up < total ? u0 + up : total;
+        } else {
+            u0 = total * blockIdx.x / nb;
+            u1 = total * (blockIdx.x + 1) / nb;
+        }
+    }
     int staged_e = -1;
     int64_t staged_chunk = -1;
     for (int64_t u = u0; u < u1;) {
