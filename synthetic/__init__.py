@@ -11,12 +11,22 @@ so any slice can be regenerated on its own and the GPU-side filler in
                pseudorandom number generators", OOPSLA 2014), all mod 2^64.
   key          mix64(mix64(seed * GOLDEN + tag) + sub * GOLDEN)
   bits(key,i)  mix64(key + (i + 1) * GOLDEN)
-  normal       Irwin-Hall(4) stand-in for N(0,1): the four 16-bit fields of
-               bits() are summed, centred (integer in [-131070, 131070], exact in
-               fp32) and multiplied by fp32(sqrt(3)/65536); variance 1 - 2^-32.
-               Its tails stop at +-2*sqrt(3) (about 3.46 sigma).
+  normal       Irwin-Hall(4) stand-in for N(0,1), used for weights only: the four
+               16-bit fields of bits() are summed, centred (integer in
+               [-131070, 131070], exact in fp32) and multiplied by
+               fp32(sqrt(3)/65536); variance 1 - 2^-32.  Its tails stop at
+               +-2*sqrt(3) (about 3.46 sigma).
   weights      fp32(normal * fp32(std)), std = 0.02
   uniform24    bits >> 40, a 24-bit integer
+
+Activations and router logits are true N(0,1) draws: numpy's PCG64 generator
+seeded with the integer triple (seed, tag, sub) through SeedSequence, float64
+standard_normal in row-major order, rounded once to fp32.  They are drawn on the
+host and copied to the device, so both sides read the same bytes.  Their tails
+matter: with the skewed router bias, cold experts are reached only through tail
+draws, so a bounded stand-in would route to far fewer experts.  The weights'
+stand-in changes neither the routing (logits are a separate draw) nor any byte
+count (sizes are fixed by the shapes).
 
 The recipes per workload (shapes, outliers, offsets, router bias) live in the
 functions below.
@@ -125,11 +135,16 @@ def weights_with_offset(seed: int, N: int, K: int, rows=None) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- activations
+def gauss(seed: int, tag: int, sub: int, shape) -> np.ndarray:
+    """True N(0,1) draws: PCG64 seeded with SeedSequence([seed, tag, sub]), float64, rounded to fp32."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tag), int(sub)])))
+    return g.standard_normal(shape).astype(np.float32)
+
+
 def activations(seed: int, M: int, K: int, tag: int = TAG_X, sub: int = 0, rows=None) -> np.ndarray:
-    """x[m][k] ~ N(0,1) (Irwin-Hall stand-in)."""
-    r = _row_indices(rows, M)
-    idx = (r[:, None] * K + np.arange(K, dtype=np.int64)[None, :]).ravel()
-    return normal(stream_key(seed, tag, sub), idx).reshape(len(r), K)
+    """x[m][k] ~ N(0,1) (true normal, see gauss); rows selects a subset of m."""
+    x = gauss(seed, tag, sub, (M, K))
+    return x if rows is None else x[np.asarray(rows, dtype=np.int64)]
 
 
 def outlier_channels(seed: int, K: int, count: int = 4) -> np.ndarray:
@@ -155,9 +170,8 @@ def activations_with_outlier_channels(seed: int, M: int, K: int, rows=None) -> n
 
 # ----------------------------------------------------------------------------- router
 def router_logits_iid(seed: int, T: int, E: int) -> np.ndarray:
-    """Toy MoE: iid N(0,1) logits, so top-1 routing is uniform over experts."""
-    idx = np.arange(T * E, dtype=np.int64)
-    return normal(stream_key(seed, TAG_LOGIT), idx).reshape(T, E)
+    """Toy MoE: iid N(0,1) logits (true normal), so top-1 routing is uniform over experts."""
+    return gauss(seed, TAG_LOGIT, 0, (T, E))
 
 
 def zipf_bias(E: int, s: float = 1.1) -> np.ndarray:

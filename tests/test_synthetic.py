@@ -19,6 +19,27 @@ def test_normal_standin_moments():
     assert np.abs(z).max() <= 2 * np.sqrt(3) + 1e-6
 
 
+def test_activations_true_normal():
+    # activations and router logits are true N(0,1) draws, tails included
+    from scipy import stats
+    x = synthetic.activations(0, 256, 4096)
+    assert x.dtype == np.float32 and abs(x.mean()) < 0.005 and abs(x.std() - 1.0) < 0.005
+    assert stats.kstest(x.ravel()[:200000].astype(np.float64), "norm").pvalue > 1e-3
+    # P(|z| > 4) = 6.33e-5: about 66 of 2^20 draws, none under a +-3.46 sigma stand-in
+    assert 30 < int((np.abs(x) > 4).sum()) < 110
+    assert np.array_equal(synthetic.activations(0, 256, 4096, rows=[7, 200]), x[[7, 200]])
+    assert not np.array_equal(synthetic.activations(1, 4, 64), synthetic.activations(0, 4, 64))
+
+
+def test_moe_layer_routing_spread():
+    # full MoE layer, 384 experts, top-8, Zipf(1.1) bias: with true-normal logits seed 0 reaches the
+    # cold experts the configured skew implies (about 166 at T=4096 and about 53 at T=64 on average)
+    for T, lo, hi in [(64, 42, 59), (4096, 155, 177)]:
+        z = synthetic.router_logits_skewed(0, T, 384)
+        ids = np.argsort(-z, axis=1, kind="stable")[:, :8]
+        assert lo <= len(np.unique(ids)) <= hi, T
+
+
 def test_weight_recipes():
     W = synthetic.weights(0, synthetic.TAG_W, 0, 64, 256)
     assert W.shape == (64, 256) and abs(W.std() - 0.02) < 0.001
