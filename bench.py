@@ -181,7 +181,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=2000,
-                   help="untimed steps first (about 0.2 s: the GPU leaves its idle clock state)")
+                   help="untimed steps after the fixed-duration warm-up")
+    p.add_argument("--warmup-seconds", type=float, default=1.0,
+                   help="untimed steps for at least this long first, whatever --warmup is (the GPU leaves "
+                        "its idle clock state: a decode launch measured 28 us cold, 25.5 us warm)")
     p.add_argument("--copies", type=int, default=6, help="weight copies rotated to defeat the MALL")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the prefill / MoE figures")
@@ -220,7 +223,7 @@ def decode_setup(torch, w4, synthetic, copies):
     return layers, tms, xs
 
 
-def run_decode(torch, w4, prep, n_layers, xs, steps, warmup):
+def run_decode(torch, w4, prep, n_layers, xs, steps, warmup, warmup_s=0.0):
     """Times `steps` decode steps, then the GEMM kernel alone.
 
     `prep(qa, sc, i, out)` prepares the GEMM over weight copy i.  Each launch is prepared once
@@ -247,9 +250,15 @@ def run_decode(torch, w4, prep, n_layers, xs, steps, warmup):
             gemms[M][calls % n_layers]()
             calls += 1
 
+    tw = time.perf_counter()
+    while time.perf_counter() - tw < warmup_s:   # fixed-duration warm-up, then the counted one
+        for _ in range(100):
+            step()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    warmed_s = time.perf_counter() - tw
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
@@ -276,7 +285,7 @@ def run_decode(torch, w4, prep, n_layers, xs, steps, warmup):
                          "TOPS": round(2 * M * N_DEC * K_DEC / (ms * 1e-3) / 1e12, 3)}
     gemm_bytes = float(np.mean([dense_bytes(M, N_DEC, K_DEC) for M in M_DEC]))
     gemm_ms = float(np.mean(launch_ms))
-    return ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m
+    return ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m, warmed_s
 
 
 def cpu_baseline(synthetic):
@@ -398,7 +407,11 @@ def secondary(torch, w4, synthetic):
            "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
            "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
            "quant_variants_K8192_N4096_M16": quant_variants(torch, w4, synthetic)}
-    from tests.gpu_common import device_experts
+
+    def device_experts(seed, tag, E, N, K):
+        return w4.pack_experts_device(
+            E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, e, K, 0, "plain"), dev)
+
     # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
     # back-to-back prepared launches that rotate three copies of the 250 MB expert set
     # (so no call finds its weights in the 256 MB Infinity Cache); the layer (route,
@@ -507,9 +520,9 @@ def main():
                                                                                    args.group)}), flush=True)
         return
     layers, tms, xs = decode_setup(torch, w4, synthetic, args.copies)
-    ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m = run_decode(
+    ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m, warmed_s = run_decode(
         torch, w4, lambda qa, sc, i, out: w4.prepare_gemm_tm(qa, sc, tms[i], out), len(tms), xs, args.steps,
-        args.warmup)
+        args.warmup, args.warmup_seconds)
     std_per_m = None
     if not args.no_secondary:  # the same step over the standard layout, for comparison
         std_per_m = run_decode(torch, w4, lambda qa, sc, i, out: w4.prepare_gemm(qa, sc, *layers[i], out),
@@ -532,6 +545,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": round(warmed_s, 2),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

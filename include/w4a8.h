@@ -39,8 +39,10 @@
  *     are validated on the host before anything is launched; a rejected call
  *     launches nothing and writes nothing.  w4a8_last_error() then describes
  *     the problem (thread-local text, valid until the next call on the thread).
- *   - group must be 128 (W4A8_EUNSUPPORTED otherwise; there is no fallback).
- *     K must be a multiple of 128 (W4A8_EINVAL; pad K at conversion time).
+ *   - group is 128 unless an entry point says otherwise (the host packers and
+ *     w4a8_gemm / w4a8_gemm_path / w4a8_gemm_debug_isums also take 64 and 256);
+ *     any other value is W4A8_EUNSUPPORTED, with no fallback.  K must be a
+ *     multiple of 128 (W4A8_EINVAL; pad K at conversion time).
  *   - Device pointers (marked "device") must be device memory owned by the
  *     caller; the library allocates nothing and keeps no pointer after the
  *     call returns.  Device calls are asynchronous on `stream` (NULL = the
@@ -72,7 +74,7 @@ typedef enum {
     W4A8_EWORKSPACE = 4     /* the caller's workspace is smaller than the call needs */
 } w4a8_status;
 
-#define W4A8_ABI_VERSION 5
+#define W4A8_ABI_VERSION 6
 #define W4A8_GROUP 128
 
 int w4a8_abi_version(void);
@@ -286,8 +288,10 @@ w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t to
  * the device: the kernel reads expert_offsets itself, so no host round trip
  * is needed between routing and the GEMM.  Each expert takes the loop for its
  * slot count: a streaming loop over 16-row chunks (up to 16 slots), one weight
- * pass for all rows (17 to 64), or the tiled loop (more); all are launched only
- * when max_slots allows an expert of that size.
+ * pass per 64 rows (17 to 128), or the tiled loop (more); a loop is launched only
+ * when max_slots allows an expert of its size.  (When K/128 is not a multiple of
+ * 4, or below 8, the streaming loop takes up to 64 slots and the tiled loop the
+ * rest.)
  *   qa [R][K] i8 and a_scale [R] (R = rows of the activation matrix),
  *   packed [E][N][K/2], scale/zp [E][K/128][N], out [max_slots][N].
  * The caller guarantees expert_offsets[E] <= max_slots and row_index[s] < R
@@ -299,6 +303,21 @@ w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_
                                   const uint16_t *scale, const uint16_t *zp, int64_t N,
                                   int32_t group, int64_t max_slots, float *out,
                                   hipStream_t stream);
+
+/* Device, test/debug aid.  The main loops of w4a8_moe_grouped_gemm (each expert
+ * takes the loop its slot count selects, as above), but instead of the fp32
+ * epilogue every per-group int32 sum is stored ([p2 §3.2, §5.4]: INT8 products
+ * accumulated in int32 per group):
+ *     isums[g][s][n] = sum_{k in group g} qa[row_index[s]][k] * (q_e[n][k] - zp_e[g][n])
+ * for g < K/128, slots s < max_slots of expert e, n < N; isums is device int32
+ * [K/128][max_slots][N], caller-owned.  Slots past expert_offsets[E] are not
+ * written; slots whose row_index is outside [0, R) get unspecified values.  No
+ * scale array is read.  Errors as w4a8_moe_grouped_gemm (group must be 128). */
+w4a8_status w4a8_moe_grouped_gemm_debug_isums(const int8_t *qa, int64_t R, const int32_t *row_index,
+                                              const int32_t *expert_offsets, int32_t E, int64_t K,
+                                              const uint8_t *packed, const uint16_t *zp, int64_t N,
+                                              int32_t group, int64_t max_slots, int32_t *isums,
+                                              hipStream_t stream);
 
 /* Device.  MoE expert activation then per-row re-quantization to INT8:
  * h = silu(gate) * up with gate = gu[p][0..I), up = gu[p][I..2I),

@@ -39,20 +39,9 @@ def device_layer(seed, tag, sub, N, K, mode="plain"):
 
 def device_experts(seed, tag, E, N, K, sub0=0, out=None):
     """Stacked expert weights [E][N][K/2], [E][G][N] x2, expert e drawn from sub-stream sub0 + e."""
-    import torch
     import w4a8_quantized_gemm_token_amd as w4
-    G = K // 128
-    if out is None:
-        out = (torch.empty((E, N, K // 2), dtype=torch.uint8, device=cuda()),
-               torch.empty((E, G, N), dtype=torch.int16, device=cuda()),
-               torch.empty((E, G, N), dtype=torch.int16, device=cuda()))
-    packed, scale, zp = out
-    W = torch.empty((N, K), dtype=torch.float32, device=cuda())
-    for e in range(E):
-        synthetic.fill_weights_device(W, seed, tag, sub0 + e, K, 0, "plain")
-        w4.pack_weights_device(W, out=(packed[e], scale[e], zp[e]))
-    del W
-    return packed, scale, zp
+    return w4.pack_experts_device(
+        E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, sub0 + e, K, 0, "plain"), cuda(), out=out)
 
 
 def oracle_columns(orc, seed, tag, sub, K, cols, mode="plain"):

@@ -410,6 +410,52 @@ def test_grouped_gemm_weight_streaming_loop(orc):
         check_close(out[s0:s1][:, cols], ref, mag, f"expert {e} ({s1 - s0} slots)")
 
 
+# Size classes of the expert loops: up to 16 slots (16-row chunks), 17-128 (one weight pass
+# per 64 rows; handed to the 16-row loop when it has too few units for the machine), more than
+# 128 (256-row tiles); and, when K/128 is not a multiple of 4, up to 64 slots streamed and the
+# rest tiled (128-row tiles up to 128 slots).
+GROUPED_ISUM_CASES = [  # (counts, N, K)
+    ([16, 17, 3, 32, 33, 0, 64, 65, 1, 128, 129, 300], 2048, 2048),   # every class at the MoE down K
+    ([5, 100, 20], 256, 2048),                  # a lone mid-size expert: the 16-row loop takes it
+    ([1, 9, 40, 64, 65, 128, 200], 544, 384),   # K/128 = 3: streamed up to 64, tiled above
+    ([7, 70, 150, 100, 40], 4096, 7168),        # the MoE gate/up shape
+    ([2, 130], 160, 8704),                      # 16-row chunks with their rows near the LDS limit
+]
+
+
+@pytest.mark.parametrize("counts,N,K", GROUPED_ISUM_CASES)
+def test_grouped_gemm_isums_bit_exact(orc, counts, N, K):
+    """The per-group int32 sums of every slot of the expert-grouped GEMM, through the debug entry
+    (the main loops each slot count selects), against the oracle's, bit for bit."""
+    w4 = w4mod()
+    E = len(counts)
+    S = sum(counts)
+    R = 311
+    rng = np.random.default_rng(K + N)
+    row_index = rng.integers(0, R, S).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    qr, _ = orc.quantize_act(synthetic.activations(K + 3, R, K))
+    packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device=cuda())
+    zp = torch.empty((E, K // 128, N), dtype=torch.int16, device=cuda())
+    refs = []
+    for e in range(E):
+        W = synthetic.fill_weights_host(K, synthetic.TAG_W, e, K, 0, N, "offset" if e % 2 else "plain")
+        q, s_, z = orc.quantize_weights(W)
+        packed[e] = to_dev(orc.pack_nibbles(q))
+        zp[e] = to_dev(z.view(np.int16))
+        refs.append((q, z))
+    isums = to_host(w4.moe_grouped_gemm_debug_isums(to_dev(qr), to_dev(row_index), to_dev(offsets), packed, zp,
+                                                    max_slots=S))
+    for e in range(E):
+        s0, s1 = offsets[e], offsets[e + 1]
+        if s0 == s1:
+            continue
+        q, z = refs[e]
+        iref = orc.group_isums(qr[row_index[s0:s1]], q, z)
+        bad = isums[:, s0:s1] != iref
+        assert not bad.any(), f"expert {e} ({s1 - s0} slots): {int(bad.sum())} sums differ"
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 512])
 def test_toy_moe_full_size_sampled(orc, B):
     """8 experts, top-1, K=4096, N=14336: route on the GPU, grouped GEMM, combine; the
@@ -460,6 +506,16 @@ def test_silu_mul_quantize(orc, P, I):
     qh, hs, h = (to_host(t) for t in w4.silu_mul_quantize(to_dev(gu), want_h=True))
     h_ref = orc.silu_mul(gu)
     assert np.allclose(h, h_ref, rtol=4e-6, atol=1e-30)
+    gxu = np.abs(gu[:, :I].astype(np.float64) * gu[:, I:].astype(np.float64))
+    assert (np.abs(h - h_ref) <= 1e-5 * gxu + 1e-7).all()
+    # the codes and row scales: bit-exact against the per-token quantizer applied to the
+    # kernel's own fp32 h
+    q_o2, s_o2 = orc.quantize_act(h)
+    assert np.array_equal(qh, q_o2)
+    assert np.array_equal(hs.view(np.uint32), s_o2.view(np.uint32))
+    # the per-token quantizer kernel over the same h bytes gives the same codes
+    qx, sx = (to_host(t) for t in w4.quantize_act(to_dev(h)))
+    assert np.array_equal(qx, qh) and np.array_equal(sx.view(np.uint32), hs.view(np.uint32))
     amax = np.abs(h_ref).max(1)
     assert np.allclose(hs, amax / 127.0, rtol=1e-5)
     # codes: the oracle's quantizer applied to the oracle's own h (rounded to fp32);

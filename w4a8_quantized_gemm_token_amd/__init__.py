@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 GROUP = 128
-ABI_VERSION = 5          # W4A8_ABI_VERSION of the header this binding follows
+ABI_VERSION = 6          # W4A8_ABI_VERSION of the header this binding follows
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
@@ -27,7 +27,8 @@ EXPORTS = (
     "w4a8_quantize_act", "w4a8_gemm", "w4a8_gemm_debug_isums", "w4a8_gemm_path",
     "w4a8_tm_bytes", "w4a8_weights_to_tm", "w4a8_gemm_tm",
     "w4a8_channel_absmax", "w4a8_smooth_factors", "w4a8_pack_weights_device_smooth", "w4a8_quantize_act_smooth",
-    "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_silu_mul_quantize", "w4a8_moe_combine",
+    "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_moe_grouped_gemm_debug_isums", "w4a8_silu_mul_quantize",
+    "w4a8_moe_combine",
     "w4a8_moe_ffn_workspace_size", "w4a8_moe_ffn_workspace_layout", "w4a8_moe_ffn",
 )
 # order of the parts of the MoE FFN workspace (enum w4a8_moe_ws_part)
@@ -74,6 +75,7 @@ def load() -> ctypes.CDLL:
         "w4a8_gemm_tm": (ctypes.c_int, [p, p, i64, i64, p, i64, i32, p, p]),
         "w4a8_moe_route": (ctypes.c_int, [p, i64, i32, i32, i32, p, p, p, p, p, p, p]),
         "w4a8_moe_grouped_gemm": (ctypes.c_int, [p, p, i64, p, p, i32, i64, p, p, p, i64, i32, i64, p, p]),
+        "w4a8_moe_grouped_gemm_debug_isums": (ctypes.c_int, [p, i64, p, p, i32, i64, p, p, i64, i32, i64, p, p]),
         "w4a8_silu_mul_quantize": (ctypes.c_int, [p, i64, i64, p, p, p, p]),
         "w4a8_moe_combine": (ctypes.c_int, [p, p, p, p, i64, i32, i64, p, p]),
         "w4a8_moe_ffn_workspace_size": (sz, [i64, i64, i64, i32, i32]),
@@ -392,6 +394,36 @@ def moe_grouped_gemm(qa, a_scale, row_index, offsets, packed, scale, zp, max_slo
           E, K, _dev_ptr(packed), _dev_ptr(scale), _dev_ptr(zp), N, group, max_slots, _dev_ptr(out),
           _stream(qa.device))
     return out
+
+
+def moe_grouped_gemm_debug_isums(qa, row_index, offsets, packed, zp, max_slots: int, group: int = GROUP):
+    """int32 [K/128][max_slots][N] per-group integer sums of every slot (test aid)."""
+    torch = _torch()
+    R, K = qa.shape
+    E, N = packed.shape[0], packed.shape[1]
+    isums = torch.zeros((K // group, max_slots, N), dtype=torch.int32, device=qa.device)
+    _call("w4a8_moe_grouped_gemm_debug_isums", _dev_ptr(qa), R, _dev_ptr(row_index), _dev_ptr(offsets), E, K,
+          _dev_ptr(packed), _dev_ptr(zp), N, group, max_slots, _dev_ptr(isums), _stream(qa.device))
+    return isums
+
+
+def pack_experts_device(E: int, N: int, K: int, fill, device, group: int = GROUP, out=None):
+    """Stacked expert weights from the device packer: (packed u8 [E][N][K/2], scale, zp i16-bits
+    [E][K/group][N]).  fill(e, W) writes expert e's fp32 weights into the device tensor W [N][K];
+    one fp32 buffer is reused for all experts."""
+    torch = _torch()
+    G = K // group
+    if out is None:
+        out = (torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
+               torch.empty((E, G, N), dtype=torch.int16, device=device),
+               torch.empty((E, G, N), dtype=torch.int16, device=device))
+    packed, scale, zp = out
+    W = torch.empty((N, K), dtype=torch.float32, device=device)
+    for e in range(E):
+        fill(e, W)
+        pack_weights_device(W, group=group, out=(packed[e], scale[e], zp[e]))
+    del W
+    return packed, scale, zp
 
 
 def prepare_moe_route(logits, topk: int, outs) -> Launch:

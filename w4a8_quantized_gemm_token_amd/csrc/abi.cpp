@@ -428,8 +428,24 @@ w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_
     W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");
     if (max_slots == 0 || R == 0) return W4A8_OK;
     return hip_status(launch_grouped_gemm(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
-                                          max_slots, max_slots, out, stream),
+                                          max_slots, max_slots, out, nullptr, stream),
                       "grouped_gemm launch");
+}
+
+w4a8_status w4a8_moe_grouped_gemm_debug_isums(const int8_t *qa, int64_t R, const int32_t *row_index,
+                                              const int32_t *expert_offsets, int32_t E, int64_t K,
+                                              const uint8_t *packed, const uint16_t *zp, int64_t N, int32_t group,
+                                              int64_t max_slots, int32_t *isums, hipStream_t stream) {
+    clear_error();
+    if (w4a8_status st = check_gemm(qa, R, K, packed, nullptr, zp, N, group, isums)) return st;
+    if (w4a8_status st = check_group(group, K)) return st;
+    W4A8_REQUIRE(expert_offsets, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
+    W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");
+    if (max_slots == 0 || R == 0) return W4A8_OK;
+    return hip_status(launch_grouped_gemm(qa, nullptr, R, row_index, expert_offsets, E, K, packed, nullptr, zp, N,
+                                          max_slots, max_slots, nullptr, isums, stream),
+                      "grouped_gemm_debug_isums launch");
 }
 
 w4a8_status w4a8_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh, float *h_scale, float *h_out,
@@ -553,12 +569,12 @@ w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t
         return hip_status(err, "moe_ffn: quantize");
     // top-k picks distinct experts per token, so no expert (the shared one included) gets more than T slots
     if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S, T,
-                                   gu, stream)) != hipSuccess)
+                                   gu, nullptr, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: gate/up grouped GEMM");
     if ((err = launch_silu_mul_quantize(gu, S, I, qh, h_scale, nullptr, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: silu*up requant");
     if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E + 1, I, dn_packed, dn_scale, dn_zp, H, S, T, y,
-                                   stream)) != hipSuccess)
+                                   nullptr, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: down grouped GEMM");
     if ((err = launch_moe_combine(y, sop, w, y + P * H, T, topk, H, out, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: combine");

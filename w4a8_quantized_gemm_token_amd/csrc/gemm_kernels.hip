@@ -148,7 +148,8 @@ __device__ __forceinline__ void stream_unit(const int8_t *__restrict__ qa, const
     auto load_group = [&](int u, int64_t g) {
         bq[u] = __builtin_nontemporal_load(bptr + g * (G128 / 2 / 16));
         zq[u] = zptr[g * N];
-        sq[u] = sptr[g * N];
+        if constexpr (!ISUMS) sq[u] = sptr[g * N];
+        else sq[u] = 0;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             const v4u *ap = reinterpret_cast<const v4u *>(aptr[t] + g * G128);
@@ -297,7 +298,8 @@ __device__ __forceinline__ void stream2_unit(float *lds_red, const int8_t *__res
         rb1[u] = __builtin_nontemporal_load(b1p + w * 8);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            rs[u][h] = sptr[(2 * w + h) * N];
+            if constexpr (!ISUMS) rs[u][h] = sptr[(2 * w + h) * N];
+            else rs[u][h] = 0;
             rz[u][h] = zptr[(2 * w + h) * N];
         }
 #pragma unroll
@@ -458,7 +460,7 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
 
 // Tiles [t0, t1) of 16 columns for the M <= 16 activation rows staged in `rows`
 // (row stride K + 16).  `store(m, col, v)` receives a_scale-free fp32 sums; with
-// ISUMS the per-group int32 sums go to isums[g][m][col] instead.
+// ISUMS the per-group int32 sums go to `istore(g, m, col, v)` instead.
 // `stage(0)` runs before the first weight windows are issued and may start loading the
 // rows; `stage(1)` runs after them (so their latency overlaps it) and is followed by a
 // workgroup barrier: it fills `rows` when they change.
@@ -475,11 +477,11 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
 // and the -zp operand of the zero-point MFMA is one byte replicated (one v_perm).
 constexpr int64_t kTmBlock = 2 * 1024 + 128;
 
-template <int U, int SPLIT, bool ISUMS, bool TM, typename Stage, typename Store>
+template <int U, int SPLIT, bool ISUMS, bool TM, typename Stage, typename Store, typename IStore>
 __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M, int64_t K,
                                           const uint8_t *__restrict__ wpk, const uint16_t *__restrict__ wsc,
                                           const uint16_t *__restrict__ wzp, int64_t N, int64_t t0, int64_t t1,
-                                          Stage stage, Store store, int32_t *__restrict__ isums) {
+                                          Stage stage, Store store, IStore istore) {
     const int64_t lda = K + 16;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -506,7 +508,8 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wpk), (short)0, (int)(uint32_t)wbytes, 0x00020000);
     const uint32_t colbyte = TM ? (uint32_t)(16 * lane) : (uint32_t)((lane & 7) * (K / 2) + lchunk);
     const uint32_t szbyte = 2048u + 8u * (uint32_t)(lane & 15);  // TM: this lane's column's words
-    const uint16_t *szbase = TM ? nullptr : ((kq < 2) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
+    // (the debug form stores int32 sums and reads no scales: every lane reads zero points)
+    const uint16_t *szbase = TM ? nullptr : ((kq < 2 && !ISUMS) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
     v4u rb0[U], rb1[U];
     uint32_t rsz[U];   // standard layout: one fp16 word per lane (spread with ds_bpermute)
     v2u rsz2[U];       // tile-major: the four words of this lane's column
@@ -636,7 +639,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const int m = 4 * kq + r;
-                                if (m < M) isums[(g * M + m) * N + col] = d[r];
+                                if (m < M) istore(g, m, col, d[r]);
                             }
                         } else {
                             float sc = half_bits_to_float((uint16_t)sz[h]);
@@ -751,7 +754,8 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
             }
             if (!ISUMS && threadIdx.x < M) sasc[threadIdx.x] = asc;
         },
-        [&](int m, int64_t col, float v) { out[m * N + col] = sasc[m] * v; }, isums);
+        [&](int m, int64_t col, float v) { out[m * N + col] = sasc[m] * v; },
+        [&](int64_t g, int m, int64_t col, int32_t v) { isums[(g * M + m) * N + col] = v; });
 }
 
 // Dense layer through the line-wide loop: a workgroup of SPLIT waves per 16-column tile.
@@ -885,14 +889,14 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
             sl.rz = zglob[(2 * g + zsub) * N];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                sl.rs[j][0] = sglob[j][2 * g * N];
-                sl.rs[j][1] = sglob[j][(2 * g + 1) * N];
+                sl.rs[j][0] = ISUMS ? 0 : sglob[j][2 * g * N];
+                sl.rs[j][1] = ISUMS ? 0 : sglob[j][(2 * g + 1) * N];
             }
         } else {
             const int64_t gg = GS == 256 ? g >> 1 : g;
             sl.rz = zglob[gg * N];
-            sl.rs[0][0] = sglob[0][gg * N];
-            sl.rs[1][0] = sglob[1][gg * N];
+            sl.rs[0][0] = ISUMS ? 0 : sglob[0][gg * N];
+            sl.rs[1][0] = ISUMS ? 0 : sglob[1][gg * N];
         }
     };
     auto lstore = [&](const Slot &sl, int buf) {
@@ -1148,12 +1152,15 @@ __device__ __forceinline__ int64_t mid_class_units(int32_t E, int64_t *lds_pfx, 
     return total;
 }
 
-template <int U>
+// ISUMS (test aid, in every expert loop): the per-group int32 sums of each slot go to
+// isums[g][slot][n] (g < K/128, slot < max_slots) instead of the fp32 output, and no
+// scale is read; slots whose row index is outside [0, R) get unspecified sums.
+template <int U, bool ISUMS>
 __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out) {
+    float *__restrict__ out, int32_t *__restrict__ isums) {
     __shared__ int64_t pfx[kMaxExperts + 1];
     const int64_t ntn = N / 16;
     const int64_t total = expert_prefix(E, pfx, kStreamThreads, [&](int e) -> int64_t {
@@ -1172,11 +1179,14 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
         const uint16_t *wz = zp + (int64_t)e * G * N;
         const StreamRows sr{s0, rows};
         if (rows <= 16)
-            stream_unit<1, U, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+            stream_unit<1, U, ISUMS>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, isums,
+                                     max_slots);
         else if (rows <= 32)
-            stream_unit<2, U2, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+            stream_unit<2, U2, ISUMS>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, isums,
+                                      max_slots);
         else
-            stream_unit<4, U4, false>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, nullptr, 0);
+            stream_unit<4, U4, ISUMS>(qa, a_scale, row_index, R, sr, K, wp, ws, wz, N, tn * 16, out, N, isums,
+                                      max_slots);
     }
 }
 
@@ -1187,12 +1197,12 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
 // range of units, so it restages rows only when the chunk changes, and its tiles of
 // one chunk run as one stream.  Each tile is split over SPLIT K parts: four when no
 // workgroup can get more than four tiles (so that all 16 waves stream), else two.
-template <int U, int SPLIT>
+template <int U, int SPLIT, bool ISUMS>
 __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int small_max, int64_t mid_floor) {
+    float *__restrict__ out, int32_t *__restrict__ isums, int small_max, int64_t mid_floor) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
     __shared__ int32_t srow[16];
@@ -1261,7 +1271,7 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
             if (phase == 0 || !restage) return;
             stage_rows_dma(dsm, lda, qa, K, rows, [&](int r) { return (int64_t)(srow[r] >= 0 ? srow[r] : 0); });
             float asc = 0.0f;
-            if (threadIdx.x < 16) {
+            if (!ISUMS && threadIdx.x < 16) {
                 const int32_t row = srow[threadIdx.x];
                 asc = a_scale[row >= 0 ? row : 0];
             }
@@ -1271,7 +1281,11 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
         auto store = [&](int m, int64_t col, float v) {
             if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
         };
-        dec_tiles<U, SPLIT, false, false>(dsm, red, rows, K, wpk, wsc, wzp, N, t0, t1, stage, store, nullptr);
+        dec_tiles<U, SPLIT, ISUMS, false>(
+            dsm, red, rows, K, wpk, wsc, wzp, N, t0, t1, stage, store,
+            [&](int64_t g, int m, int64_t col, int32_t v) {
+                if (srow[m] >= 0) isums[(g * max_slots + s0 + m) * N + col] = v;
+            });
     }
 }
 
@@ -1298,12 +1312,12 @@ constexpr int kMidSlice = 4;                       // groups per activation slic
 constexpr int kMidRow = kMidSlice * G128 + 16;     // LDS bytes per staged row and slice
 __host__ __device__ inline int64_t mid_lds_bytes(int mf) { return 2ll * 32 * mf * kMidRow; }
 
-template <int MF, int U>
+template <int MF, int U, bool ISUMS>
 __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int64_t cmin, int64_t cmax, int64_t mid_floor) {
+    float *__restrict__ out, int32_t *__restrict__ isums, int64_t cmin, int64_t cmax, int64_t mid_floor) {
     constexpr int RM = 32 * MF;                    // staged rows
     constexpr int BUF = RM * kMidRow;
     constexpr int TPR = kMidThreads / RM;          // staging threads per row
@@ -1348,7 +1362,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
         x.store = col < N;
         x.col = col < N ? col : N - 1;
         x.rw = make_rsrc(packed + (int64_t)x.e * N * (K / 2));
-        x.rs = make_rsrc(scale + (int64_t)x.e * G * N);
+        x.rs = make_rsrc((ISUMS ? zp : scale) + (int64_t)x.e * G * N);  // (ISUMS reads no scales)
         x.rz = make_rsrc(zp + (int64_t)x.e * G * N);
         x.vw = (uint32_t)(x.col * (K / 2) + 32 * h);
         x.vs = (uint32_t)(x.col * 2);
@@ -1363,6 +1377,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     auto row_scale = [&](const Unit &x, int r) -> float {
         if (r >= x.c) return -1.0f;
         const int64_t q = row_index ? (int64_t)row_index[x.s0 + r] : x.s0 + r;
+        if constexpr (ISUMS) return (q >= 0 && q < R) ? 1.0f : -1.0f;
         return (q >= 0 && q < R) ? a_scale[q] : -1.0f;
     };
 
@@ -1472,8 +1487,19 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
 #pragma unroll
                 for (int f = 0; f < MF; ++f) {
                     if (f >= mt) break;
+                    if constexpr (ISUMS) {
+                        if (cur.store) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[f][i] = fmaf(sc, (float)dacc[f][i], acc[f][i]);
+                            for (int i = 0; i < 16; ++i) {
+                                const int r = f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                                if (sasc[u & 1][r] >= 0.0f)
+                                    isums[(g * max_slots + cur.s0 + r) * N + cur.col] = dacc[f][i];
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[f][i] = fmaf(sc, (float)dacc[f][i], acc[f][i]);
+                    }
                 }
                 // refill: group g + U of this unit, else of the next one (the last unit
                 // re-reads its own first groups, which nothing consumes)
@@ -1490,7 +1516,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
         // outputs of this unit: lane holds column col, rows f*32 + 8*(i/4) + 4*h + i%4
         // (an opaque copy of the lane index keeps the compiler from computing the row
         // addresses before the slice loop, where they would hold registers throughout)
-        if (cur.store) {
+        if (!ISUMS && cur.store) {
             int ln = lane;
             __asm__ volatile("" : "+v"(ln));
             const int h2 = ln >> 5;
@@ -1513,12 +1539,12 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     __builtin_amdgcn_s_waitcnt(0);  // the ring's last (unused) loads
 }
 
-template <int WM, int WN>
+template <int WM, int WN, bool ISUMS>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int64_t cmin, int64_t cmax) {
+    float *__restrict__ out, int32_t *__restrict__ isums, int64_t cmin, int64_t cmax) {
     using S = TileShape<WM, WN>;
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
@@ -1542,9 +1568,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
         const int64_t tm = local % mt, tn = local / mt;
         const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * S::BM;
         const int rows = (int)((c - tm * S::BM) < S::BM ? (c - tm * S::BM) : S::BM);
-        tile2_unit<WM, WN, false>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
-                                  packed + (int64_t)e * N * (K / 2), scale + (int64_t)e * G * N,
-                                  zp + (int64_t)e * G * N, N, tn * S::BN, out, N, nullptr, 0);
+        tile2_unit<WM, WN, ISUMS>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
+                                  packed + (int64_t)e * N * (K / 2), (ISUMS ? nullptr : scale + (int64_t)e * G * N),
+                                  zp + (int64_t)e * G * N, N, tn * S::BN, out, N, isums, max_slots);
         __syncthreads();  // the next unit reuses the LDS buffers
     }
 }
@@ -1692,10 +1718,7 @@ namespace w4a8 {
 hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                        const uint16_t *scale, const uint16_t *zp, int64_t N, int path, float *out, int32_t *isums,
                        hipStream_t stream) {
-    // The debug entry has no scale array.  Kernels may load scale and zero point with
-    // one instruction (different lanes, same [G][N] shape), so they always get a valid
-    // pointer: the zero-point array stands in, and its values are never used as scales.
-    if (!scale) scale = zp;
+    // (the debug entry passes no scale array: its ISUMS forms read none)
     if (path == 1) {
         const int64_t G = K / G128;
         const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -1744,7 +1767,6 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
 hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                                    const uint16_t *scale, const uint16_t *zp, int64_t N, int group, int path, float *out,
                                    int32_t *isums, hipStream_t stream) {
-    if (!scale) scale = zp;  // debug entry: see launch_gemm
     const bool wide = path == 4 || (path == 2 && M > 128);
     if (group == 64)
         return wide ? launch_tiled<4, 2, 64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
@@ -1819,63 +1841,86 @@ hipError_t launch_weights_to_tm(const uint8_t *packed, const uint16_t *scale, co
 
 // Experts with more than cmin slots: 128-row tiles up to 128 slots, 256-row tiles
 // above (a 256-row tile over a 65..128-slot expert would waste most of its work).
-template <int WM, int WN>
+template <int WM, int WN, bool IS>
 static hipError_t launch_grouped_tiled_t(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                          const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                          const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                                         float *out, int64_t cmin, int64_t cmax, int cus, hipStream_t stream) {
+                                         float *out, int32_t *isums, int64_t cmin, int64_t cmax, int cus,
+                                         hipStream_t stream) {
     using S = TileShape<WM, WN>;
     const size_t lds = 2 * S::LDS_STAGE;
-    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<WM, WN>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<WM, WN, IS>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return hipGetLastError();
-    hipLaunchKernelGGL((grouped_tiled_kernel<WM, WN>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa,
-                       a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, cmin, cmax);
+    hipLaunchKernelGGL((grouped_tiled_kernel<WM, WN, IS>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa,
+                       a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums, cmin,
+                       cmax);
     return hipGetLastError();
+}
+
+template <int WM, int WN>
+static hipError_t launch_grouped_tiled_s(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
+                                         const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
+                                         const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
+                                         float *out, int32_t *isums, int64_t cmin, int64_t cmax, int cus,
+                                         hipStream_t stream) {
+    return isums ? launch_grouped_tiled_t<WM, WN, true>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
+                                                        zp, N, max_slots, out, isums, cmin, cmax, cus, stream)
+                 : launch_grouped_tiled_t<WM, WN, false>(qa, a_scale, R, row_index, expert_offsets, E, K, packed,
+                                                         scale, zp, N, max_slots, out, isums, cmin, cmax, cus, stream);
 }
 
 // experts with more than cmin slots
 static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                        const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                        const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                                       float *out, int64_t cmin, int cus, hipStream_t stream) {
+                                       float *out, int32_t *isums, int64_t cmin, int cus, hipStream_t stream) {
     if (max_slots <= cmin) return hipSuccess;
     if (cmin < 128) {
-        hipError_t err = launch_grouped_tiled_t<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
-                                                      zp, N, max_slots, out, cmin, 128, cus, stream);
+        hipError_t err = launch_grouped_tiled_s<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
+                                                      zp, N, max_slots, out, isums, cmin, 128, cus, stream);
         if (err != hipSuccess || max_slots <= 128) return err;
     }
-    return launch_grouped_tiled_t<4, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
-                                        max_slots, out, 128, INT64_MAX, cus, stream);
+    return launch_grouped_tiled_s<4, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
+                                        max_slots, out, isums, 128, INT64_MAX, cus, stream);
 }
 
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                               int64_t max_per_expert, float *out, hipStream_t stream) {
+                               int64_t max_per_expert, float *out, int32_t *isums, hipStream_t stream) {
     if (max_per_expert > max_slots) max_per_expert = max_slots;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
     const int64_t G = K / G128;
-    if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax) {
+    // the decode loop stages gathered rows with 32-bit offsets (row * K) and addresses the
+    // codes with 32-bit offsets; larger inputs take the streaming loop (64-bit addresses)
+    if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax &&
+        (int64_t)R * K < (1ll << 32)) {
         const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
         // experts with 17..128 slots: one weight pass per 64 rows when the K slicing
         // fits (at least two slices; activation offsets below 2^32)
-        const bool mid = G % kMidSlice == 0 && G >= 2 * kMidSlice && (int64_t)R * K < (1ll << 32);
+        const bool mid = G % kMidSlice == 0 && G >= 2 * kMidSlice;
         const int small_max = mid ? kMidMin : (int)kSmallRows;
         // the weight-streaming loop runs if some expert can be in its class; the decode
         // loop takes that class when it has too few units to keep a quarter of the CUs
         // busy (a lone mid-size expert): re-reading it per 16 rows is then cheaper
         const int64_t mid_floor = (mid && max_per_expert > kMidMin) ? cus / 4 : 0;
-#define W4A8_GDEC(UU, SS)                                                                                           \
+#define W4A8_GDEC1(UU, SS, IS)                                                                                      \
     do {                                                                                                            \
         const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + dec_red_bytes(SS));                 \
-        if (hipFuncSetAttribute((const void *)grouped_decode_kernel<UU, SS>,                                        \
+        if (hipFuncSetAttribute((const void *)grouped_decode_kernel<UU, SS, IS>,                                    \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)               \
             return hipGetLastError();                                                                               \
-        hipLaunchKernelGGL((grouped_decode_kernel<UU, SS>), dgrid, dblock, dlds, stream, qa, a_scale, R, row_index,  \
-                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out, small_max, mid_floor);       \
+        hipLaunchKernelGGL((grouped_decode_kernel<UU, SS, IS>), dgrid, dblock, dlds, stream, qa, a_scale, R,        \
+                           row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums, small_max, \
+                           mid_floor);                                                                              \
+    } while (0)
+#define W4A8_GDEC(UU, SS)                         \
+    do {                                          \
+        if (isums) W4A8_GDEC1(UU, SS, true);      \
+        else W4A8_GDEC1(UU, SS, false);           \
     } while (0)
         // four K parts per tile when no workgroup can get more than four tiles (an upper
         // bound of the work: each expert's last chunk may be partial)
@@ -1889,47 +1934,54 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
             else W4A8_GDEC(1, 2);
         }
 #undef W4A8_GDEC
+#undef W4A8_GDEC1
         hipError_t derr = hipGetLastError();
         if (derr != hipSuccess) return derr;
         if (!mid) return max_per_expert <= kSmallRows ? hipSuccess
                                                       : launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets,
                                                                              E, K, packed, scale, zp, N, max_slots, out,
-                                                                             kSmallRows, cus, stream);
+                                                                             isums, kSmallRows, cus, stream);
         // the other loops only when some expert can have that many slots
-#define W4A8_GMID(MF, CMIN, CMAX)                                                                                       \
+#define W4A8_GMID1(MF, CMIN, CMAX, IS)                                                                              \
     do {                                                                                                            \
-        if (max_per_expert > (CMIN)) {                                                                              \
-            if (hipFuncSetAttribute((const void *)grouped_mid_kernel<MF, 4>,                                        \
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes(MF)) != hipSuccess) \
-                return hipGetLastError();                                                                           \
-            hipLaunchKernelGGL((grouped_mid_kernel<MF, 4>), dim3((uint32_t)cus), dim3(kMidThreads),                \
-                               (size_t)mid_lds_bytes(MF), stream, qa, a_scale, R, row_index, expert_offsets, E, K,   \
-                               packed, scale, zp, N, max_slots, out, (int64_t)(CMIN), (int64_t)(CMAX), mid_floor);  \
-            if ((derr = hipGetLastError()) != hipSuccess) return derr;                                              \
-        }                                                                                                           \
+        if (hipFuncSetAttribute((const void *)grouped_mid_kernel<MF, 4, IS>,                                        \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)mid_lds_bytes(MF)) != hipSuccess)  \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((grouped_mid_kernel<MF, 4, IS>), dim3((uint32_t)cus), dim3(kMidThreads),                \
+                           (size_t)mid_lds_bytes(MF), stream, qa, a_scale, R, row_index, expert_offsets, E, K,       \
+                           packed, scale, zp, N, max_slots, out, isums, (int64_t)(CMIN), (int64_t)(CMAX),           \
+                           mid_floor);                                                                              \
+        if ((derr = hipGetLastError()) != hipSuccess) return derr;                                                  \
     } while (0)
         static_assert(kMidRows == 64, "the weight-streaming loop stages 64 rows (MF = 2)");
-        W4A8_GMID(2, kMidMin, kMidMax);  // 65..128 slots: two row blocks, the weights read twice
-#undef W4A8_GMID
+        if (max_per_expert > kMidMin) {  // 65..128 slots: two row blocks, the weights read twice
+            if (isums) W4A8_GMID1(2, kMidMin, kMidMax, true);
+            else W4A8_GMID1(2, kMidMin, kMidMax, false);
+        }
+#undef W4A8_GMID1
         if (max_per_expert <= kMidMax) return hipSuccess;
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, kMidMax, cus, stream);
+                                    out, isums, kMidMax, cus, stream);
     }
     const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
-    if (U == 4)
-        hipLaunchKernelGGL(grouped_stream_kernel<4>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
-                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
-    else if (U == 2)
-        hipLaunchKernelGGL(grouped_stream_kernel<2>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
-                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
-    else
-        hipLaunchKernelGGL(grouped_stream_kernel<1>, sgrid, sblock, 0, stream, qa, a_scale, R, row_index,
-                           expert_offsets, E, K, packed, scale, zp, N, max_slots, out);
+#define W4A8_GSTR(UU)                                                                                               \
+    do {                                                                                                            \
+        if (isums)                                                                                                  \
+            hipLaunchKernelGGL((grouped_stream_kernel<UU, true>), sgrid, sblock, 0, stream, qa, a_scale, R,         \
+                               row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums);       \
+        else                                                                                                        \
+            hipLaunchKernelGGL((grouped_stream_kernel<UU, false>), sgrid, sblock, 0, stream, qa, a_scale, R,        \
+                               row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums);       \
+    } while (0)
+    if (U == 4) W4A8_GSTR(4);
+    else if (U == 2) W4A8_GSTR(2);
+    else W4A8_GSTR(1);
+#undef W4A8_GSTR
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || max_per_expert <= kSmallRows) return err;
     return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
-                                kSmallRows, cus, stream);
+                                isums, kSmallRows, cus, stream);
 }
 
 }  // namespace w4a8

@@ -43,12 +43,13 @@ hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64
 
 // max_per_expert: a bound on any one expert's slot count known to the caller (the
 // MoE layer knows no expert gets more than T); loops for larger experts are not
-// launched.  max_slots when nothing better is known.
+// launched.  max_slots when nothing better is known.  isums != nullptr selects the
+// debug form: per-group int32 sums isums[K/128][max_slots][N] instead of `out`.
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R,
                                const int32_t *row_index, const int32_t *expert_offsets, int32_t E,
                                int64_t K, const uint8_t *packed, const uint16_t *scale,
                                const uint16_t *zp, int64_t N, int64_t max_slots, int64_t max_per_expert,
-                               float *out, hipStream_t stream);
+                               float *out, int32_t *isums, hipStream_t stream);
 
 // Tile-major weights for the decode loop (M <= 16): bytes of the array, whether a
 // shape is served, the GEMM over it, and the conversion from the standard layout.
