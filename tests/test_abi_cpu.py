@@ -125,6 +125,17 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_moe_ffn(f, f, 64, 7168, 2048, 1024, 8, f, f, f, f, f, f, f, f, need, None) == EINVAL
 
 
+def test_grouped_isums_entry_rejects_before_launch():
+    lib = w4.load()
+    f = _fake()
+    # (qa, R, row_index, offsets, E, K, packed, zp, N, group, max_slots, isums, stream)
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 128, 64, 8, f, None) == EUNSUPPORTED
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, None, 4, 256, f, f, 128, 128, 8, f, None) == EINVAL
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 0, 256, f, f, 128, 128, 8, f, None) == EINVAL
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 120, 128, 8, f, None) == EINVAL
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 128, 128, 0, f, None) == 0
+
+
 def test_moe_ffn_workspace_layout():
     """Parts in enum order, 256-byte aligned, each at least its tensor's size, total = size query."""
     T, H, I, E, k = 64, 7168, 2048, 384, 8
