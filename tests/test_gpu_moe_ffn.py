@@ -180,7 +180,9 @@ def test_moe_ffn_full_size_stagewise(orc, T):
     ref_e2e = np.zeros((n, H), np.float64)     # oracle chain: w_j * y_j per sampled slot
     tol_e2e = np.zeros((n, H), np.float64)
     wslot = np.array([1.0 if e == E else float(w_r[t][list(ids_r[t]).index(e)]) for t, e in zip(stok, sexp)])
-    for e in np.unique(sexp):
+    for i_e, e in enumerate(np.unique(sexp)):
+        if i_e % 32 == 0:
+            print(f"T={T}: oracle stages, expert {i_e} of {len(np.unique(sexp))}", flush=True)
         a, b = int(sub_off[e]), int(sub_off[e + 1])
         q, s_, z = orc.quantize_weights(synthetic.fill_weights_host(0, synthetic.TAG_W, int(e), H, 0, 2 * I))
         assert np.array_equal(isum_gu[:, a:b], orc.group_isums(qa_r[stok[a:b]], q, z)), f"gate/up isums, expert {e}"
