@@ -367,6 +367,24 @@ w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t
                          const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp,
                          float *out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): w4a8_moe_ffn with its
+ * intermediates in a fixed scratch array inside the library instead of a caller
+ * workspace.  The array holds w4a8_moe_ffn_noalloc_max_bytes() bytes (64 MiB) on
+ * each GPU the library runs on, from the library's load until the process ends;
+ * layers whose w4a8_moe_ffn_workspace_size exceeds it are rejected with
+ * W4A8_EWORKSPACE (at H=7168, I=2048, E=384, top-8 that is T above 155 tokens).
+ * Arguments, results and errors otherwise as w4a8_moe_ffn; `stream` must belong to
+ * the current device.  The call allocates nothing.  Every call on one GPU uses the
+ * same array, which keeps the last call's contents: calls that overlap on one GPU
+ * (other streams, other host threads) race, and the caller must order them. */
+size_t      w4a8_moe_ffn_noalloc_max_bytes(void);
+w4a8_status w4a8_moe_ffn_noalloc(const float *x, const float *logits, int64_t T, int64_t H, int64_t I,
+                                 int32_t E, int32_t topk,
+                                 const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
+                                 const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp,
+                                 float *out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,6 +136,19 @@ def test_grouped_isums_entry_rejects_before_launch():
     assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 128, 128, 0, f, None) == 0
 
 
+def test_moe_ffn_noalloc_rejects_layers_above_its_scratch():
+    """The entry point that allocates nothing refuses, on the host, a layer whose intermediates
+    exceed its fixed scratch (64 MiB: at H=7168, I=2048, E=384, top-8, T above 155)."""
+    lib = w4.load()
+    f = _fake()
+    assert lib.w4a8_moe_ffn_noalloc_max_bytes() == 64 << 20
+    assert lib.w4a8_moe_ffn_workspace_size(155, 7168, 2048, 384, 8) <= 64 << 20
+    assert lib.w4a8_moe_ffn_workspace_size(156, 7168, 2048, 384, 8) > 64 << 20
+    assert lib.w4a8_moe_ffn_noalloc(f, f, 156, 7168, 2048, 384, 8, f, f, f, f, f, f, f, None) == EWORKSPACE
+    assert b"scratch" in lib.w4a8_last_error()
+    assert lib.w4a8_moe_ffn_noalloc(f, f, 64, 7100, 2048, 384, 8, f, f, f, f, f, f, f, None) == EINVAL
+
+
 def test_moe_ffn_workspace_layout():
     """Parts in enum order, 256-byte aligned, each at least its tensor's size, total = size query."""
     T, H, I, E, k = 64, 7168, 2048, 384, 8

@@ -30,6 +30,7 @@ EXPORTS = (
     "w4a8_moe_route", "w4a8_moe_grouped_gemm", "w4a8_moe_grouped_gemm_debug_isums", "w4a8_silu_mul_quantize",
     "w4a8_moe_combine",
     "w4a8_moe_ffn_workspace_size", "w4a8_moe_ffn_workspace_layout", "w4a8_moe_ffn",
+    "w4a8_moe_ffn_noalloc_max_bytes", "w4a8_moe_ffn_noalloc",
 )
 # order of the parts of the MoE FFN workspace (enum w4a8_moe_ws_part)
 WS_PARTS = ("ids", "w", "offsets", "perm", "row_index", "slot_of_pair", "qa", "a_scale", "gu", "qh",
@@ -81,6 +82,8 @@ def load() -> ctypes.CDLL:
         "w4a8_moe_ffn_workspace_size": (sz, [i64, i64, i64, i32, i32]),
         "w4a8_moe_ffn_workspace_layout": (ctypes.c_int, [i64, i64, i64, i32, i32, p]),
         "w4a8_moe_ffn": (ctypes.c_int, [p, p, i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
+        "w4a8_moe_ffn_noalloc_max_bytes": (sz, []),
+        "w4a8_moe_ffn_noalloc": (ctypes.c_int, [p, p, i64, i64, i64, i32, i32, p, p, p, p, p, p, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -521,3 +524,22 @@ def moe_ffn(x, logits, topk: int, gate_up, down, workspace=None, out=None):
         n = int(np.prod(shape)) * torch.empty((), dtype=dt).element_size()
         inter[name] = workspace[o:o + n].view(dt).view(shape)
     return out, inter
+
+
+def moe_ffn_noalloc(x, logits, topk: int, gate_up, down, out=None):
+    """w4a8_moe_ffn_noalloc: the MoE FFN layer with its intermediates in the library's fixed
+    per-GPU scratch (no allocation inside the call; sizes above the scratch are rejected)."""
+    torch = _torch()
+    T, H = x.shape
+    E = logits.shape[1]
+    I = gate_up[0].shape[1] // 2
+    if out is None:
+        out = _empty((T, H), torch.float32, x)
+    _call("w4a8_moe_ffn_noalloc", _dev_ptr(x), _dev_ptr(logits), T, H, I, E, topk, _dev_ptr(gate_up[0]),
+          _dev_ptr(gate_up[1]), _dev_ptr(gate_up[2]), _dev_ptr(down[0]), _dev_ptr(down[1]), _dev_ptr(down[2]),
+          _dev_ptr(out), _stream(x.device))
+    return out
+
+
+def moe_ffn_noalloc_max_bytes() -> int:
+    return int(load().w4a8_moe_ffn_noalloc_max_bytes())

@@ -518,30 +518,24 @@ w4a8_status check_ffn_sizes(int64_t T, int64_t H, int64_t I, int32_t E, int32_t 
 
 }  // namespace
 
-size_t w4a8_moe_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk) {
-    if (check_ffn_sizes(T, H, I, E, topk) != W4A8_OK) return 0;
+}  // extern "C"
+
+namespace w4a8 {
+
+int64_t moe_ffn_ws_bytes(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk) {
+    if (check_ffn_sizes(T, H, I, E, topk) != W4A8_OK) return -1;
     int64_t off[W4A8_WS_PARTS + 1];
     ws_layout(T, H, I, E, topk, off);
-    return (size_t)off[W4A8_WS_PARTS];
+    return off[W4A8_WS_PARTS];
 }
 
-w4a8_status w4a8_moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk, int64_t *offsets) {
-    clear_error();
-    W4A8_REQUIRE(offsets, W4A8_EINVAL, "null pointer");
-    if (w4a8_status st = check_ffn_sizes(T, H, I, E, topk)) return st;
-    ws_layout(T, H, I, E, topk, offsets);
-    return W4A8_OK;
-}
-
-w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t H, int64_t I, int32_t E,
-                         int32_t topk, const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
-                         const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp, float *out,
-                         void *workspace, size_t ws_bytes, hipStream_t stream) {
-    clear_error();
+w4a8_status moe_ffn_run(const float *x, const float *logits, int64_t T, int64_t H, int64_t I, int32_t E,
+                        int32_t topk, const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
+                        const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp, float *out,
+                        void *workspace, size_t ws_bytes, hipStream_t stream) {
     if (w4a8_status st = check_ffn_sizes(T, H, I, E, topk)) return st;
     W4A8_REQUIRE(workspace && (T == 0 || (x && logits && out)), W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(gu_packed && gu_scale && gu_zp && dn_packed && dn_scale && dn_zp, W4A8_EINVAL, "null weight pointer");
-    W4A8_REQUIRE(((uintptr_t)workspace % kWsAlign) == 0, W4A8_EINVAL, "workspace must be 256-byte aligned");
     W4A8_REQUIRE(aligned16(gu_packed) && aligned16(dn_packed) && (T == 0 || (aligned16(x) && aligned16(out))),
                  W4A8_EINVAL, "x, out and packed weights must be 16-byte aligned");
     int64_t off[W4A8_WS_PARTS + 1];
@@ -579,6 +573,36 @@ w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t
     if ((err = launch_moe_combine(y, sop, w, y + P * H, T, topk, H, out, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: combine");
     return W4A8_OK;
+}
+
+}  // namespace w4a8
+
+extern "C" {
+
+size_t w4a8_moe_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk) {
+    if (check_ffn_sizes(T, H, I, E, topk) != W4A8_OK) return 0;
+    int64_t off[W4A8_WS_PARTS + 1];
+    ws_layout(T, H, I, E, topk, off);
+    return (size_t)off[W4A8_WS_PARTS];
+}
+
+w4a8_status w4a8_moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk, int64_t *offsets) {
+    clear_error();
+    W4A8_REQUIRE(offsets, W4A8_EINVAL, "null pointer");
+    if (w4a8_status st = check_ffn_sizes(T, H, I, E, topk)) return st;
+    ws_layout(T, H, I, E, topk, offsets);
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_moe_ffn(const float *x, const float *logits, int64_t T, int64_t H, int64_t I, int32_t E,
+                         int32_t topk, const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
+                         const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp, float *out,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    W4A8_REQUIRE(workspace, W4A8_EINVAL, "null pointer");
+    W4A8_REQUIRE(((uintptr_t)workspace % kWsAlign) == 0, W4A8_EINVAL, "workspace must be 256-byte aligned");
+    return w4a8::moe_ffn_run(x, logits, T, H, I, E, topk, gu_packed, gu_scale, gu_zp, dn_packed, dn_scale, dn_zp,
+                             out, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

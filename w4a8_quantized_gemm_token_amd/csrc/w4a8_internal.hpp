@@ -68,6 +68,14 @@ hipError_t launch_moe_combine(const float *y, const int32_t *slot_of_pair, const
                               const float *y_shared, int64_t T, int32_t topk, int64_t H, float *out,
                               hipStream_t stream);
 
+// The MoE FFN layer over a caller-provided workspace (validated here, except the
+// workspace's alignment); workspace bytes it needs, -1 for invalid sizes.
+w4a8_status moe_ffn_run(const float *x, const float *logits, int64_t T, int64_t H, int64_t I, int32_t E,
+                        int32_t topk, const uint8_t *gu_packed, const uint16_t *gu_scale, const uint16_t *gu_zp,
+                        const uint8_t *dn_packed, const uint16_t *dn_scale, const uint16_t *dn_zp, float *out,
+                        void *workspace, size_t ws_bytes, hipStream_t stream);
+int64_t moe_ffn_ws_bytes(int64_t T, int64_t H, int64_t I, int32_t E, int32_t topk);
+
 // Streaming-path threshold: the dense GEMM uses the streaming loop for M <= this.
 constexpr int64_t kStreamMaxM = 64;
 
