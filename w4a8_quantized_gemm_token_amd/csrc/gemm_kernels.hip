@@ -1054,6 +1054,272 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
     }
 }
 
+// ------------------------------------------------------------------ tiled loop, three LDS stages
+// The 256x128 workgroup tile for group 128 (large M, and experts with more than 128 slots).
+// Same arithmetic and wave layout as tile2_unit (eight waves of 64x64, 2x2
+// v_mfma_i32_32x32x32_i8 tiles, groups folded into fp32 in increasing g), different data flow:
+//  * activations go straight from memory into LDS (buffer_load ... lds, 16 bytes per lane):
+//    each load instruction fills 1 KB of LDS with 8 whole 128-byte rows of one group, so
+//    the loads are whole lines and use no registers and no LDS write instructions;
+//  * LDS rows are 128 bytes with the 16-byte chunks of row r XOR-swizzled by (r >> 1) & 7
+//    (the rows of a fragment read fall in distinct banks without padding), which leaves room
+//    for three stages: group g is read from stage g % 3 while the activations of group g + 2
+//    stream into stage (g + 2) % 3 and the unpacked weights of group g + 1 are written into
+//    stage (g + 1) % 3, so every load has two iterations to arrive;
+//  * the packed weights come through registers (four threads per column, 16 bytes = 32
+//    codes each) and are unpacked once per workgroup to INT8 (q - zp), one group ahead.
+// One barrier per group.  Rows past the tile's last read row 0 and columns past N read
+// column 0; neither is stored.  Offsets are 32-bit: R * K and N * K / 2 below 2^32.
+constexpr int kT3BM = 256, kT3BN = 128, kT3Threads = 512;
+constexpr int kT3StageA = kT3BM * G128, kT3StageB = kT3BN * G128, kT3Stage = kT3StageA + kT3StageB;
+constexpr int kT3Lds = 3 * kT3Stage;  // 147456 bytes
+
+// LDS has 64 banks of 4 bytes: a 128-bit read serves 16 lanes per cycle, here 16 consecutive
+// rows of one chunk.  Even and odd rows fall in the two halves of a 256-byte bank window, so
+// XOR the chunk index by (row >> 1) & 7: the 8 even rows, and the 8 odd ones, each take 8
+// distinct 16-byte slots.
+__device__ __forceinline__ int t3_sw(int row, int chunk) { return row * G128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// Workgroup barrier for the staged loop, with the waits stated here instead of a full
+// release fence: this wave's LDS writes complete (lgkmcnt 0) and at most VM of its memory
+// loads (the ones issued since the data behind this barrier) still outstanding.  A fence
+// would also wait for the activation loads still streaming into a later stage, which defeats
+// the prefetch.  The empty asm statements keep the compiler from moving LDS accesses across.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(t3_waitcnt(VM, 0));
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+template <bool ISUMS>
+__device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restrict__ qa,
+                                           const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
+                                           int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
+                                           const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
+                                           int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
+                                           int32_t *__restrict__ isums, int64_t M_isums) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t G = K / G128;
+    auto clampg = [&](int64_t g) { return g < G ? g : G - 1; };
+
+    // row scales and validity of the tile's rows (published by the prologue's barriers)
+    __shared__ float row_as[kT3BM];
+    __shared__ int8_t row_ok[kT3BM];
+    if (tid < kT3BM) {
+        int64_t r = -1;
+        if (tid < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + tid] : rows.slot0 + tid;
+        const bool ok = r >= 0 && r < R;
+        row_ok[tid] = ok ? 1 : 0;
+        if (!ISUMS) row_as[tid] = ok ? a_scale[r] : 0.0f;
+    }
+
+    // ---- activation loads: load j (0..3) of wave w fills LDS rows 8 (4 w + j) + [0, 8);
+    // lane l brings row 8 (4 w + j) + (l >> 3), chunk (l & 7) of the swizzled layout
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa);
+    uint32_t aoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rl = 8 * (4 * wave + j) + (lane >> 3);
+        int64_t r = -1;
+        if (rl < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + rl] : rows.slot0 + rl;
+        if (r < 0 || r >= R) r = 0;
+        aoff[j] = (uint32_t)(r * K) + (uint32_t)(((lane & 7) ^ ((rl >> 1) & 7)) << 4);
+    }
+    auto a_dma = [&](int st, int64_t g) {
+        uint8_t *dst = lds + st * kT3Stage + 1024 * (4 * wave);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + 1024 * j), 16, (int)aoff[j],
+                                                     (int)(g * G128), 0, 0);
+    };
+
+    // ---- packed weights: thread t takes column t >> 2, bytes 16 (t & 3) + [0, 16) of a group,
+    // with that column's zero point; and this lane's two output columns' scales
+    const int bcol = tid >> 2, bpart = tid & 3;
+    const int64_t gcol = (n0 + bcol < N) ? n0 + bcol : 0;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (the debug form reads no scales)
+    const uint32_t boff = (uint32_t)(gcol * (K / 2)) + (uint32_t)(16 * bpart);
+    const uint32_t zoff = (uint32_t)(gcol * 2);
+    int64_t scol[2];
+    uint32_t soff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        scol[j] = n0 + wn * 64 + j * 32 + (lane & 31);
+        soff[j] = (uint32_t)((scol[j] < N ? scol[j] : 0) * 2);
+    }
+    struct Slot {
+        v4u rb;
+        uint32_t rz, rs0, rs1;
+    };
+    auto b_load = [&](Slot &x, int64_t g) {
+        x.rb = __builtin_amdgcn_raw_buffer_load_b128(rb, boff, (int)(g * (G128 / 2)), 0);
+        const int gs = (int)(g * N * 2);
+        x.rz = __builtin_amdgcn_raw_buffer_load_b16(rz, zoff, gs, 0);
+        x.rs0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[0], gs, 0);
+        x.rs1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[1], gs, 0);
+    };
+    auto b_store = [&](const Slot &x, int st) {
+        const uint32_t zadd = zp_add_const((uint16_t)x.rz);
+        const uint32_t d4[4] = {x.rb.x, x.rb.y, x.rb.z, x.rb.w};
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) unpack8(d4[k], zadd, w[2 * k], w[2 * k + 1]);
+        uint8_t *B = lds + st * kT3Stage + kT3StageA;
+        *reinterpret_cast<v4u *>(B + t3_sw(bcol, 2 * bpart)) = v4u{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<v4u *>(B + t3_sw(bcol, 2 * bpart + 1)) = v4u{w[4], w[5], w[6], w[7]};
+    };
+
+    // ---- compute: lane l feeds A row (l & 31) / B column (l & 31) of a 32x32 tile with the
+    // 16 bytes of chunk 2 ks + (l >> 5); it holds accumulator rows 8 (r >> 2) + 4 (l >> 5) + (r & 3)
+    // (rows i * 32 + frow of a fragment differ from row frow by a multiple of 16, so the second
+    // fragment's address is the first one's plus an immediate 4096)
+    const int frow = lane & 31, fch = lane >> 5;
+    int aofs[4], bofs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        aofs[ks] = t3_sw(wm * 64 + frow, 2 * ks + fch);
+        bofs[ks] = kT3StageA + t3_sw(wn * 64 + frow, 2 * ks + fch);
+    }
+    float acc[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    float sc[2] = {0.0f, 0.0f}, scn[2];
+    auto group = [&](int st, int64_t g) {
+        const uint8_t *base = lds + st * kT3Stage;
+        v16i d[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            v4i af[2], bf[2];
+            const uint8_t *pa = base + aofs[ks], *pb = base + bofs[ks];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const v4i *>(pa + 4096 * i);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const v4i *>(pb + 4096 * j);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], ks ? d[i][j] : v16i{}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if (ISUMS) {
+                        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                        if (m < rows.rows && scol[j] < N)
+                            isums[(g * M_isums + rows.slot0 + m) * N + scol[j]] = d[i][j][r];
+                    } else {
+                        acc[i][j][r] = fmaf(sc[j], (float)d[i][j][r], acc[i][j][r]);
+                    }
+                }
+    };
+
+    // ---- prologue: groups 0 and 1 in flight, group 0's weights unpacked into stage 0
+    Slot sl[2];
+    a_dma(0, 0);
+    b_load(sl[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    a_dma(1, clampg(1));
+    b_load(sl[1], clampg(1));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(t3_waitcnt(8, 15));  // group 0: all but group 1's 8 loads
+    b_store(sl[0], 0);
+    scn[0] = half_bits_to_float((uint16_t)sl[0].rs0);
+    scn[1] = half_bits_to_float((uint16_t)sl[0].rs1);
+    stage_barrier<8>();
+
+    // ---- main loop: iteration g computes group g from stage g % 3; register slot g & 1 held
+    // group g's weights (unpacked last iteration) and now takes group g + 2's.  Unrolled by
+    // two so the slots stay in registers.  Per iteration each wave issues 4 activation loads
+    // of group g + 2 and then 4 weight, zero-point and scale loads; before group g + 1's
+    // weights are unpacked and the barrier passed, group g + 1's activations (issued one
+    // iteration earlier, with 8 loads after them) are waited for.
+    int st0 = 0, st1 = 1, st2 = 2;
+    auto body = [&](auto parc, int64_t g) {
+        constexpr int PAR = decltype(parc)::value;
+        Slot &fill = sl[PAR];
+        const Slot &next = sl[PAR ^ 1];
+        sc[0] = scn[0];
+        sc[1] = scn[1];
+        __asm__ volatile("" ::: "memory");
+        a_dma(st2, clampg(g + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        b_load(fill, clampg(g + 2));
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        group(st0, g);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(t3_waitcnt(8, 15));
+        b_store(next, st1);
+        scn[0] = half_bits_to_float((uint16_t)next.rs0);
+        scn[1] = half_bits_to_float((uint16_t)next.rs1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) __asm__ volatile("" : "+v"(scn[h]));
+        stage_barrier<8>();
+        const int t = st0;
+        st0 = st1;
+        st1 = st2;
+        st2 = t;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int64_t g = 0;
+    for (; g + 1 < G; g += 2) {
+        body(I0{}, g);
+        body(I1{}, g + 1);
+    }
+    if (g < G) body(I0{}, g);
+    __builtin_amdgcn_s_waitcnt(0);  // the last (unused) prefetches
+
+    if (!ISUMS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                if (m < rows.rows && row_ok[m]) {
+                    const int64_t slot = rows.slot0 + m;
+                    const float as = row_as[m];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
+                }
+            }
+    }
+}
+
+template <bool ISUMS>
+__global__ __launch_bounds__(kT3Threads) void gemm_tiled3_kernel(const int8_t *__restrict__ qa,
+                                                                 const float *__restrict__ a_scale, int64_t M,
+                                                                 int64_t K, const uint8_t *__restrict__ packed,
+                                                                 const uint16_t *__restrict__ scale,
+                                                                 const uint16_t *__restrict__ zp, int64_t N,
+                                                                 float *__restrict__ out,
+                                                                 int32_t *__restrict__ isums) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    const int64_t mt = (M + kT3BM - 1) / kT3BM, nt = (N + kT3BN - 1) / kT3BN;
+    int64_t tm, tn;
+    panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
+    const int64_t m0 = tm * kT3BM;
+    const int rows = (int)((M - m0) < kT3BM ? (M - m0) : kT3BM);
+    tile3_unit<ISUMS>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT3BN, out, N,
+                      isums, M);
+}
+
 template <int WM, int WN, bool ISUMS, int GS>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *__restrict__ qa,
                                                                   const float *__restrict__ a_scale, int64_t M,
@@ -1575,6 +1841,40 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
     }
 }
 
+// Experts with more than cmin slots in 256-row tiles of the three-stage loop (the same unit
+// order as grouped_tiled_kernel).
+template <bool ISUMS>
+__global__ __launch_bounds__(kT3Threads) void grouped_tiled3_kernel(
+    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
+    const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
+    float *__restrict__ out, int32_t *__restrict__ isums, int64_t cmin) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ int64_t pfx[kMaxExperts + 1];
+    const int64_t ntn = (N + kT3BN - 1) / kT3BN;
+    const int64_t total = expert_prefix(E, pfx, kT3Threads, [&](int e) -> int64_t {
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        return c > cmin ? ((c + kT3BM - 1) / kT3BM) * ntn : 0;
+    });
+    const int64_t G = K / G128;
+    const int64_t nb = gridDim.x;
+    const bool by_xcd = nb % 8 == 0;
+    const int64_t lane_u = by_xcd ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    for (int64_t u = lane_u; u < total; u += nb) {
+        const int e = find_expert(pfx, E, u);
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        const int64_t mt = (c + kT3BM - 1) / kT3BM;
+        const int64_t local = u - pfx[e];
+        const int64_t tm = local % mt, tn = local / mt;
+        const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * kT3BM;
+        const int rows = (int)((c - tm * kT3BM) < kT3BM ? (c - tm * kT3BM) : kT3BM);
+        tile3_unit<ISUMS>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K, packed + (int64_t)e * N * (K / 2),
+                          (ISUMS ? nullptr : scale + (int64_t)e * G * N), zp + (int64_t)e * G * N, N, tn * kT3BN,
+                          out, N, isums, max_slots);
+        __syncthreads();  // the next unit reuses the LDS stages and row tables
+    }
+}
+
 template <int MT, int U, int SPLIT>
 hipError_t launch_stream2_t(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                             const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
@@ -1632,6 +1932,30 @@ hipError_t launch_tiled(const int8_t *qa, const float *a_scale, int64_t M, int64
         hipLaunchKernelGGL((gemm_tiled_kernel<WM, WN, false, GS>), grid, block, lds, stream, qa, a_scale, M, K, packed,
                            scale, zp, N, out, isums);
     }
+    return hipGetLastError();
+}
+
+// The three-stage 256x128 loop, when its 32-bit offsets reach every operand.
+bool tiled3_fits(int64_t M, int64_t K, int64_t N) {
+    return M * K < (1ll << 32) && N * (K / 2) < (1ll << 32) && (K / G128) * N * 2 < (1ll << 31);
+}
+
+hipError_t launch_tiled3(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                         const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
+                         hipStream_t stream) {
+    const int64_t tiles = ((M + kT3BM - 1) / kT3BM) * ((N + kT3BN - 1) / kT3BN);
+    const dim3 grid((uint32_t)tiles), block(kT3Threads);
+#define W4A8_T3(IS)                                                                                                 \
+    do {                                                                                                            \
+        if (hipFuncSetAttribute((const void *)gemm_tiled3_kernel<IS>, hipFuncAttributeMaxDynamicSharedMemorySize,   \
+                                kT3Lds) != hipSuccess)                                                              \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((gemm_tiled3_kernel<IS>), grid, block, kT3Lds, stream, qa, a_scale, M, K, packed, scale, \
+                           zp, N, out, isums);                                                                      \
+    } while (0)
+    if (isums) W4A8_T3(true);
+    else W4A8_T3(false);
+#undef W4A8_T3
     return hipGetLastError();
 }
 
@@ -1757,8 +2081,11 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
 #undef W4A8_STREAM
 #undef W4A8_STREAM_U
     } else {
-        if (path == 4 || (path == 2 && M > 128))
+        if (path == 4 || (path == 2 && M > 128)) {
+            if (tiled3_fits(M, K, N))
+                return launch_tiled3(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
             return launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        }
         return launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     }
     return hipGetLastError();
@@ -1774,6 +2101,7 @@ hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64
     if (group == 256)
         return wide ? launch_tiled<4, 2, 256>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
                     : launch_tiled<2, 2, 256>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+    if (wide && tiled3_fits(M, K, N)) return launch_tiled3(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
     return wide ? launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
                 : launch_tiled<2, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
 }
@@ -1880,6 +2208,21 @@ static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, i
         hipError_t err = launch_grouped_tiled_s<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
                                                       zp, N, max_slots, out, isums, cmin, 128, cus, stream);
         if (err != hipSuccess || max_slots <= 128) return err;
+    }
+    if (tiled3_fits(R, K, N)) {
+#define W4A8_GT3(IS)                                                                                                \
+    do {                                                                                                            \
+        if (hipFuncSetAttribute((const void *)grouped_tiled3_kernel<IS>,                                            \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kT3Lds) != hipSuccess)                  \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((grouped_tiled3_kernel<IS>), dim3((uint32_t)cus), dim3(kT3Threads), kT3Lds, stream, qa,  \
+                           a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums,  \
+                           (int64_t)128);                                                                           \
+    } while (0)
+        if (isums) W4A8_GT3(true);
+        else W4A8_GT3(false);
+#undef W4A8_GT3
+        return hipGetLastError();
     }
     return launch_grouped_tiled_s<4, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
                                         max_slots, out, isums, 128, INT64_MAX, cus, stream);
