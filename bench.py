@@ -33,10 +33,10 @@ K_DEC, N_DEC, M_DEC = 8192, 28672, (1, 8, 16)
 GROUP = 128
 
 
-def dense_bytes(M, N, K):
+def dense_bytes(M, N, K, group=GROUP):
     """Algorithmic HBM bytes of one W4A8 GEMM launch: packed weights (K/2 per column),
-    fp16 scale + zp (4 B per 128 weights), INT8 activations, fp32 row scales, fp32 output."""
-    return N * K // 2 + 4 * N * (K // GROUP) + M * K + 4 * M + 4 * M * N
+    fp16 scale + zp (4 B per group), INT8 activations, fp32 row scales, fp32 output."""
+    return N * K // 2 + 4 * N * (K // group) + M * K + 4 * M + 4 * M * N
 
 
 def quant_bytes(M, K):
@@ -400,10 +400,51 @@ def quant_variants(torch, w4, synthetic):
     return res
 
 
-def secondary(torch, w4, synthetic):
-    """Prefill (M=4096, K=N=8192) TOPS, MoE layer times and the smoothing figures; context."""
+def decode_group_sizes(torch, w4, synthetic, copies, reps=50):
+    """The decode GEMM (K=8192, N=28672, M = 1, 8, 16, standard layout) at group 64 and 256:
+    per M, one event pair around `reps` back-to-back prepared launches that rotate `copies`
+    weight copies (device packer, outlier weights)."""
     dev = torch.device("cuda:0")
-    out = {"prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
+    stream = torch.cuda.current_stream()
+    x = torch.from_numpy(synthetic.activations_with_outlier_channels(0, 16, K_DEC)).to(dev)
+    res = {}
+    for group in (64, 256):
+        W = torch.empty((N_DEC, K_DEC), dtype=torch.float32, device=dev)
+        synthetic.fill_weights_device(W, 0, synthetic.TAG_W, 0, K_DEC, 0, "outliers")
+        layers = [w4.pack_weights_device(W, group=group)]
+        del W
+        for _ in range(copies - 1):
+            layers.append(tuple(t.clone() for t in layers[0]))
+        per_m = {}
+        for M in M_DEC:
+            qa, sc = w4.quantize_act(x[:M].contiguous())
+            o = torch.empty((M, N_DEC), dtype=torch.float32, device=dev)
+            launches = [w4.prepare_gemm(qa, sc, *layers[i], o, group=group) for i in range(copies)]
+            for launch in launches * 4:
+                launch()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for i in range(reps):
+                launches[i % copies]()
+            e.record(stream)
+            e.synchronize()
+            ms = s.elapsed_time(e) / reps
+            per_m[str(M)] = {"gemm_us": round(ms * 1e3, 2),
+                             "GB/s": round(dense_bytes(M, N_DEC, K_DEC, group) / (ms * 1e-3) / 1e9, 1),
+                             "TOPS": round(2 * M * N_DEC * K_DEC / (ms * 1e-3) / 1e12, 3)}
+        res[f"decode_K8192_N28672_group{group}_per_M"] = per_m
+        del layers
+        torch.cuda.empty_cache()
+    return res
+
+
+def secondary(torch, w4, synthetic, copies):
+    """Prefill (M=4096, K=N=8192) TOPS, decode at group 64 and 256, MoE layer times and the
+    smoothing figures; context."""
+    dev = torch.device("cuda:0")
+    out = {**decode_group_sizes(torch, w4, synthetic, copies),
+           "prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
            "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
            "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
            "quant_variants_K8192_N4096_M16": quant_variants(torch, w4, synthetic)}
@@ -563,7 +604,8 @@ def main():
         "decode_per_M": per_m,
     }
     if not args.no_secondary:
-        result["secondary"] = {"decode_standard_layout_per_M": std_per_m, **secondary(torch, w4, synthetic)}
+        result["secondary"] = {"decode_standard_layout_per_M": std_per_m,
+                               **secondary(torch, w4, synthetic, args.copies)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synthetic)
     print(json.dumps(result), flush=True)

@@ -39,8 +39,9 @@
  *     are validated on the host before anything is launched; a rejected call
  *     launches nothing and writes nothing.  w4a8_last_error() then describes
  *     the problem (thread-local text, valid until the next call on the thread).
- *   - group is 128 unless an entry point says otherwise (the host packers and
- *     w4a8_gemm / w4a8_gemm_path / w4a8_gemm_debug_isums also take 64 and 256);
+ *   - group is 128 unless an entry point says otherwise (the packers, the GEMM
+ *     and expert-grouped GEMM entry points and their debug forms also take 64
+ *     and 256; the tile-major layout and the MoE layer take 128 only);
  *     any other value is W4A8_EUNSUPPORTED, with no fallback.  K must be a
  *     multiple of 128 (W4A8_EINVAL; pad K at conversion time).
  *   - Device pointers (marked "device") must be device memory owned by the
@@ -87,8 +88,8 @@ const char *w4a8_last_error(void);
  * scale/zero point per group, exactly as stated at the top of this file
  * ([p2 §2.1, §2.2]).  All pointers are host memory owned by the caller.
  * A group whose scale rounds to 0 in fp16 stores scale 1.0 and zp 0.
- * group is 128, or 64 or 256 ([p2 §4.3] weighs the three) for weights that the
- * tiled GEMM loop will take (scale/zp then [K/group][N]).
+ * group is 128, 64 or 256 ([p2 §4.3] weighs the three); scale/zp are then
+ * [K/group][N].
  * Errors: W4A8_EINVAL for null pointers, N <= 0, K <= 0, K % 128 != 0,
  * K % group != 0, non-finite weights, or a group scale above the largest finite
  * fp16; W4A8_EUNSUPPORTED for another group size. */
@@ -119,7 +120,8 @@ w4a8_status w4a8_pack_weights_ex(const float *W, int64_t N, int64_t K, int32_t g
  * host.  Bit-identical to the host packer.  Device memory only.  Errors as the
  * host packer for sizes; non-finite weights or fp16 scale overflow cannot be
  * reported from the device: such groups get scale 0x7C00 (inf) and must be
- * checked by the caller if the input is untrusted. */
+ * checked by the caller if the input is untrusted.  W 8-byte aligned (16-byte
+ * for group 256), packed 2-byte aligned. */
 w4a8_status w4a8_pack_weights_device(const float *W, int64_t N, int64_t K, int32_t group,
                                      uint8_t *packed, uint16_t *scale, uint16_t *zp,
                                      hipStream_t stream);
@@ -169,7 +171,8 @@ w4a8_status w4a8_smooth_factors(const float *ax, const float *aw, int64_t K, dou
 
 /* Device, asynchronous.  w4a8_pack_weights_device of the smoothed weights
  * fp32(W[n][k] * s[k]) (s: device fp32 [K]); the smoothed matrix is not stored.
- * W and s 8-byte aligned.  Errors as w4a8_pack_weights_device. */
+ * W and s 8-byte aligned (16-byte for group 256).  Errors as
+ * w4a8_pack_weights_device. */
 w4a8_status w4a8_pack_weights_device_smooth(const float *W, int64_t N, int64_t K, int32_t group,
                                             const float *s, uint8_t *packed, uint16_t *scale,
                                             uint16_t *zp, hipStream_t stream);
@@ -190,22 +193,23 @@ w4a8_status w4a8_quantize_act_smooth(const float *x, int64_t M, int64_t K, int64
  * are widened to INT8 inside the kernel, never in memory).  Small M takes an
  * HBM-streaming path, large M an LDS-tiled MFMA path; both give the same
  * per-group int32 sums.  The fp32 epilogue adds groups in increasing g.
- * Group sizes 64 and 256 (weights from the host packer) run on the tiled loop
- * for every M: 256 keeps one int32 sum over its two 128-k stages, 64 takes two
- * sums per stage.
+ * Group sizes 64 and 256 take the decode loop for 1 <= M <= 16 when K % 256 == 0
+ * (and its size limits hold) and the tiled loop otherwise: 256 keeps one int32
+ * sum over its two 128-k halves, 64 takes two sums per half.
  * Errors: W4A8_EINVAL (null, M < 0, N <= 0, K <= 0, K % 128, K % group,
  * N % 16 != 0, misalignment), W4A8_EUNSUPPORTED (group not 64, 128 or 256; 64
- * or 256 with the streaming loop forced).  M == 0 is a no-op. */
+ * or 256 with path 1 forced outside the decode loop's range).  M == 0 is a
+ * no-op. */
 w4a8_status w4a8_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
                       const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
                       int64_t N, int32_t group, float *out, hipStream_t stream);
 
 /* Device, test/debug aid.  Same main loop as w4a8_gemm, but instead of the fp32
- * epilogue it stores every per-group int32 sum: isums[K/128][M][N] ([p2 §5.4]).
+ * epilogue it stores every per-group int32 sum: isums[K/group][M][N] ([p2 §5.4]).
  * `path` selects the main loop: 0 = the one w4a8_gemm would pick for M,
- * 1 = the small-M streaming loop (M <= 64), 2 = the large-M tiled loop with the
- * tile w4a8_gemm would pick, 3 = tiled with 128x128 workgroup tiles,
- * 4 = tiled with 256x128 workgroup tiles. */
+ * 1 = the small-M streaming loop (M <= 64; for group 64 or 256, the decode loop,
+ * M <= 16), 2 = the large-M tiled loop with the tile w4a8_gemm would pick,
+ * 3 = tiled with 128x128 workgroup tiles, 4 = tiled with 256x128 workgroup tiles. */
 w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K,
                                   const uint8_t *packed, const uint16_t *zp, int64_t N,
                                   int32_t group, int32_t path, int32_t *isums, hipStream_t stream);
@@ -291,9 +295,10 @@ w4a8_status w4a8_moe_route(const float *logits, int64_t T, int32_t E, int32_t to
  * pass per 64 rows (17 to 128), or the tiled loop (more); a loop is launched only
  * when max_slots allows an expert of its size.  (When K/128 is not a multiple of
  * 4, or below 8, the streaming loop takes up to 64 slots and the tiled loop the
- * rest.)
+ * rest.)  Group sizes 64 and 256: the 16-row loop up to 16 slots (when K/128 is
+ * a multiple of 4), the tiled loop above.
  *   qa [R][K] i8 and a_scale [R] (R = rows of the activation matrix),
- *   packed [E][N][K/2], scale/zp [E][K/128][N], out [max_slots][N].
+ *   packed [E][N][K/2], scale/zp [E][K/group][N], out [max_slots][N].
  * The caller guarantees expert_offsets[E] <= max_slots and row_index[s] < R
  * (the kernel clamps slots to max_slots and skips slots whose row_index is
  * outside [0, R)).  Errors as w4a8_gemm, plus E <= 0. */
@@ -309,10 +314,10 @@ w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_
  * epilogue every per-group int32 sum is stored ([p2 §3.2, §5.4]: INT8 products
  * accumulated in int32 per group):
  *     isums[g][s][n] = sum_{k in group g} qa[row_index[s]][k] * (q_e[n][k] - zp_e[g][n])
- * for g < K/128, slots s < max_slots of expert e, n < N; isums is device int32
- * [K/128][max_slots][N], caller-owned.  Slots past expert_offsets[E] are not
+ * for g < K/group, slots s < max_slots of expert e, n < N; isums is device int32
+ * [K/group][max_slots][N], caller-owned.  Slots past expert_offsets[E] are not
  * written; slots whose row_index is outside [0, R) get unspecified values.  No
- * scale array is read.  Errors as w4a8_moe_grouped_gemm (group must be 128). */
+ * scale array is read.  Errors as w4a8_moe_grouped_gemm. */
 w4a8_status w4a8_moe_grouped_gemm_debug_isums(const int8_t *qa, int64_t R, const int32_t *row_index,
                                               const int32_t *expert_offsets, int32_t E, int64_t K,
                                               const uint8_t *packed, const uint16_t *zp, int64_t N,

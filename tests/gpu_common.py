@@ -25,29 +25,30 @@ def to_host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def device_layer(seed, tag, sub, N, K, mode="plain"):
+def device_layer(seed, tag, sub, N, K, mode="plain", group=128):
     """Packed weights of one [N][K] layer built on the device: the GPU filler writes
-    the fp32 weights, the library's device packer quantizes them."""
+    the fp32 weights, the library's device packer quantizes them (groups of `group`)."""
     import torch
     import w4a8_quantized_gemm_token_amd as w4
     W = torch.empty((N, K), dtype=torch.float32, device=cuda())
     synthetic.fill_weights_device(W, seed, tag, sub, K, 0, mode)
-    packed, scale, zp = w4.pack_weights_device(W)
+    packed, scale, zp = w4.pack_weights_device(W, group=group)
     del W
     return packed, scale, zp
 
 
-def device_experts(seed, tag, E, N, K, sub0=0, out=None):
-    """Stacked expert weights [E][N][K/2], [E][G][N] x2, expert e drawn from sub-stream sub0 + e."""
+def device_experts(seed, tag, E, N, K, sub0=0, out=None, group=128):
+    """Stacked expert weights [E][N][K/2], [E][K/group][N] x2, expert e drawn from sub-stream sub0 + e."""
     import w4a8_quantized_gemm_token_amd as w4
     return w4.pack_experts_device(
-        E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, sub0 + e, K, 0, "plain"), cuda(), out=out)
+        E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, sub0 + e, K, 0, "plain"), cuda(),
+        group=group, out=out)
 
 
-def oracle_columns(orc, seed, tag, sub, K, cols, mode="plain"):
+def oracle_columns(orc, seed, tag, sub, K, cols, mode="plain", group=128):
     """Oracle quantization of the weight rows (= output columns) `cols` of a layer."""
     W = synthetic.weight_rows_host(seed, tag, sub, K, cols, mode)
-    return orc.quantize_weights(W)
+    return orc.quantize_weights(W, group)
 
 
 def check_close(out, ref, mag, what=""):

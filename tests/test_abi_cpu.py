@@ -50,11 +50,14 @@ def test_validation_rejects_before_launch():
     # group sizes other than 64, 128, 256: unsupported, never a silent fallback
     assert lib.w4a8_gemm(f, f, 4, 256, f, f, f, 128, 32, f, None) == EUNSUPPORTED
     assert b"group" in lib.w4a8_last_error()
-    # 64 and 256 run on the tiled loop only; the expert loops and the device packer take 128
-    assert lib.w4a8_gemm_path(f, f, 4, 256, f, f, f, 128, 64, 1, f, None) == EUNSUPPORTED
+    # 64 and 256 take the decode loop (path 1) only for M <= 16 and K % 256 == 0
+    assert lib.w4a8_gemm_path(f, f, 17, 256, f, f, f, 128, 64, 1, f, None) == EUNSUPPORTED
+    assert lib.w4a8_gemm_path(f, f, 4, 384, f, f, f, 128, 64, 1, f, None) == EUNSUPPORTED
     assert lib.w4a8_gemm_path(f, f, 4, 384, f, f, f, 128, 256, 2, f, None) == EINVAL   # K % 256
     assert lib.w4a8_gemm_path(f, f, 0, 512, f, f, f, 128, 256, 0, f, None) == 0        # M == 0: no launch
-    assert lib.w4a8_pack_weights_device(f, 16, 256, 64, f, f, f, None) == EUNSUPPORTED
+    assert lib.w4a8_pack_weights_device(f, 16, 256, 32, f, f, f, None) == EUNSUPPORTED
+    assert lib.w4a8_pack_weights_device(_fake(4104), 16, 256, 256, f, f, f, None) == EINVAL  # 16-byte W
+    assert lib.w4a8_pack_weights_device(f, 16, 384, 256, f, f, f, None) == EINVAL            # K % group
     # K not a multiple of 128
     assert lib.w4a8_gemm(f, f, 4, 200, f, f, f, 128, 128, f, None) == EINVAL
     # N not a multiple of 16
@@ -84,7 +87,8 @@ def test_validation_rejects_before_launch():
     # grouped gemm
     assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, None, 8, 256, f, f, f, 128, 128, 16, f, None) == EINVAL
     assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 0, 256, f, f, f, 128, 128, 16, f, None) == EINVAL
-    assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 8, 256, f, f, f, 128, 256, 16, f, None) == EUNSUPPORTED
+    assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 8, 256, f, f, f, 128, 32, 16, f, None) == EUNSUPPORTED
+    assert lib.w4a8_moe_grouped_gemm(f, f, 4, None, f, 8, 384, f, f, f, 128, 256, 16, f, None) == EINVAL
     # silu + requant, combine
     assert lib.w4a8_silu_mul_quantize(f, 4, 100, f, f, None, None) == EINVAL
     assert lib.w4a8_moe_combine(f, f, f, None, 4, 1, 102, f, None) == EINVAL
@@ -113,7 +117,8 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_quantize_act_smooth(f, 4, 200, 256, f, f, f, None) == EINVAL
     assert lib.w4a8_quantize_act_smooth(f, 0, 256, 256, f, f, f, None) == 0
     assert lib.w4a8_pack_weights_device_smooth(f, 16, 256, 128, _fake(4100), f, f, f, None) == EINVAL
-    assert lib.w4a8_pack_weights_device_smooth(f, 16, 256, 64, f, f, f, f, None) == EUNSUPPORTED
+    assert lib.w4a8_pack_weights_device_smooth(f, 16, 256, 32, f, f, f, f, None) == EUNSUPPORTED
+    assert lib.w4a8_pack_weights_device_smooth(f, 16, 256, 256, _fake(4104), f, f, f, None) == EINVAL
     # MoE FFN layer: sizes, workspace alignment and size
     need = lib.w4a8_moe_ffn_workspace_size(64, 7168, 2048, 384, 8)
     assert need > 0
@@ -129,7 +134,8 @@ def test_grouped_isums_entry_rejects_before_launch():
     lib = w4.load()
     f = _fake()
     # (qa, R, row_index, offsets, E, K, packed, zp, N, group, max_slots, isums, stream)
-    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 128, 64, 8, f, None) == EUNSUPPORTED
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 128, 32, 8, f, None) == EUNSUPPORTED
+    assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 384, f, f, 128, 256, 8, f, None) == EINVAL
     assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, None, 4, 256, f, f, 128, 128, 8, f, None) == EINVAL
     assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 0, 256, f, f, 128, 128, 8, f, None) == EINVAL
     assert lib.w4a8_moe_grouped_gemm_debug_isums(f, 8, f, f, 4, 256, f, f, 120, 128, 8, f, None) == EINVAL

@@ -308,7 +308,7 @@ def prepare_gemm(qa, a_scale, packed, scale, zp, out, group: int = GROUP) -> Lau
 
 
 def gemm_debug_isums(qa, packed, zp, path: int = 0, group: int = GROUP):
-    """int32 [K/128][M][N] per-group integer sums (test aid)."""
+    """int32 [K/group][M][N] per-group integer sums (test aid)."""
     torch = _torch()
     M, K = qa.shape
     N = packed.shape[0]
@@ -400,7 +400,7 @@ def moe_grouped_gemm(qa, a_scale, row_index, offsets, packed, scale, zp, max_slo
 
 
 def moe_grouped_gemm_debug_isums(qa, row_index, offsets, packed, zp, max_slots: int, group: int = GROUP):
-    """int32 [K/128][max_slots][N] per-group integer sums of every slot (test aid)."""
+    """int32 [K/group][max_slots][N] per-group integer sums of every slot (test aid)."""
     torch = _torch()
     R, K = qa.shape
     E, N = packed.shape[0], packed.shape[1]

@@ -239,9 +239,11 @@ w4a8_status w4a8_pack_weights_device(const float *W, int64_t N, int64_t K, int32
     clear_error();
     W4A8_REQUIRE(W && packed && scale && zp, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
-    if (w4a8_status st = check_group(group, K)) return st;
-    W4A8_REQUIRE(((uintptr_t)W & 7u) == 0, W4A8_EINVAL, "W must be 8-byte aligned");
-    return hip_status(launch_pack_weights(W, N, K, nullptr, packed, scale, zp, stream), "pack_weights_device launch");
+    if (w4a8_status st = check_group_any(group, K)) return st;
+    W4A8_REQUIRE(((uintptr_t)W & (group == 256 ? 15u : 7u)) == 0 && ((uintptr_t)packed & 1u) == 0, W4A8_EINVAL,
+                 "W must be 8-byte aligned (16 for group 256) and packed 2-byte aligned");
+    return hip_status(launch_pack_weights(W, N, K, group, nullptr, packed, scale, zp, stream),
+                      "pack_weights_device launch");
 }
 
 w4a8_status w4a8_pack_weights_device_smooth(const float *W, int64_t N, int64_t K, int32_t group, const float *s,
@@ -249,9 +251,12 @@ w4a8_status w4a8_pack_weights_device_smooth(const float *W, int64_t N, int64_t K
     clear_error();
     W4A8_REQUIRE(W && s && packed && scale && zp, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(N > 0, W4A8_EINVAL, "N=%lld must be positive", (long long)N);
-    if (w4a8_status st = check_group(group, K)) return st;
-    W4A8_REQUIRE(((uintptr_t)W & 7u) == 0 && ((uintptr_t)s & 7u) == 0, W4A8_EINVAL, "W and s must be 8-byte aligned");
-    return hip_status(launch_pack_weights(W, N, K, s, packed, scale, zp, stream), "pack_weights_device_smooth launch");
+    if (w4a8_status st = check_group_any(group, K)) return st;
+    const uintptr_t am = group == 256 ? 15u : 7u;
+    W4A8_REQUIRE(((uintptr_t)W & am) == 0 && ((uintptr_t)s & am) == 0 && ((uintptr_t)packed & 1u) == 0, W4A8_EINVAL,
+                 "W and s must be 8-byte aligned (16 for group 256) and packed 2-byte aligned");
+    return hip_status(launch_pack_weights(W, N, K, group, s, packed, scale, zp, stream),
+                      "pack_weights_device_smooth launch");
 }
 
 w4a8_status w4a8_channel_absmax(const float *A, int64_t rows, int64_t K, int64_t lda, float *out, hipStream_t stream) {
@@ -328,9 +333,11 @@ static w4a8_status gemm_common(const int8_t *qa, const float *a_scale, int64_t M
                                float *out, int32_t *isums, hipStream_t stream) {
     W4A8_REQUIRE(path >= 0 && path <= 4, W4A8_EINVAL, "path=%d must be in [0, 4]", (int)path);
     if (group != W4A8_GROUP) {
-        // group sizes 64 and 256 run on the tiled loop, for any M
-        if (path == 0) path = 2;
-        W4A8_REQUIRE(path >= 2, W4A8_EUNSUPPORTED, "group size %d runs on the tiled loop only (path 0, 2, 3 or 4)",
+        // group sizes 64 and 256: the decode loop for M <= 16 (K a multiple of 256), the
+        // tiled loop otherwise
+        if (path == 0) path = decode_group_fits(M, K, N) ? 1 : 2;
+        W4A8_REQUIRE(path != 1 || M == 0 || decode_group_fits(M, K, N), W4A8_EUNSUPPORTED,
+                     "group size %d takes the decode loop (path 1) only for 1 <= M <= 16 and K %% 256 == 0",
                      (int)group);
         if (M == 0) return W4A8_OK;
         return hip_status(launch_gemm_tiled_group(qa, a_scale, M, K, packed, scale, zp, N, group, path, out, isums,
@@ -422,13 +429,12 @@ w4a8_status w4a8_moe_grouped_gemm(const int8_t *qa, const float *a_scale, int64_
                                   int64_t max_slots, float *out, hipStream_t stream) {
     clear_error();
     if (w4a8_status st = check_gemm(qa, R, K, packed, scale, zp, N, group, out)) return st;
-    if (w4a8_status st = check_group(group, K)) return st;  // the expert loops take 128 only
     W4A8_REQUIRE(a_scale && scale && expert_offsets, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
     W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");
     if (max_slots == 0 || R == 0) return W4A8_OK;
     return hip_status(launch_grouped_gemm(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
-                                          max_slots, max_slots, out, nullptr, stream),
+                                          max_slots, max_slots, out, nullptr, group, stream),
                       "grouped_gemm launch");
 }
 
@@ -438,13 +444,12 @@ w4a8_status w4a8_moe_grouped_gemm_debug_isums(const int8_t *qa, int64_t R, const
                                               int64_t max_slots, int32_t *isums, hipStream_t stream) {
     clear_error();
     if (w4a8_status st = check_gemm(qa, R, K, packed, nullptr, zp, N, group, isums)) return st;
-    if (w4a8_status st = check_group(group, K)) return st;
     W4A8_REQUIRE(expert_offsets, W4A8_EINVAL, "null pointer");
     W4A8_REQUIRE(E > 0 && E <= 1024, W4A8_EINVAL, "E=%d must be in [1, 1024]", (int)E);
     W4A8_REQUIRE(max_slots >= 0 && max_slots < (1ll << 31), W4A8_EINVAL, "bad max_slots");
     if (max_slots == 0 || R == 0) return W4A8_OK;
     return hip_status(launch_grouped_gemm(qa, nullptr, R, row_index, expert_offsets, E, K, packed, nullptr, zp, N,
-                                          max_slots, max_slots, nullptr, isums, stream),
+                                          max_slots, max_slots, nullptr, isums, group, stream),
                       "grouped_gemm_debug_isums launch");
 }
 
@@ -563,12 +568,12 @@ w4a8_status moe_ffn_run(const float *x, const float *logits, int64_t T, int64_t 
         return hip_status(err, "moe_ffn: quantize");
     // top-k picks distinct experts per token, so no expert (the shared one included) gets more than T slots
     if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S, T,
-                                   gu, nullptr, stream)) != hipSuccess)
+                                   gu, nullptr, W4A8_GROUP, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: gate/up grouped GEMM");
     if ((err = launch_silu_mul_quantize(gu, S, I, qh, h_scale, nullptr, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: silu*up requant");
     if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E + 1, I, dn_packed, dn_scale, dn_zp, H, S, T, y,
-                                   nullptr, stream)) != hipSuccess)
+                                   nullptr, W4A8_GROUP, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: down grouped GEMM");
     if ((err = launch_moe_combine(y, sop, w, y + P * H, T, topk, H, out, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: combine");

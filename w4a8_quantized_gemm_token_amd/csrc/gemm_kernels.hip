@@ -477,7 +477,13 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
 // and the -zp operand of the zero-point MFMA is one byte replicated (one v_perm).
 constexpr int64_t kTmBlock = 2 * 1024 + 128;
 
-template <int U, int SPLIT, bool ISUMS, bool TM, typename Stage, typename Store, typename IStore>
+// Group size GS (standard layout only; the tile-major array is defined for 128): a window
+// always covers 256 k.  GS = 256: the window is one group, its two 128-k halves add into the
+// same int32 sums, one fp32 fold per window.  GS = 64: each 128-k half holds two groups, k
+// 0..63 in lanes kq < 2 and k 64..127 in lanes kq >= 2, so each half runs its MFMAs twice,
+// with the A operand zeroed in the other lanes, and folds the two sums with their own scales;
+// the -zp operand of each lane is its own group's.
+template <int U, int SPLIT, bool ISUMS, bool TM, int GS, typename Stage, typename Store, typename IStore>
 __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M, int64_t K,
                                           const uint8_t *__restrict__ wpk, const uint16_t *__restrict__ wsc,
                                           const uint16_t *__restrict__ wzp, int64_t N, int64_t t0, int64_t t1,
@@ -508,10 +514,21 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wpk), (short)0, (int)(uint32_t)wbytes, 0x00020000);
     const uint32_t colbyte = TM ? (uint32_t)(16 * lane) : (uint32_t)((lane & 7) * (K / 2) + lchunk);
     const uint32_t szbyte = 2048u + 8u * (uint32_t)(lane & 15);  // TM: this lane's column's words
-    // (the debug form stores int32 sums and reads no scales: every lane reads zero points)
-    const uint16_t *szbase = TM ? nullptr : ((kq < 2 && !ISUMS) ? wsc : wzp) + (kq & 1) * N + (lane & 15);
+    static_assert(GS == 128 || (!TM && (GS == 64 || GS == 256)), "group size");
+    // Standard layout, fp16 words per window and column, one per lane (spread with ds_bpermute):
+    //  GS 128: lanes kq = 0..3 read scale[2w], scale[2w+1], zp[2w], zp[2w+1]
+    //  GS 256: lanes kq < 2 read scale[w], lanes kq >= 2 read zp[w]
+    //  GS 64:  lane kq reads scale[4w + kq] (rsz) and zp[4w + kq] (rszb)
+    // (the debug form stores int32 sums and reads no scales: those lanes read zero points)
+    const uint16_t *szbase =
+        TM ? nullptr
+           : (GS == 64 ? (ISUMS ? wzp : wsc) + kq * N
+                       : ((kq < 2 && !ISUMS) ? wsc : wzp) + (GS == 128 ? (kq & 1) * N : 0)) + (lane & 15);
+    const uint16_t *zbase64 = wzp + kq * N + (lane & 15);
+    constexpr int SZSTEP = GS == 64 ? 4 : (GS == 128 ? 2 : 1);  // scale/zp rows per window
     v4u rb0[U], rb1[U];
     uint32_t rsz[U];   // standard layout: one fp16 word per lane (spread with ds_bpermute)
+    uint32_t rszb[U];  // GS 64: this lane's zero-point word
     v2u rsz2[U];       // tile-major: the four words of this lane's column
     // first byte of window w of tile `tile`, less this lane's part
     // TM: 32-bit arithmetic (every offset is below the buffer size), with the product
@@ -536,7 +553,8 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
         } else {
             rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
             rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o + (uint32_t)(8 * (K / 2)), 0, 2);
-            rsz[u] = szbase[tile * 16 + 2 * w * N];
+            rsz[u] = szbase[tile * 16 + SZSTEP * w * N];
+            if constexpr (GS == 64) rszb[u] = zbase64[tile * 16 + SZSTEP * w * N];
         }
     };
     stage(0);  // issue the staging loads (older than the ring's, so waiting for them does not wait for the weights)
@@ -558,7 +576,8 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                 rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o : 0xFFFFFFF0u, 0, 2);
                 rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o + (uint32_t)(8 * (K / 2)) : 0xFFFFFFF0u, 0,
                                                               2);
-                rsz[u] = szbase[tile * 16 + 2 * (win0 + u) * N];
+                rsz[u] = szbase[tile * 16 + SZSTEP * (win0 + u) * N];
+                if constexpr (GS == 64) rszb[u] = zbase64[tile * 16 + SZSTEP * (win0 + u) * N];
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -595,6 +614,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                         }
                     }
                     uint32_t sz[4];  // scale g0, scale g1, zp g0, zp g1 of this lane's column
+                    uint32_t sz64[4];  // GS 64: zp of the window's four groups
                     if constexpr (TM) {
                         sz[0] = rsz2[u][0] & 0xFFFFu;
                         sz[1] = rsz2[u][0] >> 16;
@@ -604,7 +624,14 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             sz[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)rsz[u]);
+                        if constexpr (GS == 64) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                sz64[i] =
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute((i * 16 + (lane & 15)) * 4, (int)rszb[u]);
+                        }
                     }
+                    v4i dw = {0, 0, 0, 0};  // GS 256: the window's sums
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int64_t g = 2 * w + h;
@@ -626,26 +653,59 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                         if constexpr (TM) {
                             z4 = (int)__builtin_amdgcn_perm(0u, rsz2[u][1], h ? 0x01010101u : 0u);
                         } else {
-                            const int zneg = -(int)half_bits_to_float((uint16_t)sz[2 + h]);
+                            const uint32_t zb = GS == 64 ? (kq < 2 ? sz64[2 * h] : sz64[2 * h + 1])
+                                                         : (GS == 256 ? sz[2] : sz[2 + h]);
+                            const int zneg = -(int)half_bits_to_float((uint16_t)zb);
                             z4 = (int)((uint32_t)(zneg & 0xFF) * 0x01010101u);
                         }
                         const v4i bz = {z4, z4, z4, z4};
-                        v4i d = {0, 0, 0, 0};
-                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq1, d, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bz, d, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bz, d, 0, 0, 0);
-                        if (ISUMS) {
+                        if constexpr (GS == 64) {
+                            // the two 64-k groups of this half: lanes kq < 2, then kq >= 2
+                            const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int m = 4 * kq + r;
-                                if (m < M) istore(g, m, col, d[r]);
+                            for (int s2 = 0; s2 < 2; ++s2) {
+                                const bool mine = (kq >> 1) == s2;
+                                const v4i b0 = mine ? a0 : zero, b1 = mine ? a1 : zero;
+                                v4i d = {0, 0, 0, 0};
+                                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, bq0, d, 0, 0, 0);
+                                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, bq1, d, 0, 0, 0);
+                                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, bz, d, 0, 0, 0);
+                                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, bz, d, 0, 0, 0);
+                                const int64_t g64 = 2 * g + s2;
+                                if (ISUMS) {
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r) {
+                                        const int m = 4 * kq + r;
+                                        if (m < M) istore(g64, m, col, d[r]);
+                                    }
+                                } else {
+                                    float sc = half_bits_to_float((uint16_t)sz[2 * h + s2]);
+                                    __asm__ volatile("" : "+v"(sc));
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, (float)d[r], acc[r]);
+                                }
                             }
                         } else {
-                            float sc = half_bits_to_float((uint16_t)sz[h]);
-                            __asm__ volatile("" : "+v"(sc));  // one conversion, plain fmas
+                            v4i d = GS == 256 ? dw : v4i{0, 0, 0, 0};
+                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq0, d, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq1, d, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bz, d, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bz, d, 0, 0, 0);
+                            if (GS == 256 && h == 0) {
+                                dw = d;  // the window's second half adds into the same sums
+                            } else if (ISUMS) {
+                                const int64_t gg = GS == 256 ? w : g;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, (float)d[r], acc[r]);
+                                for (int r = 0; r < 4; ++r) {
+                                    const int m = 4 * kq + r;
+                                    if (m < M) istore(gg, m, col, d[r]);
+                                }
+                            } else {
+                                float sc = half_bits_to_float((uint16_t)sz[GS == 256 ? 0 : h]);
+                                __asm__ volatile("" : "+v"(sc));  // one conversion, plain fmas
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, (float)d[r], acc[r]);
+                            }
                         }
                     }
                     // refill: window w + U of this tile, else the next tile's window
@@ -689,7 +749,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
     }
 }
 
-template <int U, int SPLIT, bool ISUMS, int SB, bool TM>
+template <int U, int SPLIT, bool ISUMS, int SB, bool TM, int GS = G128>
 __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *__restrict__ qa,
                                                                  const float *__restrict__ a_scale, int64_t M,
                                                                  int64_t K, const uint8_t *__restrict__ wpk,
@@ -708,7 +768,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const int8_t *
     const bool batched = M * K <= (int64_t)kStageBatch * kDecThreads * 16;
     v4u stg[kStageBatch];
     float asc = 0.0f;
-    dec_tiles<U, SPLIT, ISUMS, TM>(
+    dec_tiles<U, SPLIT, ISUMS, TM, GS>(
         dsm, red, (int)M, K, wpk, wsc, wzp, N, t0, t1,
         [&](int phase) {  // qa[M][K] -> LDS
             if constexpr (TM) {
@@ -1419,7 +1479,7 @@ __device__ __forceinline__ int64_t mid_class_units(int32_t E, int64_t *lds_pfx, 
 }
 
 // ISUMS (test aid, in every expert loop): the per-group int32 sums of each slot go to
-// isums[g][slot][n] (g < K/128, slot < max_slots) instead of the fp32 output, and no
+// isums[g][slot][n] (g < K/GS, slot < max_slots) instead of the fp32 output, and no
 // scale is read; slots whose row index is outside [0, R) get unspecified sums.
 template <int U, bool ISUMS>
 __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
@@ -1463,7 +1523,7 @@ __global__ __launch_bounds__(kStreamThreads) void grouped_stream_kernel(
 // range of units, so it restages rows only when the chunk changes, and its tiles of
 // one chunk run as one stream.  Each tile is split over SPLIT K parts: four when no
 // workgroup can get more than four tiles (so that all 16 waves stream), else two.
-template <int U, int SPLIT, bool ISUMS>
+template <int U, int SPLIT, bool ISUMS, int GS = G128>
 __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
@@ -1530,7 +1590,7 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
             staged_chunk = chunk;
         }
         const uint8_t *wpk = packed + (int64_t)e * N * (K / 2);
-        const uint16_t *wsc = scale + (int64_t)e * G * N, *wzp = zp + (int64_t)e * G * N;
+        const uint16_t *wsc = scale + (int64_t)e * (K / GS) * N, *wzp = zp + (int64_t)e * (K / GS) * N;
         auto stage = [&](int phase) {  // the chunk's activation rows -> LDS (only when they
                                        // changed); rows outside [0, R) read row 0 and are
                                        // never stored.  The row scales load alongside.
@@ -1547,7 +1607,7 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
         auto store = [&](int m, int64_t col, float v) {
             if (srow[m] >= 0) out[(s0 + m) * N + col] = sasc[m] * v;
         };
-        dec_tiles<U, SPLIT, ISUMS, false>(
+        dec_tiles<U, SPLIT, ISUMS, false, GS>(
             dsm, red, rows, K, wpk, wsc, wzp, N, t0, t1, stage, store,
             [&](int64_t g, int m, int64_t col, int32_t v) {
                 if (srow[m] >= 0) isums[(g * max_slots + s0 + m) * N + col] = v;
@@ -1805,7 +1865,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     __builtin_amdgcn_s_waitcnt(0);  // the ring's last (unused) loads
 }
 
-template <int WM, int WN, bool ISUMS>
+template <int WM, int WN, bool ISUMS, int GS = G128>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
@@ -1834,9 +1894,10 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
         const int64_t tm = local % mt, tn = local / mt;
         const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * S::BM;
         const int rows = (int)((c - tm * S::BM) < S::BM ? (c - tm * S::BM) : S::BM);
-        tile2_unit<WM, WN, ISUMS>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
-                                  packed + (int64_t)e * N * (K / 2), (ISUMS ? nullptr : scale + (int64_t)e * G * N),
-                                  zp + (int64_t)e * G * N, N, tn * S::BN, out, N, isums, max_slots);
+        tile2_unit<WM, WN, ISUMS, GS>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
+                                      packed + (int64_t)e * N * (K / 2),
+                                      (ISUMS ? nullptr : scale + (int64_t)e * (K / GS) * N),
+                                      zp + (int64_t)e * (K / GS) * N, N, tn * S::BN, out, N, isums, max_slots);
         __syncthreads();  // the next unit reuses the LDS buffers
     }
 }
@@ -1960,6 +2021,7 @@ hipError_t launch_tiled3(const int8_t *qa, const float *a_scale, int64_t M, int6
 }
 
 // tm: `packed` is the tile-major array (scale and zp unused; no isums)
+template <int GS = G128>
 hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                          const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
                          bool tm, hipStream_t stream) {
@@ -1988,11 +2050,12 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
     const bool one = M * K <= (int64_t)kDecThreads * 16;
 #define W4A8_DEC1(UU, SS, IS, SB, TT)                                                                               \
     do {                                                                                                            \
-        if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, IS, SB, TT>,                               \
+        constexpr int GG = (TT) ? G128 : GS;                                                                        \
+        if (hipFuncSetAttribute((const void *)gemm_decode_kernel<UU, SS, IS, SB, TT, GG>,                           \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)                \
             return hipGetLastError();                                                                               \
-        hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, IS, SB, TT>), grid, block, lds, stream, qa, a_scale, M, K,   \
-                           packed, scale, zp, N, tpw, out, isums);                                                  \
+        hipLaunchKernelGGL((gemm_decode_kernel<UU, SS, IS, SB, TT, GG>), grid, block, lds, stream, qa, a_scale, M,  \
+                           K, packed, scale, zp, N, tpw, out, isums);                                               \
     } while (0)
 #define W4A8_DEC(UU, SS)                                                                                            \
     do {                                                                                                            \
@@ -2003,7 +2066,7 @@ hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int6
     // tile-major weights: contiguous streams take a deeper ring (four windows in flight);
     // the rows are staged by direct-to-LDS loads, so the staging batch does not apply
 #define W4A8_DEC_TM(UU, SS) W4A8_DEC1(UU, SS, false, 1, true)
-    if (tm) {
+    if (GS == G128 && tm) {
         if (split == 4) {
             if (nwin % 4 == 0) W4A8_DEC_TM(4, 4);
             else if (nwin % 2 == 0) W4A8_DEC_TM(2, 4);
@@ -2091,9 +2154,18 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
     return hipGetLastError();
 }
 
+bool decode_group_fits(int64_t M, int64_t K, int64_t N) {
+    return M >= 1 && M <= 16 && K % (2 * G128) == 0 && dec_lds_bytes(M, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax;
+}
+
 hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                                    const uint16_t *scale, const uint16_t *zp, int64_t N, int group, int path, float *out,
                                    int32_t *isums, hipStream_t stream) {
+    if (path == 1) {  // the decode loop (the caller checked decode_group_fits)
+        if (group == 64)
+            return launch_decode<64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, false, stream);
+        return launch_decode<256>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, false, stream);
+    }
     const bool wide = path == 4 || (path == 2 && M > 128);
     if (group == 64)
         return wide ? launch_tiled<4, 2, 64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
@@ -2169,7 +2241,7 @@ hipError_t launch_weights_to_tm(const uint8_t *packed, const uint16_t *scale, co
 
 // Experts with more than cmin slots: 128-row tiles up to 128 slots, 256-row tiles
 // above (a 256-row tile over a 65..128-slot expert would waste most of its work).
-template <int WM, int WN, bool IS>
+template <int WM, int WN, bool IS, int GS>
 static hipError_t launch_grouped_tiled_t(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                          const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                          const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
@@ -2177,10 +2249,10 @@ static hipError_t launch_grouped_tiled_t(const int8_t *qa, const float *a_scale,
                                          hipStream_t stream) {
     using S = TileShape<WM, WN>;
     const size_t lds = 2 * S::LDS_STAGE;
-    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<WM, WN, IS>,
+    if (hipFuncSetAttribute((const void *)grouped_tiled_kernel<WM, WN, IS, GS>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return hipGetLastError();
-    hipLaunchKernelGGL((grouped_tiled_kernel<WM, WN, IS>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa,
+    hipLaunchKernelGGL((grouped_tiled_kernel<WM, WN, IS, GS>), dim3((uint32_t)cus), dim3(S::THREADS), lds, stream, qa,
                        a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums, cmin,
                        cmax);
     return hipGetLastError();
@@ -2190,26 +2262,36 @@ template <int WM, int WN>
 static hipError_t launch_grouped_tiled_s(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                          const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                          const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                                         float *out, int32_t *isums, int64_t cmin, int64_t cmax, int cus,
+                                         float *out, int32_t *isums, int64_t cmin, int64_t cmax, int cus, int gs,
                                          hipStream_t stream) {
-    return isums ? launch_grouped_tiled_t<WM, WN, true>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
-                                                        zp, N, max_slots, out, isums, cmin, cmax, cus, stream)
-                 : launch_grouped_tiled_t<WM, WN, false>(qa, a_scale, R, row_index, expert_offsets, E, K, packed,
-                                                         scale, zp, N, max_slots, out, isums, cmin, cmax, cus, stream);
+#define W4A8_GTS(IS, GG)                                                                                            \
+    return launch_grouped_tiled_t<WM, WN, IS, GG>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,   \
+                                                  zp, N, max_slots, out, isums, cmin, cmax, cus, stream)
+    if (gs == 64) {
+        if (isums) W4A8_GTS(true, 64);
+        W4A8_GTS(false, 64);
+    }
+    if (gs == 256) {
+        if (isums) W4A8_GTS(true, 256);
+        W4A8_GTS(false, 256);
+    }
+    if (isums) W4A8_GTS(true, G128);
+    W4A8_GTS(false, G128);
+#undef W4A8_GTS
 }
 
 // experts with more than cmin slots
 static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                        const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                        const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                                       float *out, int32_t *isums, int64_t cmin, int cus, hipStream_t stream) {
+                                       float *out, int32_t *isums, int64_t cmin, int cus, int gs, hipStream_t stream) {
     if (max_slots <= cmin) return hipSuccess;
     if (cmin < 128) {
         hipError_t err = launch_grouped_tiled_s<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
-                                                      zp, N, max_slots, out, isums, cmin, 128, cus, stream);
+                                                      zp, N, max_slots, out, isums, cmin, 128, cus, gs, stream);
         if (err != hipSuccess || max_slots <= 128) return err;
     }
-    if (tiled3_fits(R, K, N)) {
+    if (gs == G128 && tiled3_fits(R, K, N)) {
 #define W4A8_GT3(IS)                                                                                                \
     do {                                                                                                            \
         if (hipFuncSetAttribute((const void *)grouped_tiled3_kernel<IS>,                                            \
@@ -2225,18 +2307,65 @@ static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, i
         return hipGetLastError();
     }
     return launch_grouped_tiled_s<4, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
-                                        max_slots, out, isums, 128, INT64_MAX, cus, stream);
+                                        max_slots, out, isums, 128, INT64_MAX, cus, gs, stream);
 }
 
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                               int64_t max_per_expert, float *out, int32_t *isums, hipStream_t stream) {
+                               int64_t max_per_expert, float *out, int32_t *isums, int gs, hipStream_t stream) {
     if (max_per_expert > max_slots) max_per_expert = max_slots;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipGetLastError();
     const int64_t G = K / G128;
+    if (gs != G128) {
+        // group sizes 64 and 256: the 16-row loop up to 16 slots when its conditions hold,
+        // the tiled loop (128- and 256-row tiles) above
+        int64_t cmin = 0;
+        if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax &&
+            (int64_t)R * K < (1ll << 32)) {
+            const dim3 dgrid((uint32_t)cus), dblock(kDecThreads);
+            const int64_t chunks = std::min<int64_t>(max_slots, (max_slots + 15) / 16 + E);
+            const bool four = G % 8 == 0 && chunks * (N / 16) <= 4 * (int64_t)cus;
+            const int split = four ? 4 : 2;
+            const size_t dlds = (size_t)(((dec_lds_bytes(16, K) + 15) / 16) * 16 + dec_red_bytes(split));
+#define W4A8_GDG(UU, SS, IS, GG)                                                                                    \
+    do {                                                                                                            \
+        if (hipFuncSetAttribute((const void *)grouped_decode_kernel<UU, SS, IS, GG>,                                \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dlds) != hipSuccess)               \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((grouped_decode_kernel<UU, SS, IS, GG>), dgrid, dblock, dlds, stream, qa, a_scale, R,    \
+                           row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums, 16,        \
+                           (int64_t)0);                                                                             \
+    } while (0)
+#define W4A8_GDG2(UU, SS)                                                                                           \
+    do {                                                                                                            \
+        if (gs == 64) {                                                                                             \
+            if (isums) W4A8_GDG(UU, SS, true, 64);                                                                  \
+            else W4A8_GDG(UU, SS, false, 64);                                                                       \
+        } else {                                                                                                    \
+            if (isums) W4A8_GDG(UU, SS, true, 256);                                                                 \
+            else W4A8_GDG(UU, SS, false, 256);                                                                      \
+        }                                                                                                           \
+    } while (0)
+            if (four) {
+                if ((G / 8) % 2 == 0) W4A8_GDG2(2, 4);
+                else W4A8_GDG2(1, 4);
+            } else {
+                if ((G / 4) % 2 == 0) W4A8_GDG2(2, 2);
+                else W4A8_GDG2(1, 2);
+            }
+#undef W4A8_GDG2
+#undef W4A8_GDG
+            const hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            cmin = 16;
+        }
+        if (max_per_expert <= cmin) return hipSuccess;
+        return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
+                                    out, isums, cmin, cus, gs, stream);
+    }
     // the decode loop stages gathered rows with 32-bit offsets (row * K) and addresses the
     // codes with 32-bit offsets; larger inputs take the streaming loop (64-bit addresses)
     if (G % 4 == 0 && dec_lds_bytes(16, K) <= kDecLdsMax && N * (K / 2) < kDecCodesMax &&
@@ -2283,7 +2412,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         if (!mid) return max_per_expert <= kSmallRows ? hipSuccess
                                                       : launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets,
                                                                              E, K, packed, scale, zp, N, max_slots, out,
-                                                                             isums, kSmallRows, cus, stream);
+                                                                             isums, kSmallRows, cus, G128, stream);
         // the other loops only when some expert can have that many slots
 #define W4A8_GMID1(MF, CMIN, CMAX, IS)                                                                              \
     do {                                                                                                            \
@@ -2304,7 +2433,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
 #undef W4A8_GMID1
         if (max_per_expert <= kMidMax) return hipSuccess;
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, isums, kMidMax, cus, stream);
+                                    out, isums, kMidMax, cus, G128, stream);
     }
     const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
@@ -2324,7 +2453,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || max_per_expert <= kSmallRows) return err;
     return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
-                                isums, kSmallRows, cus, stream);
+                                isums, kSmallRows, cus, G128, stream);
 }
 
 }  // namespace w4a8

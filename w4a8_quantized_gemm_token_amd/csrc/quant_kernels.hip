@@ -188,30 +188,82 @@ __global__ __launch_bounds__(kActThreads) void silu_mul_quantize_long_kernel(con
     for (int64_t c = threadIdx.x; c < I; c += kActThreads) qh[p * I + c] = (int8_t)quantize_i8(silu_mul(gate[c], up[c]), s);
 }
 
-// One wave per (output feature n, group g); lane l owns weights 2l and 2l+1 of
-// the group, i.e. exactly packed byte l of the group.
+// One wave per unit of one output feature n and SPAN consecutive k (128, or 256 for GS 256):
+//  GS 128: one group per wave; lane l owns weights 2l and 2l+1, i.e. packed byte l.
+//  GS 64:  two groups per wave (lanes 0-31 and 32-63), lane l again weights 2l, 2l+1 of the
+//          wave's 128 k; the range is reduced over each half-wave.
+//  GS 256: one group per wave; lane l owns weights 4l .. 4l+3, i.e. packed bytes 2l, 2l+1.
 // SMOOTH: each weight is first multiplied by its channel's smoothing factor
 // s[k] (one fp32 product), so the smoothed matrix is never written out.
 constexpr int kPackThreads = 256;
-template <bool SMOOTH>
+
+template <int GS>
+__device__ __forceinline__ float unit_min(float v) {
+    if constexpr (GS == 64) {
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
+        return v;
+    } else {
+        return wave_min(v);
+    }
+}
+template <int GS>
+__device__ __forceinline__ float unit_max(float v) {
+    if constexpr (GS == 64) {
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+        return v;
+    } else {
+        return wave_max(v);
+    }
+}
+
+template <bool SMOOTH, int GS>
 __global__ __launch_bounds__(kPackThreads) void pack_weights_kernel(const float *__restrict__ W, int64_t N,
                                                                     int64_t K, const float *__restrict__ sf,
                                                                     uint8_t *__restrict__ packed,
                                                                     uint16_t *__restrict__ scale,
                                                                     uint16_t *__restrict__ zp) {
-    const int64_t G = K / W4A8_GROUP;
+    constexpr int SPAN = GS == 256 ? 256 : 128;  // k covered by one wave
+    constexpr int PER = SPAN / kWave;            // weights per lane: 2 or 4
+    const int64_t U = K / SPAN;
     const int64_t unit = (int64_t)blockIdx.x * (kPackThreads / kWave) + threadIdx.x / kWave;
-    if (unit >= N * G) return;
-    const int64_t n = unit / G, g = unit % G;
+    if (unit >= N * U) return;
+    const int64_t n = unit / U, u = unit % U;
     const int lane = threadIdx.x % kWave;
-    float2 w = reinterpret_cast<const float2 *>(W + n * K + g * W4A8_GROUP)[lane];
-    if (SMOOTH) {
-        const float2 f = reinterpret_cast<const float2 *>(sf + g * W4A8_GROUP)[lane];
-        w = make_float2(w.x * f.x, w.y * f.y);
+    float w[PER];
+    if constexpr (PER == 2) {
+        const float2 v = reinterpret_cast<const float2 *>(W + n * K + u * SPAN)[lane];
+        w[0] = v.x;
+        w[1] = v.y;
+        if (SMOOTH) {
+            const float2 f = reinterpret_cast<const float2 *>(sf + u * SPAN)[lane];
+            w[0] = w[0] * f.x;
+            w[1] = w[1] * f.y;
+        }
+    } else {
+        const float4 v = reinterpret_cast<const float4 *>(W + n * K + u * SPAN)[lane];
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+        if (SMOOTH) {
+            const float4 f = reinterpret_cast<const float4 *>(sf + u * SPAN)[lane];
+            w[0] = w[0] * f.x;
+            w[1] = w[1] * f.y;
+            w[2] = w[2] * f.z;
+            w[3] = w[3] * f.w;
+        }
     }
     // the range always contains 0: zp in [0, 15], (q - zp) in [-15, 15]
-    const float lo = wave_min(fminf(fminf(w.x, w.y), 0.0f));
-    const float hi = wave_max(fmaxf(fmaxf(w.x, w.y), 0.0f));
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        lo = fminf(lo, w[i]);
+        hi = fmaxf(hi, w[i]);
+    }
+    lo = unit_min<GS>(lo);
+    hi = unit_max<GS>(hi);
     uint16_t sh = float_to_half_bits((hi - lo) / 15.0f);
     float s = half_bits_to_float(sh);
     if (s == 0.0f) {
@@ -219,10 +271,19 @@ __global__ __launch_bounds__(kPackThreads) void pack_weights_kernel(const float 
         s = 1.0f;
     }
     const int z = (int)fminf(fmaxf(__builtin_rintf(-lo / s), 0.0f), 15.0f);
-    const int q0 = min(max((int)__builtin_rintf(w.x / s) + z, 0), 15);
-    const int q1 = min(max((int)__builtin_rintf(w.y / s) + z, 0), 15);
-    packed[n * (K / 2) + g * (W4A8_GROUP / 2) + lane] = (uint8_t)(q0 | (q1 << 4));
-    if (lane == 0) {
+    int q[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) q[i] = min(max((int)__builtin_rintf(w[i] / s) + z, 0), 15);
+    if constexpr (PER == 2) {
+        packed[n * (K / 2) + u * (SPAN / 2) + lane] = (uint8_t)(q[0] | (q[1] << 4));
+    } else {
+        const uint16_t two = (uint16_t)((q[0] | (q[1] << 4)) | ((q[2] | (q[3] << 4)) << 8));
+        reinterpret_cast<uint16_t *>(packed + n * (K / 2) + u * (SPAN / 2))[lane] = two;
+    }
+    // the group's first lane writes its scale and zero point ([K / GS][N])
+    const bool first = GS == 64 ? (lane & 31) == 0 : lane == 0;
+    if (first) {
+        const int64_t g = GS == 64 ? 2 * u + (lane >> 5) : u;
         scale[g * N + n] = sh;
         zp[g * N + n] = float_to_half_bits((float)z);
     }
@@ -303,17 +364,26 @@ hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_
     return hipGetLastError();
 }
 
-hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, const float *s, uint8_t *packed, uint16_t *scale,
-                               uint16_t *zp, hipStream_t stream) {
-    const int64_t units = N * (K / W4A8_GROUP);
+hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, int group, const float *s, uint8_t *packed,
+                               uint16_t *scale, uint16_t *zp, hipStream_t stream) {
+    const int64_t span = group == 256 ? 256 : 128;
+    const int64_t units = N * (K / span);
     const int64_t per_block = kPackThreads / kWave;
     const dim3 grid((uint32_t)((units + per_block - 1) / per_block));
-    if (s)
-        hipLaunchKernelGGL(pack_weights_kernel<true>, grid, dim3(kPackThreads), 0, stream, W, N, K, s, packed, scale,
-                           zp);
-    else
-        hipLaunchKernelGGL(pack_weights_kernel<false>, grid, dim3(kPackThreads), 0, stream, W, N, K, s, packed, scale,
-                           zp);
+#define W4A8_PACK(SM, GG)                                                                                           \
+    hipLaunchKernelGGL((pack_weights_kernel<SM, GG>), grid, dim3(kPackThreads), 0, stream, W, N, K, s, packed,      \
+                       scale, zp)
+    if (group == 64) {
+        if (s) W4A8_PACK(true, 64);
+        else W4A8_PACK(false, 64);
+    } else if (group == 256) {
+        if (s) W4A8_PACK(true, 256);
+        else W4A8_PACK(false, 256);
+    } else {
+        if (s) W4A8_PACK(true, 128);
+        else W4A8_PACK(false, 128);
+    }
+#undef W4A8_PACK
     return hipGetLastError();
 }
 

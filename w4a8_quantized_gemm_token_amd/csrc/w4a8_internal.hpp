@@ -24,7 +24,7 @@ hipError_t launch_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh,
                                     float *h_scale, float *h_out, hipStream_t stream);
 // s: per-channel smoothing factors [K] applied before quantization (nullptr: none).
-hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, const float *s, uint8_t *packed,
+hipError_t launch_pack_weights(const float *W, int64_t N, int64_t K, int group, const float *s, uint8_t *packed,
                                uint16_t *scale, uint16_t *zp, hipStream_t stream);
 hipError_t launch_channel_absmax(const float *A, int64_t rows, int64_t K, int64_t lda, float *out,
                                  hipStream_t stream);
@@ -35,8 +35,10 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
                        const uint8_t *packed, const uint16_t *scale, const uint16_t *zp,
                        int64_t N, int path, float *out, int32_t *isums, hipStream_t stream);
 
-// The tiled loop for group size 64, 128 or 256 (K a multiple of 128 and of the group);
-// path 2 or 3 (the 128-row tile unless path 2 has M > 128) or 4 (256-row tiles).
+// Group size 64 or 256 (K a multiple of 128 and of the group): path 1 = the decode loop
+// (M <= 16, decode_group_fits), path 2 or 3 = the tiled loop (the 128-row tile unless path
+// 2 has M > 128), 4 = tiled with 256-row tiles.
+bool decode_group_fits(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                                    const uint16_t *scale, const uint16_t *zp, int64_t N, int group, int path, float *out,
                                    int32_t *isums, hipStream_t stream);
@@ -44,12 +46,13 @@ hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64
 // max_per_expert: a bound on any one expert's slot count known to the caller (the
 // MoE layer knows no expert gets more than T); loops for larger experts are not
 // launched.  max_slots when nothing better is known.  isums != nullptr selects the
-// debug form: per-group int32 sums isums[K/128][max_slots][N] instead of `out`.
+// debug form: per-group int32 sums isums[K/group][max_slots][N] instead of `out`.
+// group: 64, 128 or 256 (scale/zp [E][K/group][N]).
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R,
                                const int32_t *row_index, const int32_t *expert_offsets, int32_t E,
                                int64_t K, const uint8_t *packed, const uint16_t *scale,
                                const uint16_t *zp, int64_t N, int64_t max_slots, int64_t max_per_expert,
-                               float *out, int32_t *isums, hipStream_t stream);
+                               float *out, int32_t *isums, int group, hipStream_t stream);
 
 // Tile-major weights for the decode loop (M <= 16): bytes of the array, whether a
 // shape is served, the GEMM over it, and the conversion from the standard layout.
