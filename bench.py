@@ -198,8 +198,10 @@ def parse():
                    help="print the mean SQ/GRBM counters of --kernel over rocprofv3 --pmc runs; no GPU")
     p.add_argument("--kernel", default="gemm_tiled_kernel", help="kernel named by --summarize-counters")
     p.add_argument("--cmd", action="append", default=[], help="command text recorded in a summary")
-    p.add_argument("--only", choices=["prefill"],
+    p.add_argument("--only", choices=["prefill", "toy_moe", "moe_ffn"],
                    help="run one secondary workload alone and print its figures (for counter runs)")
+    p.add_argument("--size", type=int, action="append",
+                   help="batch B (toy_moe) or tokens T (moe_ffn) for --only; repeatable")
     p.add_argument("--group", type=int, default=GROUP, choices=(64, 128, 256),
                    help="group size of the weights for --only prefill")
     p.add_argument("--reps", type=int, default=10, help="timed launches for --only")
@@ -442,38 +444,47 @@ def decode_group_sizes(torch, w4, synthetic, copies, reps=50):
 def secondary(torch, w4, synthetic, copies):
     """Prefill (M=4096, K=N=8192) TOPS, decode at group 64 and 256, MoE layer times and the
     smoothing figures; context."""
-    dev = torch.device("cuda:0")
     out = {**decode_group_sizes(torch, w4, synthetic, copies),
            "prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
            "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
            "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
            "quant_variants_K8192_N4096_M16": quant_variants(torch, w4, synthetic)}
 
-    def device_experts(seed, tag, E, N, K):
-        return w4.pack_experts_device(
-            E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, e, K, 0, "plain"), dev)
+    out.update(toy_moe(torch, w4, synthetic, (1, 2, 4, 512)))
+    out.update(moe_ffn_layer(torch, w4, synthetic, (64, 4096)))
+    return out
 
-    # toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
-    # back-to-back prepared launches that rotate three copies of the 250 MB expert set
-    # (so no call finds its weights in the 256 MB Infinity Cache); the layer (route,
-    # quantize, grouped GEMM, combine) is timed the same way.
-    E8, K8, N8, copies = 8, 4096, 14336, 3
-    sets = [device_experts(0, synthetic.TAG_W, E8, N8, K8) for _ in range(copies)]
-    ebytes = N8 * K8 // 2 + 4 * N8 * (K8 // GROUP)  # packed codes + fp16 scale and zero point
+
+def _device_experts(torch, w4, synthetic, seed, tag, E, N, K):
+    dev = torch.device("cuda:0")
+    return w4.pack_experts_device(
+        E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, e, K, 0, "plain"), dev)
+
+
+def _timed(torch, fns, reps):
     stream = torch.cuda.current_stream()
+    for i in range(20):
+        fns[i % len(fns)]()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
 
-    def timed(fns, reps):
-        for i in range(20):
-            fns[i % len(fns)]()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        for i in range(reps):
-            fns[i % len(fns)]()
-        e.record(stream)
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / reps
 
-    for B in (1, 2, 4, 512):
+def toy_moe(torch, w4, synthetic, batches, reps=60):
+    """Toy MoE: 8 experts, top-1, K=4096, N=14336.  The grouped GEMM is timed alone over
+    back-to-back prepared launches that rotate three copies of the 250 MB expert set (so no
+    call finds its weights in the 256 MB Infinity Cache); the layer (route, quantize,
+    grouped GEMM, combine) is timed the same way."""
+    dev = torch.device("cuda:0")
+    out = {}
+    E8, K8, N8, copies = 8, 4096, 14336, 3
+    sets = [_device_experts(torch, w4, synthetic, 0, synthetic.TAG_W, E8, N8, K8) for _ in range(copies)]
+    ebytes = N8 * K8 // 2 + 4 * N8 * (K8 // GROUP)  # packed codes + fp16 scale and zero point
+    for B in batches:
         x = torch.from_numpy(synthetic.activations(100 + B, B, K8)).to(dev)
         logits = torch.from_numpy(synthetic.router_logits_iid(100 + B, B, E8)).to(dev)
         i32, f32 = torch.int32, torch.float32
@@ -492,22 +503,29 @@ def secondary(torch, w4, synthetic, copies):
         quant()
         torch.cuda.synchronize()
         touched = int((np.diff(routed[2].cpu().numpy()) > 0).sum())
-        gemm_ms = timed(ggs, 60)
+        gemm_ms = _timed(torch, ggs, reps)
         layers = [lambda c=c: (route(), quant(), ggs[c](), comb()) for c in range(copies)]
-        layer_ms = timed(layers, 60)
+        layer_ms = _timed(torch, layers, reps)
         gbytes = touched * ebytes + B * (K8 + 4) + 4 * B * N8
         t_roof = max(gbytes / (HBM_PEAK_GBS * 1e9), 2.0 * B * N8 * K8 / (INT8_PEAK_TOPS * 1e12))
         out[f"toy_moe_B{B}"] = {"gemm_us": round(gemm_ms * 1e3, 2), "experts_touched": touched,
                                 "GB/s": round(gbytes / (gemm_ms * 1e-3) / 1e9, 1),
                                 "frac_roofline": round(t_roof / (gemm_ms * 1e-3), 4),
                                 "layer_us": round(layer_ms * 1e3, 2)}
-    del sets, ggs, layers
+    del sets
     torch.cuda.empty_cache()
-    # MoE FFN layer, 384 experts + shared, top-8, H=7168, I=2048
+    return out
+
+
+def moe_ffn_layer(torch, w4, synthetic, tokens, reps=5):
+    """MoE FFN layer, 384 experts + shared, top-8, H=7168, I=2048, true-normal activations
+    and skewed router logits; `reps` back-to-back layers after four untimed ones."""
+    dev = torch.device("cuda:0")
+    out = {}
     E, k, H, I = 384, 8, 7168, 2048
-    gate_up = device_experts(0, synthetic.TAG_W, E + 1, 2 * I, H)
-    down = device_experts(0, synthetic.TAG_W_DOWN, E + 1, H, I)
-    for T in (64, 4096):
+    gate_up = _device_experts(torch, w4, synthetic, 0, synthetic.TAG_W, E + 1, 2 * I, H)
+    down = _device_experts(torch, w4, synthetic, 0, synthetic.TAG_W_DOWN, E + 1, H, I)
+    for T in tokens:
         x = torch.from_numpy(synthetic.activations(0, T, H)).to(dev)
         logits = torch.from_numpy(synthetic.router_logits_skewed(0, T, E)).to(dev)
         total, _ = w4.moe_ffn_workspace(T, H, I, E, k)
@@ -515,7 +533,6 @@ def secondary(torch, w4, synthetic, copies):
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
         for _ in range(4):
             _, inter = w4.moe_ffn(x, logits, k, gate_up, down, workspace=ws, out=y)
-        reps = 5
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(torch.cuda.current_stream())
         for _ in range(reps):
@@ -559,6 +576,12 @@ def main():
     if args.only == "prefill":
         print(json.dumps({f"prefill_M4096_K8192_N8192_group{args.group}": prefill(torch, w4, synthetic, args.reps,
                                                                                    args.group)}), flush=True)
+        return
+    if args.only == "toy_moe":
+        print(json.dumps(toy_moe(torch, w4, synthetic, args.size or (1, 2, 4, 512), args.reps)), flush=True)
+        return
+    if args.only == "moe_ffn":
+        print(json.dumps(moe_ffn_layer(torch, w4, synthetic, args.size or (64, 4096), args.reps)), flush=True)
         return
     layers, tms, xs = decode_setup(torch, w4, synthetic, args.copies)
     ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m, warmed_s = run_decode(

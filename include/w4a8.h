@@ -352,7 +352,17 @@ w4a8_status w4a8_moe_combine(const float *y, const int32_t *slot_of_pair, const 
  *   5. w4a8_moe_grouped_gemm, E+1 experts        down weights [E+1][H][I/2]
  *   6. w4a8_moe_combine (y_shared = the shared expert's rows)  -> out [T][H]
  * with S = T*k + T slots (routed pairs, then one shared slot per token).
- * Expert E of each weight stack is the shared expert.  The intermediates live in
+ * Expert E of each weight stack is the shared expert.  Steps 3-4 and 5-6 are partly
+ * fused ([p1 §4.3]: the dequant/requant around the INT8 product stays in registers):
+ *   - an expert with more than 128 slots runs its gate/up product on the tiled loop
+ *     with SiLU(gate) * up in the epilogue.  Its gu lines then hold h [I] and, after
+ *     it, the largest |h| of each 16 columns [I/16] instead of gate | up (h is
+ *     bit-identical to step 4's own h of those gate/up rows), and the requant takes
+ *     the row maximum from those maxima.  Other experts' lines hold gate | up.
+ *   - with T > 128 the shared expert's down product runs after the routed experts'
+ *     with the combine in its epilogue.  The layer output is the same bits as step 6,
+ *     and the shared expert's rows are still written to y.
+ * The intermediates live in
  * the caller's workspace (device memory, at least w4a8_moe_ffn_workspace_size
  * bytes, 256-byte aligned); w4a8_moe_ffn_workspace_layout gives each part's byte
  * offset in it (enum w4a8_moe_ws_part order), so a caller can read any stage.

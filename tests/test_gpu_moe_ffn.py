@@ -107,12 +107,17 @@ def test_moe_ffn_full_size_stagewise(orc, T):
     """384 routed experts (Zipf-skewed router bias) + 1 shared, top-8, H=7168, I=2048, true-normal
     router logits and activations.  Routing tables in full; then, on the slots of 64 tokens (all
     of them at T=64; each token's k routed slots and its shared slot), stage by stage:
-    (i) gate/up int32 sums bit-exact and the layer's fp32 gate/up rows within the product bound;
+    (i) gate/up int32 sums bit-exact and the fp32 gate/up rows within the product bound (the
+    layer's own rows, or for experts above 128 slots, whose epilogue folds SiLU * up in, the
+    grouped GEMM entry's rows on the same routing, with the layer's h and per-16-column maxima
+    bit-identical to the silu kernel's of those rows);
     (ii) h of the silu kernel within its bound of silu(gate)*up of those rows;
     (iii) the requantized codes and row scales bit-exact against the per-token quantizer
     applied to that h; (iv) down int32 sums bit-exact on the GPU's codes and the layer's fp32
     down rows within the product bound; (v) the combine of the GPU's own down rows within its
-    bound.  Last, the layer output of those tokens end to end against the oracle's independent
+    bound, and every token's output bit-identical to the combine kernel over the layer's own
+    down rows (at T=4096 the combine is folded into the shared expert's down product).
+    Last, the layer output of those tokens end to end against the oracle's independent
     chain, each re-quantized code that lies within fp32 noise of a rounding tie allowed its
     one-step change."""
     import w4a8_quantized_gemm_token_amd as w4
@@ -154,7 +159,19 @@ def test_moe_ffn_full_size_stagewise(orc, T):
     n = len(slots)
     sub_off = np.searchsorted(sexp, np.arange(E + 2)).astype(np.int32)   # offsets over the E+1 experts
     sl_dev = to_dev(slots)
-    gu = to_host(inter["gu"][sl_dev])
+    # experts with more than 128 slots fold SiLU * up into the gate/up epilogue: their gu lines
+    # hold h and its per-16-column maxima.  Their gate | up rows come from the grouped GEMM entry
+    # on the same routing (the same loops); the layer's h must be the silu kernel's h of them.
+    S = P + T
+    offs = to_host(inter["offsets"])
+    fused = np.repeat(np.diff(offs) > 128, np.diff(offs))[slots]
+    gu_layer = to_host(inter["gu"][sl_dev])
+    gu_all = w4.moe_grouped_gemm(inter["qa"], inter["a_scale"], inter["row_index"], inter["offsets"], *gate_up,
+                                 max_slots=S)
+    gu = to_host(gu_all[sl_dev])
+    del gu_all
+    print(f"T={T}: {int(fused.sum())} of {n} sampled slots on the fused gate/up epilogue")
+    assert np.array_equal(gu_layer[~fused].view(np.uint32), gu[~fused].view(np.uint32)), "unfused gate|up lines"
     qh = to_host(inter["qh"][sl_dev])
     hs = to_host(inter["h_scale"][sl_dev])
     y = to_host(inter["y"][sl_dev])
@@ -166,6 +183,9 @@ def test_moe_ffn_full_size_stagewise(orc, T):
                                                       gate_up[0], gate_up[2], max_slots=n))
     # (ii), (iii) the silu kernel over the layer's own gate/up rows gives the layer's codes
     qh2, hs2, h2 = (to_host(t) for t in w4.silu_mul_quantize(to_dev(gu), want_h=True))
+    assert np.array_equal(gu_layer[fused, :I].view(np.uint32), h2[fused].view(np.uint32)), "fused h"
+    pm = np.abs(h2[fused]).reshape(-1, I // 16, 16).max(axis=2)
+    assert np.array_equal(gu_layer[fused, I:I + I // 16].view(np.uint32), pm.view(np.uint32)), "fused row maxima"
     assert np.array_equal(qh2, qh) and np.array_equal(hs2.view(np.uint32), hs.view(np.uint32))
     h_ref = orc.silu_mul(gu)
     gxu = np.abs(gu[:, :I].astype(np.float64) * gu[:, I:].astype(np.float64))
@@ -216,6 +236,10 @@ def test_moe_ffn_full_size_stagewise(orc, T):
         mag = (np.abs(wt) * np.abs(yj)).sum(0) + np.abs(ysh)
         err = np.abs(out[t] - ref)
         assert (err <= 1e-5 * mag + 1e-6).all(), f"combine, token {t}: worst {err.max():.3e}"
+    # every token: the layer output is the combine kernel's over the layer's own down rows
+    comb = to_host(w4.moe_combine(inter["y"][:P], inter["slot_of_pair"].view(T, k), inter["w"],
+                                  y_shared=inter["y"][P:]))
+    assert np.array_equal(out.view(np.uint32), comb.view(np.uint32)), "layer output vs the combine kernel"
     # end to end
     for t in tokens:
         rows = stok == t
@@ -223,3 +247,68 @@ def test_moe_ffn_full_size_stagewise(orc, T):
         bound = tol_e2e[rows].sum(0) + 1e-6
         err = np.abs(out[t] - ref)
         assert (err <= bound).all(), f"token {t}: worst {err.max():.3e} vs bound {bound[err.argmax()]:.3e}"
+
+
+def test_moe_ffn_fused_epilogues(orc):
+    """The layer's fused steps on E=8 routed experts + 1 shared, top-3, H=640, I=384, T=300
+    skewed tokens (seed 0: experts of 258, 199, 141 and, shared, 300 slots take the tiled loop
+    with SiLU * up in the gate/up epilogue; 103, 69, 47, 46 and 37 do not; T > 128 folds the
+    combine into the shared expert's down product).  Against the unfused entry points on the
+    same data, bit for bit: h of the fused rows (and their per-16-column maxima), gate | up of
+    the others, the codes and row scales, and the layer output against the combine kernel over
+    the layer's own down rows.  Against the oracle: the codes against the per-token quantizer
+    on the GPU's own h, the shared expert's down rows on the GPU's codes, and every token's
+    output through the oracle's independent chain."""
+    import w4a8_quantized_gemm_token_amd as w4
+    E, k, H, I, T = 8, 3, 640, 384, 300
+    gate_up = device_experts(0, synthetic.TAG_W, E + 1, 2 * I, H)
+    down = device_experts(0, synthetic.TAG_W_DOWN, E + 1, H, I)
+    x = synthetic.activations(0, T, H)
+    logits = synthetic.router_logits_skewed(0, T, E)
+    out, inter = _run_gpu_ffn(x, logits, k, gate_up, down)
+    ids_r, w_r = orc.route_topk(logits, k)
+    assert np.array_equal(to_host(inter["ids"]), ids_r)
+    P, S = T * k, T * k + T
+    offsets = to_host(inter["offsets"])
+    counts = np.diff(offsets)
+    assert sorted(counts[:E].tolist(), reverse=True) == [258, 199, 141, 103, 69, 47, 46, 37] and counts[E] == T
+    fused = np.repeat(counts > 128, counts)                       # per slot
+    # the unfused chain on the same data: grouped GEMM over every expert, then the silu kernel
+    gu_u = w4.moe_grouped_gemm(inter["qa"], inter["a_scale"], inter["row_index"], inter["offsets"], *gate_up,
+                               max_slots=S)
+    qh_u, hs_u, h_u = (to_host(t) for t in w4.silu_mul_quantize(gu_u, want_h=True))
+    gu_l, gu_u = to_host(inter["gu"]), to_host(gu_u)
+    assert np.array_equal(gu_l[~fused].view(np.uint32), gu_u[~fused].view(np.uint32)), "unfused gate|up lines"
+    assert np.array_equal(gu_l[fused, :I].view(np.uint32), h_u[fused].view(np.uint32)), "fused h"
+    pm = np.abs(h_u[fused]).reshape(-1, I // 16, 16).max(axis=2)
+    assert np.array_equal(gu_l[fused, I:I + I // 16].view(np.uint32), pm.view(np.uint32)), "fused row maxima"
+    qh, hs = to_host(inter["qh"]), to_host(inter["h_scale"])
+    assert np.array_equal(qh, qh_u) and np.array_equal(hs.view(np.uint32), hs_u.view(np.uint32))
+    q_o2, s_o2 = orc.quantize_act(h_u)
+    assert np.array_equal(qh, q_o2) and np.array_equal(hs.view(np.uint32), s_o2.view(np.uint32))
+    # the shared expert's down rows (written by the fused epilogue) on the GPU's codes
+    y = to_host(inter["y"])
+    qd, sd, zd = orc.quantize_weights(synthetic.weights(0, synthetic.TAG_W_DOWN, E, H, I))
+    yr, mag = orc.gemm(qh[P:], hs[P:], qd, sd, zd)
+    check_close(y[P:], yr, mag, "shared expert down rows")
+    # the folded combine gives the combine kernel's bits over the layer's own rows
+    comb = to_host(w4.moe_combine(inter["y"][:P], inter["slot_of_pair"].view(T, k), inter["w"],
+                                  y_shared=inter["y"][P:]))
+    assert np.array_equal(out.view(np.uint32), comb.view(np.uint32)), "folded combine"
+    # every token end to end against the oracle's chain
+    cache_gu, cache_d = {}, {}
+
+    def gu_q(e):
+        if e not in cache_gu:
+            cache_gu[e] = orc.quantize_weights(synthetic.weights(0, synthetic.TAG_W, e, 2 * I, H))
+        return cache_gu[e]
+
+    def d_q(e):
+        if e not in cache_d:
+            cache_d[e] = orc.quantize_weights(synthetic.weights(0, synthetic.TAG_W_DOWN, e, H, I))
+        return cache_d[e]
+
+    for t in range(T):
+        ref, tol = oracle_token(orc, x[t], list(ids_r[t]) + [E], list(w_r[t]) + [1.0], gu_q, d_q, I)
+        err = np.abs(out[t] - ref)
+        assert (err <= tol).all(), f"token {t}: worst {err.max():.3e} vs tol {tol[err.argmax()]:.3e}"

@@ -566,12 +566,31 @@ w4a8_status moe_ffn_run(const float *x, const float *logits, int64_t T, int64_t 
     if (T == 0) return W4A8_OK;
     if ((err = launch_quantize_act(x, T, H, H, nullptr, qa, a_scale, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: quantize");
-    // top-k picks distinct experts per token, so no expert (the shared one included) gets more than T slots
+    // top-k picks distinct experts per token, so no expert (the shared one included) gets more than T slots.
+    // Experts on the three-stage tiled loop fold SiLU * up into the gate/up epilogue (their gu
+    // lines then hold h and its per-16-column maxima); the requant reads either form.
+    T3Epi silu;
+    silu.half = I;
+    int64_t fused_min = INT64_MAX;
+    const bool fuse_silu = I <= 4096;
     if ((err = launch_grouped_gemm(qa, a_scale, T, slot_row, offsets, E + 1, H, gu_packed, gu_scale, gu_zp, 2 * I, S, T,
-                                   gu, nullptr, W4A8_GROUP, stream)) != hipSuccess)
+                                   gu, nullptr, W4A8_GROUP, stream, fuse_silu ? &silu : nullptr, &fused_min)) !=
+        hipSuccess)
         return hip_status(err, "moe_ffn: gate/up grouped GEMM");
-    if ((err = launch_silu_mul_quantize(gu, S, I, qh, h_scale, nullptr, stream)) != hipSuccess)
+    if ((err = launch_moe_requant(gu, S, I, offsets, E + 1, fused_min, qh, h_scale, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: silu*up requant");
+    if (shared_combine_fits(T, I, H, topk)) {
+        // routed experts, then the shared one (slots P .. S, token order) with the combine folded in
+        if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E, I, dn_packed, dn_scale, dn_zp, H, S, T, y,
+                                       nullptr, W4A8_GROUP, stream)) != hipSuccess)
+            return hip_status(err, "moe_ffn: down grouped GEMM");
+        const int64_t eb = (int64_t)E;
+        if ((err = launch_shared_combine(qh + P * I, h_scale + P, T, I, dn_packed + eb * H * (I / 2),
+                                         dn_scale + eb * (I / W4A8_GROUP) * H, dn_zp + eb * (I / W4A8_GROUP) * H, H,
+                                         y + P * H, y, sop, w, topk, out, stream)) != hipSuccess)
+            return hip_status(err, "moe_ffn: shared expert down GEMM + combine");
+        return W4A8_OK;
+    }
     if ((err = launch_grouped_gemm(qh, h_scale, S, nullptr, offsets, E + 1, I, dn_packed, dn_scale, dn_zp, H, S, T, y,
                                    nullptr, W4A8_GROUP, stream)) != hipSuccess)
         return hip_status(err, "moe_ffn: down grouped GEMM");

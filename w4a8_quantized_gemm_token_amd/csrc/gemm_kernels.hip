@@ -40,6 +40,7 @@
 #include "w4a8_internal.hpp"
 
 using namespace w4a8dev;
+using w4a8::T3Epi;
 
 namespace {
 
@@ -1153,18 +1154,45 @@ __device__ __forceinline__ void stage_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-template <bool ISUMS>
+// Epilogues of the three-stage unit besides the plain store (kEpiOut):
+//  kEpiSilu  the MoE gate/up product with SiLU(gate) * up folded in.  The weight matrix has
+//            2 * half rows (gate rows [0, half), up rows [half, 2 half)); tile n0 covers h
+//            columns [n0, n0 + 64), and its 128 MFMA columns are ordered so that each wave's
+//            two 32-column blocks are the gate and the up rows of the same 32 h columns: a lane
+//            holds gate and up of one (row, column) pair.  The row's out line (stride ldo =
+//            2 half) receives h in columns [0, half) and, at half + c / 16, the largest |h| of
+//            h columns c .. c + 15 (the per-row maximum is then a maximum of maxima).
+//            gate and up are the fp32 values the plain epilogue would store, and h comes from
+//            the same silu_mul as the unfused kernel, so h is bit-identical to that path's.
+//  kEpiCombine  the MoE down product of the shared expert (rows = tokens), with the weighted
+//            combine folded in: out[t][n] = (sum_j w[t][j] * y[slot(t, j)][n], fused multiply-adds
+//            in j order from 0) + v[t][n], the same operations in the same order as the
+//            combine kernel, where v is this tile's own product (also stored at out as usual).
+//            The tile's values go through LDS so that each thread combines whole float4 runs.
+constexpr int kEpiOut = 0, kEpiSilu = 1, kEpiCombine = 2;
+
+template <bool ISUMS, int EPI = kEpiOut>
 __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restrict__ qa,
                                            const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
                                            int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
                                            const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
                                            int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
-                                           int32_t *__restrict__ isums, int64_t M_isums) {
+                                           int32_t *__restrict__ isums, int64_t M_isums, const T3Epi &ep = T3Epi{}) {
+    static_assert(EPI == kEpiOut || !ISUMS, "the debug form stores int32 sums only");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t G = K / G128;
     auto clampg = [&](int64_t g) { return g < G ? g : G - 1; };
+    // weight row of MFMA column c of the tile (-1: past the matrix)
+    auto wrow = [&](int c) -> int64_t {
+        if constexpr (EPI == kEpiSilu) {
+            const int64_t hc = n0 + (c >> 6) * 32 + (c & 31);
+            return hc < ep.half ? ((c & 32) ? ep.half + hc : hc) : -1;
+        } else {
+            return n0 + c < N ? n0 + c : -1;
+        }
+    };
 
     // row scales and validity of the tile's rows (published by the prologue's barriers)
     __shared__ float row_as[kT3BM];
@@ -1200,7 +1228,7 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     // ---- packed weights: thread t takes column t >> 2, bytes 16 (t & 3) + [0, 16) of a group,
     // with that column's zero point; and this lane's two output columns' scales
     const int bcol = tid >> 2, bpart = tid & 3;
-    const int64_t gcol = (n0 + bcol < N) ? n0 + bcol : 0;
+    const int64_t gcol = wrow(bcol) >= 0 ? wrow(bcol) : 0;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (the debug form reads no scales)
@@ -1210,8 +1238,9 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     uint32_t soff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        scol[j] = n0 + wn * 64 + j * 32 + (lane & 31);
-        soff[j] = (uint32_t)((scol[j] < N ? scol[j] : 0) * 2);
+        const int64_t wr = wrow(wn * 64 + j * 32 + (lane & 31));
+        scol[j] = wr >= 0 ? wr : N;  // (kEpiOut / kEpiCombine: the output column)
+        soff[j] = (uint32_t)((wr >= 0 ? wr : 0) * 2);
     }
     struct Slot {
         v4u rb;
@@ -1345,7 +1374,7 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     if (g < G) body(I0{}, g);
     __builtin_amdgcn_s_waitcnt(0);  // the last (unused) prefetches
 
-    if (!ISUMS) {
+    if constexpr (!ISUMS && EPI == kEpiOut) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1359,25 +1388,114 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
                         if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
                 }
             }
+    } else if constexpr (EPI == kEpiSilu) {
+        const int64_t hc = n0 + wn * 32 + (lane & 31);  // this lane's h column
+        const bool col_ok = hc < ep.half;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                const bool ok = m < rows.rows && row_ok[m];
+                const float as = row_as[m];
+                const float gate = as * acc[i][0][r], up = as * acc[i][1][r];
+                const float h = silu_mul(gate, up);
+                float hm = (ok && col_ok) ? fabsf(h) : 0.0f;
+                // largest |h| over each 16-lane row (one tile row, 16 h columns): DPP steps,
+                // no LDS traffic
+                hm = dpp_max<0xB1>(hm);   // quad_perm [1,0,3,2]
+                hm = dpp_max<0x4E>(hm);   // quad_perm [2,3,0,1]
+                hm = dpp_max<0x124>(hm);  // row_ror:4
+                hm = dpp_max<0x128>(hm);  // row_ror:8
+                if (ok) {
+                    float *line = out + (rows.slot0 + m) * ldo;
+                    if (col_ok) line[hc] = h;
+                    if ((lane & 15) == 0) line[ep.half + (n0 + wn * 32 + (lane & 16)) / 16] = hm;
+                }
+            }
+    } else if constexpr (EPI == kEpiCombine) {
+        // the tile's products -> LDS [256][128] fp32 (the stages are free once every wave is
+        // past its last group), the rows' slots and weights after them
+        __syncthreads();
+        float *ct = reinterpret_cast<float *>(lds);
+        int32_t *tsop = reinterpret_cast<int32_t *>(lds + kT3BM * kT3BN * 4);
+        float *tw = reinterpret_cast<float *>(lds + kT3BM * kT3BN * 4 + kT3BM * 8 * 4);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                const float as = row_as[m];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) ct[m * kT3BN + wn * 64 + j * 32 + (lane & 31)] = as * acc[i][j][r];
+            }
+        for (int idx = tid; idx < rows.rows * ep.k; idx += kT3Threads) {
+            const int m = idx / ep.k, jj = idx - m * ep.k;
+            const int64_t pr = (rows.slot0 + m) * ep.k + jj;
+            tsop[m * 8 + jj] = ep.sop[pr];
+            tw[m * 8 + jj] = ep.tw[pr];
+        }
+        __syncthreads();
+        // thread: float4 column c4 of rows tid / 32 + 16 i; two rows at a time, all their
+        // routed rows' loads issued before the multiply-adds (16 loads in flight per thread)
+        const int c4 = tid & 31;
+        const int64_t col = n0 + 4 * c4;
+        if (col < N) {
+            for (int mb = tid >> 5; mb < rows.rows; mb += 2 * (kT3Threads / 32)) {
+                float4 v[2][8];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int m = mb + q * (kT3Threads / 32);
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        if (m < rows.rows && jj < ep.k)
+                            v[q][jj] = *reinterpret_cast<const float4 *>(ep.y + (int64_t)tsop[m * 8 + jj] * N + col);
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int m = mb + q * (kT3Threads / 32);
+                    if (m >= rows.rows) continue;
+                    const int64_t t = rows.slot0 + m;
+                    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        if (jj < ep.k) {
+                            const float wj = tw[m * 8 + jj];
+                            o.x = fmaf(wj, v[q][jj].x, o.x);
+                            o.y = fmaf(wj, v[q][jj].y, o.y);
+                            o.z = fmaf(wj, v[q][jj].z, o.z);
+                            o.w = fmaf(wj, v[q][jj].w, o.w);
+                        }
+                    }
+                    const float4 sh = *reinterpret_cast<const float4 *>(ct + m * kT3BN + 4 * c4);
+                    o.x += sh.x;
+                    o.y += sh.y;
+                    o.z += sh.z;
+                    o.w += sh.w;
+                    *reinterpret_cast<float4 *>(ep.fin + t * N + col) = o;
+                    *reinterpret_cast<float4 *>(out + t * ldo + col) = sh;
+                }
+            }
+        }
     }
 }
 
-template <bool ISUMS>
+template <bool ISUMS, int EPI = kEpiOut>
 __global__ __launch_bounds__(kT3Threads) void gemm_tiled3_kernel(const int8_t *__restrict__ qa,
                                                                  const float *__restrict__ a_scale, int64_t M,
                                                                  int64_t K, const uint8_t *__restrict__ packed,
                                                                  const uint16_t *__restrict__ scale,
                                                                  const uint16_t *__restrict__ zp, int64_t N,
                                                                  float *__restrict__ out,
-                                                                 int32_t *__restrict__ isums) {
+                                                                 int32_t *__restrict__ isums, T3Epi ep) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     const int64_t mt = (M + kT3BM - 1) / kT3BM, nt = (N + kT3BN - 1) / kT3BN;
     int64_t tm, tn;
     panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
     const int64_t m0 = tm * kT3BM;
     const int rows = (int)((M - m0) < kT3BM ? (M - m0) : kT3BM);
-    tile3_unit<ISUMS>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT3BN, out, N,
-                      isums, M);
+    tile3_unit<ISUMS, EPI>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT3BN, out,
+                           N, isums, M, ep);
 }
 
 template <int WM, int WN, bool ISUMS, int GS>
@@ -1904,15 +2022,18 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
 
 // Experts with more than cmin slots in 256-row tiles of the three-stage loop (the same unit
 // order as grouped_tiled_kernel).
-template <bool ISUMS>
+// EPI = kEpiSilu: the gate/up product with SiLU * up folded in (N = 2 I weight rows, tiles of
+// 64 h columns, out lines of 2 I floats: h, then the per-16-column maxima).
+template <bool ISUMS, int EPI = kEpiOut>
 __global__ __launch_bounds__(kT3Threads) void grouped_tiled3_kernel(
     const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
     const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
-    float *__restrict__ out, int32_t *__restrict__ isums, int64_t cmin) {
+    float *__restrict__ out, int32_t *__restrict__ isums, int64_t cmin, T3Epi ep) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int64_t pfx[kMaxExperts + 1];
-    const int64_t ntn = (N + kT3BN - 1) / kT3BN;
+    constexpr int TBN = EPI == kEpiSilu ? kT3BN / 2 : kT3BN;  // output columns per tile
+    const int64_t ntn = ((EPI == kEpiSilu ? ep.half : N) + TBN - 1) / TBN;
     const int64_t total = expert_prefix(E, pfx, kT3Threads, [&](int e) -> int64_t {
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
         return c > cmin ? ((c + kT3BM - 1) / kT3BM) * ntn : 0;
@@ -1929,9 +2050,9 @@ __global__ __launch_bounds__(kT3Threads) void grouped_tiled3_kernel(
         const int64_t tm = local % mt, tn = local / mt;
         const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * kT3BM;
         const int rows = (int)((c - tm * kT3BM) < kT3BM ? (c - tm * kT3BM) : kT3BM);
-        tile3_unit<ISUMS>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K, packed + (int64_t)e * N * (K / 2),
-                          (ISUMS ? nullptr : scale + (int64_t)e * G * N), zp + (int64_t)e * G * N, N, tn * kT3BN,
-                          out, N, isums, max_slots);
+        tile3_unit<ISUMS, EPI>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
+                               packed + (int64_t)e * N * (K / 2), (ISUMS ? nullptr : scale + (int64_t)e * G * N),
+                               zp + (int64_t)e * G * N, N, tn * TBN, out, N, isums, max_slots, ep);
         __syncthreads();  // the next unit reuses the LDS stages and row tables
     }
 }
@@ -2012,7 +2133,7 @@ hipError_t launch_tiled3(const int8_t *qa, const float *a_scale, int64_t M, int6
                                 kT3Lds) != hipSuccess)                                                              \
             return hipGetLastError();                                                                               \
         hipLaunchKernelGGL((gemm_tiled3_kernel<IS>), grid, block, kT3Lds, stream, qa, a_scale, M, K, packed, scale, \
-                           zp, N, out, isums);                                                                      \
+                           zp, N, out, isums, T3Epi{});                                                             \
     } while (0)
     if (isums) W4A8_T3(true);
     else W4A8_T3(false);
@@ -2284,7 +2405,8 @@ static hipError_t launch_grouped_tiled_s(const int8_t *qa, const float *a_scale,
 static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                        const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                        const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                                       float *out, int32_t *isums, int64_t cmin, int cus, int gs, hipStream_t stream) {
+                                       float *out, int32_t *isums, int64_t cmin, int cus, int gs, hipStream_t stream,
+                                       const T3Epi *silu, int64_t *fused_min) {
     if (max_slots <= cmin) return hipSuccess;
     if (cmin < 128) {
         hipError_t err = launch_grouped_tiled_s<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
@@ -2299,10 +2421,21 @@ static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, i
             return hipGetLastError();                                                                               \
         hipLaunchKernelGGL((grouped_tiled3_kernel<IS>), dim3((uint32_t)cus), dim3(kT3Threads), kT3Lds, stream, qa,  \
                            a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out, isums,  \
-                           (int64_t)128);                                                                           \
+                           (int64_t)128, T3Epi{});                                                                  \
     } while (0)
-        if (isums) W4A8_GT3(true);
-        else W4A8_GT3(false);
+        if (isums) {
+            W4A8_GT3(true);
+        } else if (silu) {  // the >128-slot experts with SiLU * up folded into the epilogue
+            if (hipFuncSetAttribute((const void *)grouped_tiled3_kernel<false, kEpiSilu>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kT3Lds) != hipSuccess)
+                return hipGetLastError();
+            hipLaunchKernelGGL((grouped_tiled3_kernel<false, kEpiSilu>), dim3((uint32_t)cus), dim3(kT3Threads), kT3Lds,
+                               stream, qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N,
+                               max_slots, out, isums, (int64_t)128, *silu);
+            if (fused_min) *fused_min = 128;
+        } else {
+            W4A8_GT3(false);
+        }
 #undef W4A8_GT3
         return hipGetLastError();
     }
@@ -2313,7 +2446,8 @@ static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, i
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int64_t max_slots,
-                               int64_t max_per_expert, float *out, int32_t *isums, int gs, hipStream_t stream) {
+                               int64_t max_per_expert, float *out, int32_t *isums, int gs, hipStream_t stream,
+                               const T3Epi *silu, int64_t *fused_min) {
     if (max_per_expert > max_slots) max_per_expert = max_slots;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -2364,7 +2498,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         }
         if (max_per_expert <= cmin) return hipSuccess;
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, isums, cmin, cus, gs, stream);
+                                    out, isums, cmin, cus, gs, stream, silu, fused_min);
     }
     // the decode loop stages gathered rows with 32-bit offsets (row * K) and addresses the
     // codes with 32-bit offsets; larger inputs take the streaming loop (64-bit addresses)
@@ -2412,7 +2546,8 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
         if (!mid) return max_per_expert <= kSmallRows ? hipSuccess
                                                       : launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets,
                                                                              E, K, packed, scale, zp, N, max_slots, out,
-                                                                             isums, kSmallRows, cus, G128, stream);
+                                                                             isums, kSmallRows, cus, G128, stream, silu,
+                                                                             fused_min);
         // the other loops only when some expert can have that many slots
 #define W4A8_GMID1(MF, CMIN, CMAX, IS)                                                                              \
     do {                                                                                                            \
@@ -2433,7 +2568,7 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
 #undef W4A8_GMID1
         if (max_per_expert <= kMidMax) return hipSuccess;
         return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots,
-                                    out, isums, kMidMax, cus, G128, stream);
+                                    out, isums, kMidMax, cus, G128, stream, silu, fused_min);
     }
     const int U = ring_depth(G, 4);
     const dim3 sgrid((uint32_t)(cus * 8)), sblock(kStreamThreads);
@@ -2453,7 +2588,31 @@ hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || max_per_expert <= kSmallRows) return err;
     return launch_grouped_tiled(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,
-                                isums, kSmallRows, cus, G128, stream);
+                                isums, kSmallRows, cus, G128, stream, silu, fused_min);
+}
+
+// The MoE shared expert's down product (T token rows) with the weighted combine folded in.
+bool shared_combine_fits(int64_t T, int64_t I, int64_t H, int32_t topk) {
+    return T > 128 && topk <= 8 && H % 4 == 0 && tiled3_fits(T, I, H);
+}
+
+hipError_t launch_shared_combine(const int8_t *qh, const float *h_scale, int64_t T, int64_t I, const uint8_t *packed,
+                                 const uint16_t *scale, const uint16_t *zp, int64_t H, float *y_shared,
+                                 const float *y, const int32_t *slot_of_pair, const float *topk_w, int32_t topk,
+                                 float *out, hipStream_t stream) {
+    const int64_t tiles = ((T + kT3BM - 1) / kT3BM) * ((H + kT3BN - 1) / kT3BN);
+    T3Epi ep{};
+    ep.y = y;
+    ep.sop = slot_of_pair;
+    ep.tw = topk_w;
+    ep.k = topk;
+    ep.fin = out;
+    if (hipFuncSetAttribute((const void *)gemm_tiled3_kernel<false, kEpiCombine>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kT3Lds) != hipSuccess)
+        return hipGetLastError();
+    hipLaunchKernelGGL((gemm_tiled3_kernel<false, kEpiCombine>), dim3((uint32_t)tiles), dim3(kT3Threads), kT3Lds,
+                       stream, qh, h_scale, T, I, packed, scale, zp, H, y_shared, (int32_t *)nullptr, ep);
+    return hipGetLastError();
 }
 
 }  // namespace w4a8

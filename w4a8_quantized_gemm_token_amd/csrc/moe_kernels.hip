@@ -241,14 +241,26 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *_
     const int64_t c4 = (int64_t)blockIdx.y * kCombineThreads + threadIdx.x;
     if (c4 * 4 >= H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float wj = topk_w[t * k + j];
-        const int64_t s = slot_of_pair[t * k + j];
-        const float4 v = reinterpret_cast<const float4 *>(y + s * H)[c4];
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-        acc.z = fmaf(wj, v.z, acc.z);
-        acc.w = fmaf(wj, v.w, acc.w);
+    // eight routed rows at a time, every load issued before the multiply-adds (in j order)
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float4 v[8];
+        float wv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (j0 + jj < k) {
+                wv[jj] = topk_w[t * k + j0 + jj];
+                v[jj] = reinterpret_cast<const float4 *>(y + (int64_t)slot_of_pair[t * k + j0 + jj] * H)[c4];
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (j0 + jj < k) {
+                acc.x = fmaf(wv[jj], v[jj].x, acc.x);
+                acc.y = fmaf(wv[jj], v[jj].y, acc.y);
+                acc.z = fmaf(wv[jj], v[jj].z, acc.z);
+                acc.w = fmaf(wv[jj], v[jj].w, acc.w);
+            }
+        }
     }
     if (y_shared) {
         const float4 v = reinterpret_cast<const float4 *>(y_shared + t * H)[c4];

@@ -128,8 +128,6 @@ __global__ __launch_bounds__(kRowThreads) void quantize_act_row_kernel(const flo
     }
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
 // One workgroup per row p of gu [P][2I]; h lives in registers between the max
 // and the quantization (VPT4 float4 per thread covers I <= 4 * VPT4 * 256).
 template <int VPT4>
@@ -186,6 +184,71 @@ __global__ __launch_bounds__(kActThreads) void silu_mul_quantize_long_kernel(con
     const float s = amax / 127.0f;
     if (threadIdx.x == 0) h_scale[p] = s;
     for (int64_t c = threadIdx.x; c < I; c += kActThreads) qh[p * I + c] = (int8_t)quantize_i8(silu_mul(gate[c], up[c]), s);
+}
+
+// The MoE requant after the gate/up product, kRequantRows slots per workgroup.  A slot of an
+// expert with more than fused_min slots holds h [I] and the maxima of |h| over each 16
+// columns [I / 16] (the fused gate/up epilogue), the others gate [I] | up [I].  The row
+// maximum of |h| is the same number either way (a maximum of maxima), so the codes and
+// scales are those of silu_mul_quantize_kernel for the same h.
+constexpr int kRequantRows = 8;
+constexpr int kMaxOffsets = 1025;
+template <int VPT4>
+__global__ __launch_bounds__(kActThreads) void moe_requant_kernel(const float *__restrict__ gu, int64_t S, int64_t I,
+                                                                  const int32_t *__restrict__ offsets, int32_t E1,
+                                                                  int64_t fused_min, int8_t *__restrict__ qh,
+                                                                  float *__restrict__ h_scale) {
+    __shared__ float red[kActWaves];
+    __shared__ int32_t off[kMaxOffsets];
+    for (int e = threadIdx.x; e <= E1; e += kActThreads) off[e] = offsets[e];
+    __syncthreads();
+    const int64_t I4 = I / 4;
+    const int64_t p1 = ((int64_t)blockIdx.x + 1) * kRequantRows < S ? ((int64_t)blockIdx.x + 1) * kRequantRows : S;
+    for (int64_t p = (int64_t)blockIdx.x * kRequantRows; p < p1; ++p) {
+        // the expert of slot p: the last e with off[e] <= p
+        int lo = 0, hi = E1;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= p) lo = mid;
+            else hi = mid;
+        }
+        const bool fused = (int64_t)(off[lo + 1] - off[lo]) > fused_min;
+        const float4 *line = reinterpret_cast<const float4 *>(gu + p * 2 * I);
+        float4 h[VPT4];
+        float amax = 0.0f;
+        if (fused) {
+#pragma unroll
+            for (int i = 0; i < VPT4; ++i) {
+                const int64_t c = threadIdx.x + (int64_t)i * kActThreads;
+                if (c < I4) h[i] = line[c];
+            }
+            for (int64_t c = threadIdx.x; c < I / 16; c += kActThreads) amax = fmaxf(amax, gu[p * 2 * I + I + c]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VPT4; ++i) {
+                const int64_t c = threadIdx.x + (int64_t)i * kActThreads;
+                if (c < I4) {
+                    const float4 g = line[c], u = line[I4 + c];
+                    h[i] = make_float4(silu_mul(g.x, u.x), silu_mul(g.y, u.y), silu_mul(g.z, u.z),
+                                       silu_mul(g.w, u.w));
+                    amax = fmaxf(amax,
+                                 fmaxf(fmaxf(fabsf(h[i].x), fabsf(h[i].y)), fmaxf(fabsf(h[i].z), fabsf(h[i].w))));
+                }
+            }
+        }
+        amax = block_max(amax, red);
+        const float s = amax / 127.0f;
+        if (threadIdx.x == 0) h_scale[p] = s;
+        uint32_t *out = reinterpret_cast<uint32_t *>(qh + p * I);
+#pragma unroll
+        for (int i = 0; i < VPT4; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * kActThreads;
+            if (c < I4)
+                out[c] = pack4_i8(quantize_i8(h[i].x, s), quantize_i8(h[i].y, s), quantize_i8(h[i].z, s),
+                                  quantize_i8(h[i].w, s));
+        }
+        __syncthreads();  // red is reused by the next row
+    }
 }
 
 // One wave per unit of one output feature n and SPAN consecutive k (128, or 256 for GS 256):
@@ -361,6 +424,24 @@ hipError_t launch_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_
     else
         hipLaunchKernelGGL(silu_mul_quantize_long_kernel, dim3((uint32_t)P), dim3(kActThreads), 0, stream, gu, I, qh,
                            h_scale, h_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_requant(const float *gu, int64_t S, int64_t I, const int32_t *offsets, int32_t E1,
+                              int64_t fused_min, int8_t *qh, float *h_scale, hipStream_t stream) {
+    const int64_t I4 = I / 4;
+    // no fused rows, or rows the fused kernel does not take: the plain kernel
+    if (fused_min == INT64_MAX || E1 + 1 > kMaxOffsets || I % 128 != 0 || I4 > kActThreads * 4 ||
+        (uintptr_t)gu % 16 != 0)
+        return fused_min == INT64_MAX ? launch_silu_mul_quantize(gu, S, I, qh, h_scale, nullptr, stream)
+                                      : hipErrorInvalidValue;
+    const dim3 grid((uint32_t)((S + kRequantRows - 1) / kRequantRows));
+    if (I4 <= kActThreads * 2)
+        hipLaunchKernelGGL(moe_requant_kernel<2>, grid, dim3(kActThreads), 0, stream, gu, S, I, offsets, E1,
+                           fused_min, qh, h_scale);
+    else
+        hipLaunchKernelGGL(moe_requant_kernel<4>, grid, dim3(kActThreads), 0, stream, gu, S, I, offsets, E1,
+                           fused_min, qh, h_scale);
     return hipGetLastError();
 }
 

@@ -43,16 +43,46 @@ hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64
                                    const uint16_t *scale, const uint16_t *zp, int64_t N, int group, int path, float *out,
                                    int32_t *isums, hipStream_t stream);
 
+// Extra operands of the fused MoE epilogues of the three-stage tiled loop.
+struct T3Epi {
+    int64_t half = 0;               // gate/up with SiLU * up: I (gate rows [0, I), up rows [I, 2I))
+    const float *y = nullptr;       // shared-expert combine: routed down rows [*][H]
+    const int32_t *sop = nullptr;   //   slot of pair (t, j), [T][k]
+    const float *tw = nullptr;      //   routing weights [T][k]
+    int32_t k = 0;                  //   routed experts per token (<= 8)
+    float *fin = nullptr;           //   layer output [T][H]
+};
+
 // max_per_expert: a bound on any one expert's slot count known to the caller (the
 // MoE layer knows no expert gets more than T); loops for larger experts are not
 // launched.  max_slots when nothing better is known.  isums != nullptr selects the
 // debug form: per-group int32 sums isums[K/group][max_slots][N] instead of `out`.
 // group: 64, 128 or 256 (scale/zp [E][K/group][N]).
+// silu (group 128, MoE gate/up with N = 2 silu->half): experts that take the three-stage
+// tiled loop (more than 128 slots) get SiLU(gate) * up in their epilogue: their out line
+// holds h [half] and then the per-16-column maxima of |h| [half / 16] instead of gate | up;
+// *fused_min is then set to 128 (left alone when no expert can take that loop).
 hipError_t launch_grouped_gemm(const int8_t *qa, const float *a_scale, int64_t R,
                                const int32_t *row_index, const int32_t *expert_offsets, int32_t E,
                                int64_t K, const uint8_t *packed, const uint16_t *scale,
                                const uint16_t *zp, int64_t N, int64_t max_slots, int64_t max_per_expert,
-                               float *out, int32_t *isums, int group, hipStream_t stream);
+                               float *out, int32_t *isums, int group, hipStream_t stream,
+                               const T3Epi *silu = nullptr, int64_t *fused_min = nullptr);
+
+// The MoE requant after the gate/up product: rows of experts (E1 of them, slots
+// offsets[e] .. offsets[e+1]) with more than fused_min slots hold h and its per-16-column
+// maxima (above), the others gate | up; qh and h_scale as launch_silu_mul_quantize.
+hipError_t launch_moe_requant(const float *gu, int64_t S, int64_t I, const int32_t *offsets, int32_t E1,
+                              int64_t fused_min, int8_t *qh, float *h_scale, hipStream_t stream);
+
+// The MoE shared expert's down product over its T token rows (qh, h_scale of those rows)
+// with the weighted combine folded in: y_shared [T][H] receives the product, out [T][H]
+// the layer output sum_j w[t][j] y[slot(t, j)] + y_shared[t] (the combine kernel's order).
+bool shared_combine_fits(int64_t T, int64_t I, int64_t H, int32_t topk);
+hipError_t launch_shared_combine(const int8_t *qh, const float *h_scale, int64_t T, int64_t I, const uint8_t *packed,
+                                 const uint16_t *scale, const uint16_t *zp, int64_t H, float *y_shared,
+                                 const float *y, const int32_t *slot_of_pair, const float *topk_w, int32_t topk,
+                                 float *out, hipStream_t stream);
 
 // Tile-major weights for the decode loop (M <= 16): bytes of the array, whether a
 // shape is served, the GEMM over it, and the conversion from the standard layout.
@@ -128,6 +158,17 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 }
 __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// The MoE expert activation SiLU(g) * u = g / (1 + e^-g) * u, with e^-g = 2^(-g log2 e) from
+// the hardware base-2 exponential and the quotient as g times the hardware reciprocal (about
+// 1 ulp each; relative error a few 1e-7 for |g| < 20): a few instructions where the library
+// exp and the correctly rounded divide take some twenty, which matters in the gate/up
+// epilogue.  One definition for the unfused kernel and the fused epilogue, so both give the
+// same bits.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // Per-token symmetric INT8 code of v for a row scale s (s == 0 -> 0).
