@@ -1284,6 +1284,59 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     float sc[2] = {0.0f, 0.0f}, scn[2];
+    // Rolling fold (plain epilogue): the four 32x32 chains of a group run one after the
+    // other, (0,0), (0,1), (1,0), (1,1), and each chain's 16 int32 sums are folded into fp32
+    // while the next chain's four MFMAs execute, so the conversions and fused multiply-adds
+    // issue between MFMAs instead of after them.  The last chain of group g is folded during
+    // the first chain of group g + 1 (prev, with that group's scale).  Every element still
+    // takes its groups in increasing g, one fmaf each: the same operations as the plain loop.
+    v16i prev = {};
+    float prev_sc = 0.0f;  // fmaf(0, 0, acc) == acc before the first group
+    auto fold = [&](const v16i &dd, int i, int j, float s_) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s_, (float)dd[r], acc[i][j][r]);
+    };
+    auto chain = [&](const v4i *a, const v4i *b) {
+        v16i dd = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], v16i{}, 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < 4; ++ks) dd = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ks], b[ks], dd, 0, 0, 0);
+        return dd;
+    };
+    auto interleave = [&]() {  // four MFMAs, each followed by eight VALU instructions
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+    };
+    auto group_rolling = [&](int st) {
+        const uint8_t *base = lds + st * kT3Stage;
+        // every fragment of the group is requested up front (in the order the chains use them)
+        v4i a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            a0[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks]);
+            b0[ks] = *reinterpret_cast<const v4i *>(base + bofs[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b1[ks] = *reinterpret_cast<const v4i *>(base + bofs[ks] + 4096);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a1[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks] + 4096);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        const v16i d00 = chain(a0, b0);
+        fold(prev, 1, 1, prev_sc);
+        interleave();
+        const v16i d01 = chain(a0, b1);
+        fold(d00, 0, 0, sc[0]);
+        interleave();
+        const v16i d10 = chain(a1, b0);
+        fold(d01, 0, 1, sc[1]);
+        interleave();
+        prev = chain(a1, b1);
+        fold(d10, 1, 0, sc[0]);
+        interleave();
+        prev_sc = sc[1];
+    };
     auto group = [&](int st, int64_t g) {
         const uint8_t *base = lds + st * kT3Stage;
         v16i d[2][2];
@@ -1350,7 +1403,8 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         b_load(fill, clampg(g + 2));
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        group(st0, g);
+        if constexpr (ISUMS) group(st0, g);
+        else group_rolling(st0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(t3_waitcnt(8, 15));
         b_store(next, st1);
@@ -1373,6 +1427,7 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     }
     if (g < G) body(I0{}, g);
     __builtin_amdgcn_s_waitcnt(0);  // the last (unused) prefetches
+    if constexpr (!ISUMS) fold(prev, 1, 1, prev_sc);  // the last group's last chain
 
     if constexpr (!ISUMS && EPI == kEpiOut) {
 #pragma unroll
