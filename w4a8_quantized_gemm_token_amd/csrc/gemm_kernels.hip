@@ -1944,7 +1944,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
         const int64_t nqrow = more ? qa_row(nxt, srow_t) : qrow;
         const float nasc = (more && tid < RM) ? row_scale(nxt, tid) : 0.0f;
         // 32-row fragments that hold rows of this expert (wave-uniform)
-        const int mt = cur.c > 32 ? MF : 1;
+        const int mt = cur.c > 32 * (MF - 1) ? MF : (int)((cur.c + 31) / 32);
         float acc[MF][16];
 #pragma unroll
         for (int f = 0; f < MF; ++f)
@@ -1964,11 +1964,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
                 __asm__ volatile("" : "+v"(sc));
                 const uint32_t d8[8] = {rw0[slot].x, rw0[slot].y, rw0[slot].z, rw0[slot].w,
                                         rw1[slot].x, rw1[slot].y, rw1[slot].z, rw1[slot].w};
-                v16i dacc[MF];
-#pragma unroll
-                for (int f = 0; f < MF; ++f)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) dacc[f][i] = 0;
+                v16i dacc[MF];  // (the first step starts from an inline zero: no register clearing)
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
                     const uint32_t a0 = d8[2 * s4], a1 = d8[2 * s4 + 1];
@@ -1980,7 +1976,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
                     for (int f = 0; f < MF; ++f) {
                         if (f >= mt) break;
                         const v4i av = *reinterpret_cast<const v4i *>(abuf + f * 32 * kMidRow + gs * G128 + 16 * s4);
-                        dacc[f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bq, dacc[f], 0, 0, 0);
+                        dacc[f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bq, s4 ? dacc[f] : v16i{}, 0, 0, 0);
                     }
                 }
 #pragma unroll
