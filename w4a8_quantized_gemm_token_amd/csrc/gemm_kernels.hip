@@ -1750,24 +1750,34 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
         const bool restage = e != staged_e || chunk != staged_chunk;
         if (restage) {
             __syncthreads();  // every wave is done with the previous rows
-            if (threadIdx.x < 16) {
-                int32_t row = -1;
-                if ((int)threadIdx.x < rows) {
-                    const int64_t r = row_index ? (int64_t)row_index[s0 + threadIdx.x] : s0 + threadIdx.x;
-                    row = (r >= 0 && r < R) ? (int32_t)r : -1;
-                }
-                srow[threadIdx.x] = row;
-            }
-            __syncthreads();
             staged_e = e;
             staged_chunk = chunk;
         }
         const uint8_t *wpk = packed + (int64_t)e * N * (K / 2);
         const uint16_t *wsc = scale + (int64_t)e * (K / GS) * N, *wzp = zp + (int64_t)e * (K / GS) * N;
+        // This chunk's row indices are requested in stage(0), before the first weight windows,
+        // by every thread (thread t reads slot s0 + min(t % 16, rows - 1): one uniform load, no
+        // branch), so that waiting for them later waits for none of the weight loads (the
+        // memory counter retires loads in order).  Only the expert's offsets then stand
+        // between the launch and the first weight load.
+        int32_t ridx = 0;
         auto stage = [&](int phase) {  // the chunk's activation rows -> LDS (only when they
                                        // changed); rows outside [0, R) read row 0 and are
                                        // never stored.  The row scales load alongside.
-            if (phase == 0 || !restage) return;
+            if (!restage) return;
+            if (phase == 0) {
+                const int tr = (int)(threadIdx.x & 15) < rows ? (int)(threadIdx.x & 15) : rows - 1;
+                // (an always-valid address when there is no row index: no branch around the load)
+                const int32_t *src = row_index ? row_index + s0 + tr : offsets;
+                const int32_t v = *src;
+                ridx = row_index ? v : (int32_t)(s0 + tr);
+                return;
+            }
+            if (threadIdx.x < 16) {
+                const bool ok = (int)threadIdx.x < rows && ridx >= 0 && (int64_t)ridx < R;
+                srow[threadIdx.x] = ok ? ridx : -1;
+            }
+            __syncthreads();
             stage_rows_dma(dsm, lda, qa, K, rows, [&](int r) { return (int64_t)(srow[r] >= 0 ? srow[r] : 0); });
             float asc = 0.0f;
             if (!ISUMS && threadIdx.x < 16) {
