@@ -125,6 +125,36 @@ def summarize_traffic(fetch_csv, write_csv, cmd):
     return "\n".join(out)
 
 
+def summarize_kernel_traffic(fetch_csv, write_csv, cmd, kernel):
+    """Text summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) for every kernel whose
+    name contains `kernel`: HBM bytes per dispatch (mean, min, max), each counter scaled by what it
+    reads for one plain 512 MiB device copy in the same process."""
+    out = [f"# HBM traffic per dispatch of kernels matching '{kernel}'",
+           "# commands (run from /tmp with TMPDIR=/tmp; <repo> = the repository root):"]
+    for c in cmd:
+        out.append("#   " + c)
+    scaled = {}
+    for label, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == label]
+        cop = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not cop:
+            raise SystemExit(f"{path}: no copy dispatch with {label}")
+        factor = COPY_BYTES / (max(cop) * 1024.0)
+        out.append(f"{label.lower()}_scale: {factor:.4f}")
+        for r in rows:
+            if kernel in r["Kernel_Name"]:
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+                scaled.setdefault(name.strip(), {}).setdefault(label, []).append(
+                    float(r["Counter_Value"]) * 1024.0 * factor)
+    for name, d in sorted(scaled.items()):
+        for label in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = d.get(label, [])
+            if v:
+                out.append(f"{name} {label.lower()}_bytes: mean {np.mean(v):.0f} min {np.min(v):.0f} "
+                           f"max {np.max(v):.0f} ({len(v)} dispatches)")
+    return "\n".join(out)
+
+
 def summarize_stats(stats_csv, cmd, top=12):
     """Short text table of a rocprofv3 --kernel-trace --stats kernel summary."""
     rows = _counter_rows(stats_csv)
@@ -196,7 +226,9 @@ def parse():
                    help="print a short table of a rocprofv3 kernel_stats.csv; no GPU")
     p.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV",
                    help="print the mean SQ/GRBM counters of --kernel over rocprofv3 --pmc runs; no GPU")
-    p.add_argument("--kernel", default="gemm_tiled_kernel", help="kernel named by --summarize-counters")
+    p.add_argument("--kernel", default="gemm_tiled3_kernel", help="kernel named by --summarize-counters")
+    p.add_argument("--summarize-kernel-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="print the HBM traffic per dispatch of the kernels matching --kernel; no GPU")
     p.add_argument("--cmd", action="append", default=[], help="command text recorded in a summary")
     p.add_argument("--only", choices=["prefill", "toy_moe", "moe_ffn"],
                    help="run one secondary workload alone and print its figures (for counter runs)")
@@ -552,10 +584,22 @@ def moe_ffn_layer(torch, w4, synthetic, tokens, reps=5):
     return out
 
 
+def profile_copy(torch):
+    """One plain 512 MiB device copy: the known-size dispatch that calibrates the HBM counters."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, args.cmd))
+        return
+    if args.summarize_kernel_traffic:
+        print(summarize_kernel_traffic(*args.summarize_kernel_traffic, args.cmd, args.kernel))
         return
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.cmd))
@@ -573,15 +617,17 @@ def main():
     import w4a8_quantized_gemm_token_amd as w4
 
     w4.load()
-    if args.only == "prefill":
-        print(json.dumps({f"prefill_M4096_K8192_N8192_group{args.group}": prefill(torch, w4, synthetic, args.reps,
-                                                                                   args.group)}), flush=True)
-        return
-    if args.only == "toy_moe":
-        print(json.dumps(toy_moe(torch, w4, synthetic, args.size or (1, 2, 4, 512), args.reps)), flush=True)
-        return
-    if args.only == "moe_ffn":
-        print(json.dumps(moe_ffn_layer(torch, w4, synthetic, args.size or (64, 4096), args.reps)), flush=True)
+    if args.only:
+        if args.only == "prefill":
+            res = {f"prefill_M4096_K8192_N8192_group{args.group}": prefill(torch, w4, synthetic, args.reps,
+                                                                            args.group)}
+        elif args.only == "toy_moe":
+            res = toy_moe(torch, w4, synthetic, args.size or (1, 2, 4, 512), args.reps)
+        else:
+            res = moe_ffn_layer(torch, w4, synthetic, args.size or (64, 4096), args.reps)
+        if args.profile_copy:
+            profile_copy(torch)
+        print(json.dumps(res), flush=True)
         return
     layers, tms, xs = decode_setup(torch, w4, synthetic, args.copies)
     ms_per_step, step_bytes, gemm_bytes, gemm_ms, per_m, warmed_s = run_decode(
@@ -592,11 +638,7 @@ def main():
         std_per_m = run_decode(torch, w4, lambda qa, sc, i, out: w4.prepare_gemm(qa, sc, *layers[i], out),
                                len(layers), xs, args.steps, 200)[4]
     if args.profile_copy:
-        a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        profile_copy(torch)
     del layers, tms
     torch.cuda.empty_cache()
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
