@@ -249,29 +249,21 @@ def test_moe_ffn_full_size_stagewise(orc, T):
         assert (err <= bound).all(), f"token {t}: worst {err.max():.3e} vs bound {bound[err.argmax()]:.3e}"
 
 
-def test_moe_ffn_fused_epilogues(orc):
-    """The layer's fused steps on E=8 routed experts + 1 shared, top-3, H=640, I=384, T=300
-    skewed tokens (seed 0: experts of 258, 199, 141 and, shared, 300 slots take the tiled loop
-    with SiLU * up in the gate/up epilogue; 103, 69, 47, 46 and 37 do not; T > 128 folds the
-    combine into the shared expert's down product).  Against the unfused entry points on the
-    same data, bit for bit: h of the fused rows (and their per-16-column maxima), gate | up of
-    the others, the codes and row scales, and the layer output against the combine kernel over
-    the layer's own down rows.  Against the oracle: the codes against the per-token quantizer
-    on the GPU's own h, the shared expert's down rows on the GPU's codes, and every token's
-    output through the oracle's independent chain."""
+def _check_fused_layer(orc, E, k, H, I, T, x, logits, seed, counts_expected):
+    """The layer's fused steps against the unfused entry points on the same data, bit for bit (h
+    and per-16-column maxima of the fused lines, gate | up of the others, codes, row scales, the
+    output against the combine kernel over the layer's own down rows), and against the oracle
+    (codes on the GPU's own h, the shared expert's down rows, every token end to end)."""
     import w4a8_quantized_gemm_token_amd as w4
-    E, k, H, I, T = 8, 3, 640, 384, 300
-    gate_up = device_experts(0, synthetic.TAG_W, E + 1, 2 * I, H)
-    down = device_experts(0, synthetic.TAG_W_DOWN, E + 1, H, I)
-    x = synthetic.activations(0, T, H)
-    logits = synthetic.router_logits_skewed(0, T, E)
+    gate_up = device_experts(seed, synthetic.TAG_W, E + 1, 2 * I, H)
+    down = device_experts(seed, synthetic.TAG_W_DOWN, E + 1, H, I)
     out, inter = _run_gpu_ffn(x, logits, k, gate_up, down)
     ids_r, w_r = orc.route_topk(logits, k)
     assert np.array_equal(to_host(inter["ids"]), ids_r)
     P, S = T * k, T * k + T
     offsets = to_host(inter["offsets"])
     counts = np.diff(offsets)
-    assert sorted(counts[:E].tolist(), reverse=True) == [258, 199, 141, 103, 69, 47, 46, 37] and counts[E] == T
+    assert counts.tolist() == counts_expected, counts.tolist()
     fused = np.repeat(counts > 128, counts)                       # per slot
     # the unfused chain on the same data: grouped GEMM over every expert, then the silu kernel
     gu_u = w4.moe_grouped_gemm(inter["qa"], inter["a_scale"], inter["row_index"], inter["offsets"], *gate_up,
@@ -286,12 +278,12 @@ def test_moe_ffn_fused_epilogues(orc):
     assert np.array_equal(qh, qh_u) and np.array_equal(hs.view(np.uint32), hs_u.view(np.uint32))
     q_o2, s_o2 = orc.quantize_act(h_u)
     assert np.array_equal(qh, q_o2) and np.array_equal(hs.view(np.uint32), s_o2.view(np.uint32))
-    # the shared expert's down rows (written by the fused epilogue) on the GPU's codes
+    # the shared expert's down rows (written by the fused epilogue when T > 128) on the GPU's codes
     y = to_host(inter["y"])
-    qd, sd, zd = orc.quantize_weights(synthetic.weights(0, synthetic.TAG_W_DOWN, E, H, I))
+    qd, sd, zd = orc.quantize_weights(synthetic.weights(seed, synthetic.TAG_W_DOWN, E, H, I))
     yr, mag = orc.gemm(qh[P:], hs[P:], qd, sd, zd)
     check_close(y[P:], yr, mag, "shared expert down rows")
-    # the folded combine gives the combine kernel's bits over the layer's own rows
+    # the layer output is the combine kernel's bits over the layer's own rows
     comb = to_host(w4.moe_combine(inter["y"][:P], inter["slot_of_pair"].view(T, k), inter["w"],
                                   y_shared=inter["y"][P:]))
     assert np.array_equal(out.view(np.uint32), comb.view(np.uint32)), "folded combine"
@@ -300,15 +292,40 @@ def test_moe_ffn_fused_epilogues(orc):
 
     def gu_q(e):
         if e not in cache_gu:
-            cache_gu[e] = orc.quantize_weights(synthetic.weights(0, synthetic.TAG_W, e, 2 * I, H))
+            cache_gu[e] = orc.quantize_weights(synthetic.weights(seed, synthetic.TAG_W, e, 2 * I, H))
         return cache_gu[e]
 
     def d_q(e):
         if e not in cache_d:
-            cache_d[e] = orc.quantize_weights(synthetic.weights(0, synthetic.TAG_W_DOWN, e, H, I))
+            cache_d[e] = orc.quantize_weights(synthetic.weights(seed, synthetic.TAG_W_DOWN, e, H, I))
         return cache_d[e]
 
     for t in range(T):
         ref, tol = oracle_token(orc, x[t], list(ids_r[t]) + [E], list(w_r[t]) + [1.0], gu_q, d_q, I)
         err = np.abs(out[t] - ref)
         assert (err <= tol).all(), f"token {t}: worst {err.max():.3e} vs tol {tol[err.argmax()]:.3e}"
+
+
+def test_moe_ffn_fused_epilogues(orc):
+    """E=8 routed experts + 1 shared, top-3, H=640, I=384, T=300 skewed tokens (seed 0: experts of
+    258, 199, 141 and, shared, 300 slots take the tiled loop with SiLU * up in the gate/up
+    epilogue; 103, 69, 47, 46 and 37 do not; T > 128 folds the combine into the shared expert's
+    down product)."""
+    E, k, H, I, T = 8, 3, 640, 384, 300
+    x = synthetic.activations(0, T, H)
+    logits = synthetic.router_logits_skewed(0, T, E)
+    counts = np.bincount(np.argsort(-logits, axis=1, kind="stable")[:, :k].ravel(), minlength=E)
+    assert sorted(counts.tolist(), reverse=True) == [258, 199, 141, 103, 69, 47, 46, 37]
+    _check_fused_layer(orc, E, k, H, I, T, x, logits, 0, counts.tolist() + [T])
+
+
+def test_moe_ffn_fused_thresholds(orc):
+    """The fold thresholds exactly: two routed experts of 129 and 128 slots (the first takes the
+    SiLU fold, the second not) and the shared expert of T = 257 slots (two row tiles, the second
+    one row, with the combine folded in); top-1, H=256, I=256, routing fixed by the logits."""
+    E, k, H, I, T = 2, 1, 256, 256, 257
+    x = synthetic.activations(5, T, H)
+    logits = np.zeros((T, E), np.float32)
+    logits[:129, 0] = 1.0
+    logits[129:, 1] = 1.0
+    _check_fused_layer(orc, E, k, H, I, T, x, logits, 5, [129, 128, T])
