@@ -326,9 +326,12 @@ w4a8_status w4a8_moe_grouped_gemm_debug_isums(const int8_t *qa, int64_t R, const
 
 /* Device.  MoE expert activation then per-row re-quantization to INT8:
  * h = silu(gate) * up with gate = gu[p][0..I), up = gu[p][I..2I),
- * silu(v) = v / (1 + exp(-v)) in fp32; then the per-token quantizer above on
- * each row of h: qh[P][I], h_scale[P].  h_out[P][I] (optional, may be NULL)
- * receives the fp32 h.  Errors: W4A8_EINVAL (null, P < 0, I <= 0, I % 16). */
+ * silu(v) * u = v * (1 / (1 + 2^(-v log2 e))) * u in fp32 with the hardware
+ * base-2 exponential and reciprocal (about 1 ulp each, relative error a few 1e-7;
+ * the pages fix no precision for the activation); then the per-token quantizer
+ * above on each row of h: qh[P][I], h_scale[P].  h_out[P][I] (optional, may be
+ * NULL) receives the fp32 h that was quantized.  Errors: W4A8_EINVAL (null,
+ * P < 0, I <= 0, I % 16). */
 w4a8_status w4a8_silu_mul_quantize(const float *gu, int64_t P, int64_t I, int8_t *qh,
                                    float *h_scale, float *h_out, hipStream_t stream);
 
