@@ -520,7 +520,9 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
     //  GS 128: lanes kq = 0..3 read scale[2w], scale[2w+1], zp[2w], zp[2w+1]
     //  GS 256: lanes kq < 2 read scale[w], lanes kq >= 2 read zp[w]
     //  GS 64:  lane kq reads scale[4w + kq] (rsz) and zp[4w + kq] (rszb)
-    // (the debug form stores int32 sums and reads no scales: those lanes read zero points)
+    // (the debug form stores int32 sums and reads no scales: the lanes that hold scale words
+    // load nothing; their address is formed over the zero points)
+    const bool sz_load = !ISUMS || (GS != 64 && kq >= 2);
     const uint16_t *szbase =
         TM ? nullptr
            : (GS == 64 ? (ISUMS ? wzp : wsc) + kq * N
@@ -554,7 +556,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
         } else {
             rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o, 0, 2);
             rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, o + (uint32_t)(8 * (K / 2)), 0, 2);
-            rsz[u] = szbase[tile * 16 + SZSTEP * w * N];
+            rsz[u] = sz_load ? szbase[tile * 16 + SZSTEP * w * N] : 0u;
             if constexpr (GS == 64) rszb[u] = zbase64[tile * 16 + SZSTEP * w * N];
         }
     };
@@ -577,7 +579,7 @@ __device__ __forceinline__ void dec_tiles(const uint8_t *rows, float *red, int M
                 rb0[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o : 0xFFFFFFF0u, 0, 2);
                 rb1[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, has ? o + (uint32_t)(8 * (K / 2)) : 0xFFFFFFF0u, 0,
                                                               2);
-                rsz[u] = szbase[tile * 16 + SZSTEP * (win0 + u) * N];
+                rsz[u] = sz_load ? szbase[tile * 16 + SZSTEP * (win0 + u) * N] : 0u;
                 if constexpr (GS == 64) rszb[u] = zbase64[tile * 16 + SZSTEP * (win0 + u) * N];
             }
         }
@@ -1231,7 +1233,7 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     const int64_t gcol = wrow(bcol) >= 0 ? wrow(bcol) : 0;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (the debug form reads no scales)
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (unused by the debug form)
     const uint32_t boff = (uint32_t)(gcol * (K / 2)) + (uint32_t)(16 * bpart);
     const uint32_t zoff = (uint32_t)(gcol * 2);
     int64_t scol[2];
@@ -1250,9 +1252,14 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         x.rb = __builtin_amdgcn_raw_buffer_load_b128(rb, boff, (int)(g * (G128 / 2)), 0);
         const int gs = (int)(g * N * 2);
         x.rz = __builtin_amdgcn_raw_buffer_load_b16(rz, zoff, gs, 0);
-        x.rs0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[0], gs, 0);
-        x.rs1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[1], gs, 0);
+        if constexpr (!ISUMS) {
+            x.rs0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[0], gs, 0);
+            x.rs1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[1], gs, 0);
+        } else {
+            x.rs0 = x.rs1 = 0;
+        }
     };
+    constexpr int LPG = ISUMS ? 6 : 8;  // loads per wave and group (the debug form reads no scales)
     auto b_store = [&](const Slot &x, int st) {
         const uint32_t zadd = zp_add_const((uint16_t)x.rz);
         const uint32_t d4[4] = {x.rb.x, x.rb.y, x.rb.z, x.rb.w};
@@ -1378,18 +1385,18 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     a_dma(1, clampg(1));
     b_load(sl[1], clampg(1));
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(t3_waitcnt(8, 15));  // group 0: all but group 1's 8 loads
+    __builtin_amdgcn_s_waitcnt(t3_waitcnt(LPG, 15));  // group 0: all but group 1's loads
     b_store(sl[0], 0);
     scn[0] = half_bits_to_float((uint16_t)sl[0].rs0);
     scn[1] = half_bits_to_float((uint16_t)sl[0].rs1);
-    stage_barrier<8>();
+    stage_barrier<LPG>();
 
     // ---- main loop: iteration g computes group g from stage g % 3; register slot g & 1 held
     // group g's weights (unpacked last iteration) and now takes group g + 2's.  Unrolled by
     // two so the slots stay in registers.  Per iteration each wave issues 4 activation loads
-    // of group g + 2 and then 4 weight, zero-point and scale loads; before group g + 1's
-    // weights are unpacked and the barrier passed, group g + 1's activations (issued one
-    // iteration earlier, with 8 loads after them) are waited for.
+    // of group g + 2 and then 4 weight, zero-point and scale loads (2, without the scales, in
+    // the debug form); before group g + 1's weights are unpacked and the barrier passed, group
+    // g + 1's activations (issued one iteration earlier, with LPG loads after them) are waited for.
     int st0 = 0, st1 = 1, st2 = 2;
     auto body = [&](auto parc, int64_t g) {
         constexpr int PAR = decltype(parc)::value;
@@ -1406,13 +1413,13 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         if constexpr (ISUMS) group(st0, g);
         else group_rolling(st0);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(t3_waitcnt(8, 15));
+        __builtin_amdgcn_s_waitcnt(t3_waitcnt(LPG, 15));
         b_store(next, st1);
         scn[0] = half_bits_to_float((uint16_t)next.rs0);
         scn[1] = half_bits_to_float((uint16_t)next.rs1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) __asm__ volatile("" : "+v"(scn[h]));
-        stage_barrier<8>();
+        stage_barrier<LPG>();
         const int t = st0;
         st0 = st1;
         st1 = st2;
@@ -1871,7 +1878,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
         x.store = col < N;
         x.col = col < N ? col : N - 1;
         x.rw = make_rsrc(packed + (int64_t)x.e * N * (K / 2));
-        x.rs = make_rsrc((ISUMS ? zp : scale) + (int64_t)x.e * G * N);  // (ISUMS reads no scales)
+        x.rs = make_rsrc((ISUMS ? zp : scale) + (int64_t)x.e * G * N);  // (unused by the debug form)
         x.rz = make_rsrc(zp + (int64_t)x.e * G * N);
         x.vw = (uint32_t)(x.col * (K / 2) + 32 * h);
         x.vs = (uint32_t)(x.col * 2);
@@ -1914,12 +1921,12 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
     // ---- weight ring: U groups in flight per wave (cached loads: the other half of each
     // 128-byte line, the next group, is read a few groups later from L2)
     v4u rw0[U], rw1[U];
-    uint16_t rs[U], rz[U];
+    uint16_t rs[U] = {}, rz[U];  // (rs stays zero in the debug form)
     auto load_group = [&](int slot, const Unit &x, int64_t g) {
         const int gw = (int)(g * (G128 / 2)), gs2 = (int)(g * N * 2);
         rw0[slot] = __builtin_amdgcn_raw_buffer_load_b128(x.rw, x.vw, gw, 0);
         rw1[slot] = __builtin_amdgcn_raw_buffer_load_b128(x.rw, x.vw + 16, gw, 0);
-        rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(x.rs, x.vs, gs2, 0);
+        if constexpr (!ISUMS) rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(x.rs, x.vs, gs2, 0);
         rz[slot] = __builtin_amdgcn_raw_buffer_load_b16(x.rz, x.vs, gs2, 0);
     };
     // the same without a branch between the two units (the memory-counter waits stay exact)
@@ -1930,7 +1937,7 @@ __global__ __launch_bounds__(kMidThreads) void grouped_mid_kernel(
         const uint32_t vw = here ? a.vw : b.vw, vs = here ? a.vs : b.vs;
         rw0[slot] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw, gw, 0);
         rw1[slot] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw + 16, gw, 0);
-        rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(rsc, vs, gs2, 0);
+        if constexpr (!ISUMS) rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(rsc, vs, gs2, 0);
         rz[slot] = __builtin_amdgcn_raw_buffer_load_b16(rzp, vs, gs2, 0);
     };
 
