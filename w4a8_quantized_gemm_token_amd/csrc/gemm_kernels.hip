@@ -1133,7 +1133,9 @@ __device__ __forceinline__ void tile2_unit(uint8_t *lds, const int8_t *__restric
 //    codes each) and are unpacked once per workgroup to INT8 (q - zp), one group ahead.
 // One barrier per group.  Rows past the tile's last read row 0 and columns past N read
 // column 0; neither is stored.  Offsets are 32-bit: R * K and N * K / 2 below 2^32.
-constexpr int kT3BM = 256, kT3BN = 128, kT3Threads = 512;
+constexpr int kT3BM = 256, kT3BN = 128;
+constexpr int kT3FI = 2;                         // 32-row fragments per wave (see tile3_unit)
+constexpr int kT3Threads = 64 * 16 / kT3FI;      // 512: two waves per SIMD
 constexpr int kT3StageA = kT3BM * G128, kT3StageB = kT3BN * G128, kT3Stage = kT3StageA + kT3StageB;
 constexpr int kT3Lds = 3 * kT3Stage;  // 147456 bytes
 
@@ -1173,7 +1175,9 @@ __device__ __forceinline__ void stage_barrier() {
 //            The tile's values go through LDS so that each thread combines whole float4 runs.
 constexpr int kEpiOut = 0, kEpiSilu = 1, kEpiCombine = 2;
 
-template <bool ISUMS, int EPI = kEpiOut>
+// FI: 32-row fragments per wave.  FI = 2: 8 waves of 64x64 (two per SIMD); FI = 4: 4 waves of
+// 128x64, one per SIMD (each wave's MFMAs and fold then issue from one instruction stream).
+template <bool ISUMS, int EPI = kEpiOut, int FI = 2>
 __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restrict__ qa,
                                            const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
                                            int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
@@ -1181,6 +1185,10 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
                                            int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
                                            int32_t *__restrict__ isums, int64_t M_isums, const T3Epi &ep = T3Epi{}) {
     static_assert(EPI == kEpiOut || !ISUMS, "the debug form stores int32 sums only");
+    static_assert(FI == 2 || FI == 4, "fragments per wave");
+    constexpr int NWAVE = 16 / FI, NT = 64 * NWAVE;  // waves and threads of the workgroup
+    constexpr int LA = 32 / NWAVE;                  // 1 KB activation loads per wave and group
+    constexpr int NB = 512 / NT;                    // weight pieces per thread and group
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -1199,43 +1207,49 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     // row scales and validity of the tile's rows (published by the prologue's barriers)
     __shared__ float row_as[kT3BM];
     __shared__ int8_t row_ok[kT3BM];
-    if (tid < kT3BM) {
+    for (int t = tid; t < kT3BM; t += NT) {
         int64_t r = -1;
-        if (tid < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + tid] : rows.slot0 + tid;
+        if (t < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + t] : rows.slot0 + t;
         const bool ok = r >= 0 && r < R;
-        row_ok[tid] = ok ? 1 : 0;
-        if (!ISUMS) row_as[tid] = ok ? a_scale[r] : 0.0f;
+        row_ok[t] = ok ? 1 : 0;
+        if (!ISUMS) row_as[t] = ok ? a_scale[r] : 0.0f;
     }
 
-    // ---- activation loads: load j (0..3) of wave w fills LDS rows 8 (4 w + j) + [0, 8);
-    // lane l brings row 8 (4 w + j) + (l >> 3), chunk (l & 7) of the swizzled layout
+    // ---- activation loads: load j (0..LA-1) of wave w fills LDS rows 8 (LA w + j) + [0, 8);
+    // lane l brings row 8 (LA w + j) + (l >> 3), chunk (l & 7) of the swizzled layout
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa);
-    uint32_t aoff[4];
+    uint32_t aoff[LA];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int rl = 8 * (4 * wave + j) + (lane >> 3);
+    for (int j = 0; j < LA; ++j) {
+        const int rl = 8 * (LA * wave + j) + (lane >> 3);
         int64_t r = -1;
         if (rl < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + rl] : rows.slot0 + rl;
         if (r < 0 || r >= R) r = 0;
-        aoff[j] = (uint32_t)(r * K) + (uint32_t)(((lane & 7) ^ ((rl >> 1) & 7)) << 4);
+        aoff[j] = (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 7) ^ ((rl >> 1) & 7)) << 4);
     }
     auto a_dma = [&](int st, int64_t g) {
-        uint8_t *dst = lds + st * kT3Stage + 1024 * (4 * wave);
+        uint8_t *dst = lds + st * kT3Stage + 1024 * (LA * wave);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < LA; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + 1024 * j), 16, (int)aoff[j],
                                                      (int)(g * G128), 0, 0);
     };
 
-    // ---- packed weights: thread t takes column t >> 2, bytes 16 (t & 3) + [0, 16) of a group,
-    // with that column's zero point; and this lane's two output columns' scales
+    // ---- packed weights: thread t takes column (t >> 2) + (NT / 4) q for q < NB, bytes
+    // 16 (t & 3) + [0, 16) of a group, with that column's zero point; and this lane's two output
+    // columns' scales
     const int bcol = tid >> 2, bpart = tid & 3;
-    const int64_t gcol = wrow(bcol) >= 0 ? wrow(bcol) : 0;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (unused by the debug form)
-    const uint32_t boff = (uint32_t)(gcol * (K / 2)) + (uint32_t)(16 * bpart);
-    const uint32_t zoff = (uint32_t)(gcol * 2);
+    uint32_t boff[NB], zoff[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        const int c = bcol + (NT / 4) * q;
+        const int64_t gc = wrow(c) >= 0 ? wrow(c) : 0;
+        boff[q] = (uint32_t)(gc * (K / 2)) + (uint32_t)(16 * bpart);
+        zoff[q] = (uint32_t)(gc * 2);
+    }
     int64_t scol[2];
     uint32_t soff[2];
 #pragma unroll
@@ -1245,13 +1259,16 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         soff[j] = (uint32_t)((wr >= 0 ? wr : 0) * 2);
     }
     struct Slot {
-        v4u rb;
-        uint32_t rz, rs0, rs1;
+        v4u rb[NB];
+        uint32_t rz[NB], rs0, rs1;
     };
     auto b_load = [&](Slot &x, int64_t g) {
-        x.rb = __builtin_amdgcn_raw_buffer_load_b128(rb, boff, (int)(g * (G128 / 2)), 0);
         const int gs = (int)(g * N * 2);
-        x.rz = __builtin_amdgcn_raw_buffer_load_b16(rz, zoff, gs, 0);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            x.rb[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[q], (int)(g * (G128 / 2)), 0);
+            x.rz[q] = __builtin_amdgcn_raw_buffer_load_b16(rz, zoff[q], gs, 0);
+        }
         if constexpr (!ISUMS) {
             x.rs0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[0], gs, 0);
             x.rs1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[1], gs, 0);
@@ -1259,16 +1276,21 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
             x.rs0 = x.rs1 = 0;
         }
     };
-    constexpr int LPG = ISUMS ? 6 : 8;  // loads per wave and group (the debug form reads no scales)
+    // loads per wave and group (the debug form reads no scales)
+    constexpr int LPG = LA + 2 * NB + (ISUMS ? 0 : 2);
     auto b_store = [&](const Slot &x, int st) {
-        const uint32_t zadd = zp_add_const((uint16_t)x.rz);
-        const uint32_t d4[4] = {x.rb.x, x.rb.y, x.rb.z, x.rb.w};
-        uint32_t w[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) unpack8(d4[k], zadd, w[2 * k], w[2 * k + 1]);
         uint8_t *B = lds + st * kT3Stage + kT3StageA;
-        *reinterpret_cast<v4u *>(B + t3_sw(bcol, 2 * bpart)) = v4u{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<v4u *>(B + t3_sw(bcol, 2 * bpart + 1)) = v4u{w[4], w[5], w[6], w[7]};
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const uint32_t zadd = zp_add_const((uint16_t)x.rz[q]);
+            const uint32_t d4[4] = {x.rb[q].x, x.rb[q].y, x.rb[q].z, x.rb[q].w};
+            uint32_t w[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) unpack8(d4[k], zadd, w[2 * k], w[2 * k + 1]);
+            const int c = bcol + (NT / 4) * q;
+            *reinterpret_cast<v4u *>(B + t3_sw(c, 2 * bpart)) = v4u{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<v4u *>(B + t3_sw(c, 2 * bpart + 1)) = v4u{w[4], w[5], w[6], w[7]};
+        }
     };
 
     // ---- compute: lane l feeds A row (l & 31) / B column (l & 31) of a 32x32 tile with the
@@ -1279,12 +1301,12 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     int aofs[4], bofs[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        aofs[ks] = t3_sw(wm * 64 + frow, 2 * ks + fch);
+        aofs[ks] = t3_sw(wm * 32 * FI + frow, 2 * ks + fch);
         bofs[ks] = kT3StageA + t3_sw(wn * 64 + frow, 2 * ks + fch);
     }
-    float acc[2][2][16];
+    float acc[FI][2][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1319,56 +1341,59 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     auto group_rolling = [&](int st) {
         const uint8_t *base = lds + st * kT3Stage;
         // every fragment of the group is requested up front (in the order the chains use them)
-        v4i a0[4], a1[4], b0[4], b1[4];
+        v4i a[FI][4], b[2][4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            a0[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks]);
-            b0[ks] = *reinterpret_cast<const v4i *>(base + bofs[ks]);
+            a[0][ks] = *reinterpret_cast<const v4i *>(base + aofs[ks]);
+            b[0][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks]);
         }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) b1[ks] = *reinterpret_cast<const v4i *>(base + bofs[ks] + 4096);
+        for (int ks = 0; ks < 4; ++ks) b[1][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks] + 4096);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) a1[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks] + 4096);
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        const v16i d00 = chain(a0, b0);
-        fold(prev, 1, 1, prev_sc);
+        for (int i = 1; i < FI; ++i)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) a[i][ks] = *reinterpret_cast<const v4i *>(base + aofs[ks] + 4096 * i);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (FI + 2), 0);
+        // chains (i, j) in order; each folds the one before it (the first, the last of the group before)
+        v16i d = chain(a[0], b[0]);
+        fold(prev, FI - 1, 1, prev_sc);
         interleave();
-        const v16i d01 = chain(a0, b1);
-        fold(d00, 0, 0, sc[0]);
-        interleave();
-        const v16i d10 = chain(a1, b0);
-        fold(d01, 0, 1, sc[1]);
-        interleave();
-        prev = chain(a1, b1);
-        fold(d10, 1, 0, sc[0]);
-        interleave();
+#pragma unroll
+        for (int c = 1; c < 2 * FI; ++c) {
+            const int i = c >> 1, j = c & 1;
+            const v16i dn = chain(a[i], b[j]);
+            fold(d, (c - 1) >> 1, (c - 1) & 1, sc[(c - 1) & 1]);
+            interleave();
+            d = dn;
+        }
+        prev = d;
         prev_sc = sc[1];
     };
     auto group = [&](int st, int64_t g) {
         const uint8_t *base = lds + st * kT3Stage;
-        v16i d[2][2];
+        v16i d[FI][2];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            v4i af[2], bf[2];
+            v4i af[FI], bf[2];
             const uint8_t *pa = base + aofs[ks], *pb = base + bofs[ks];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const v4i *>(pa + 4096 * i);
+            for (int i = 0; i < FI; ++i) af[i] = *reinterpret_cast<const v4i *>(pa + 4096 * i);
 #pragma unroll
             for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const v4i *>(pb + 4096 * j);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FI; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], ks ? d[i][j] : v16i{}, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if (ISUMS) {
-                        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                        const int m = wm * 32 * FI + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
                         if (m < rows.rows && scol[j] < N)
                             isums[(g * M_isums + rows.slot0 + m) * N + scol[j]] = d[i][j][r];
                     } else {
@@ -1434,14 +1459,14 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
     }
     if (g < G) body(I0{}, g);
     __builtin_amdgcn_s_waitcnt(0);  // the last (unused) prefetches
-    if constexpr (!ISUMS) fold(prev, 1, 1, prev_sc);  // the last group's last chain
+    if constexpr (!ISUMS) fold(prev, FI - 1, 1, prev_sc);  // the last group's last chain
 
     if constexpr (!ISUMS && EPI == kEpiOut) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                const int m = wm * 32 * FI + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
                 if (m < rows.rows && row_ok[m]) {
                     const int64_t slot = rows.slot0 + m;
                     const float as = row_as[m];
@@ -1454,10 +1479,10 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         const int64_t hc = n0 + wn * 32 + (lane & 31);  // this lane's h column
         const bool col_ok = hc < ep.half;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                const int m = wm * 32 * FI + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
                 const bool ok = m < rows.rows && row_ok[m];
                 const float as = row_as[m];
                 const float gate = as * acc[i][0][r], up = as * acc[i][1][r];
@@ -1483,15 +1508,15 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         int32_t *tsop = reinterpret_cast<int32_t *>(lds + kT3BM * kT3BN * 4);
         float *tw = reinterpret_cast<float *>(lds + kT3BM * kT3BN * 4 + kT3BM * 8 * 4);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                const int m = wm * 32 * FI + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
                 const float as = row_as[m];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) ct[m * kT3BN + wn * 64 + j * 32 + (lane & 31)] = as * acc[i][j][r];
             }
-        for (int idx = tid; idx < rows.rows * ep.k; idx += kT3Threads) {
+        for (int idx = tid; idx < rows.rows * ep.k; idx += NT) {
             const int m = idx / ep.k, jj = idx - m * ep.k;
             const int64_t pr = (rows.slot0 + m) * ep.k + jj;
             tsop[m * 8 + jj] = ep.sop[pr];
@@ -1503,11 +1528,11 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
         const int c4 = tid & 31;
         const int64_t col = n0 + 4 * c4;
         if (col < N) {
-            for (int mb = tid >> 5; mb < rows.rows; mb += 2 * (kT3Threads / 32)) {
+            for (int mb = tid >> 5; mb < rows.rows; mb += 2 * (NT / 32)) {
                 float4 v[2][8];
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const int m = mb + q * (kT3Threads / 32);
+                    const int m = mb + q * (NT / 32);
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj)
                         if (m < rows.rows && jj < ep.k)
@@ -1515,7 +1540,7 @@ __device__ __forceinline__ void tile3_unit(uint8_t *lds, const int8_t *__restric
                 }
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const int m = mb + q * (kT3Threads / 32);
+                    const int m = mb + q * (NT / 32);
                     if (m >= rows.rows) continue;
                     const int64_t t = rows.slot0 + m;
                     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1556,7 +1581,7 @@ __global__ __launch_bounds__(kT3Threads) void gemm_tiled3_kernel(const int8_t *_
     panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
     const int64_t m0 = tm * kT3BM;
     const int rows = (int)((M - m0) < kT3BM ? (M - m0) : kT3BM);
-    tile3_unit<ISUMS, EPI>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT3BN, out,
+    tile3_unit<ISUMS, EPI, kT3FI>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT3BN, out,
                            N, isums, M, ep);
 }
 
@@ -2118,7 +2143,7 @@ __global__ __launch_bounds__(kT3Threads) void grouped_tiled3_kernel(
         const int64_t tm = local % mt, tn = local / mt;
         const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * kT3BM;
         const int rows = (int)((c - tm * kT3BM) < kT3BM ? (c - tm * kT3BM) : kT3BM);
-        tile3_unit<ISUMS, EPI>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
+        tile3_unit<ISUMS, EPI, kT3FI>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
                                packed + (int64_t)e * N * (K / 2), (ISUMS ? nullptr : scale + (int64_t)e * G * N),
                                zp + (int64_t)e * G * N, N, tn * TBN, out, N, isums, max_slots, ep);
         __syncthreads();  // the next unit reuses the LDS stages and row tables
