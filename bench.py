@@ -237,6 +237,9 @@ def parse():
     p.add_argument("--group", type=int, default=GROUP, choices=(64, 128, 256),
                    help="group size of the weights for --only prefill")
     p.add_argument("--reps", type=int, default=10, help="timed launches for --only")
+    p.add_argument("--path", type=int, action="append",
+                   help="main loop of --only prefill (as w4a8_gemm_path; default: the one w4a8_gemm picks); "
+                        "repeatable, each timed in turn")
     return p.parse_args()
 
 
@@ -346,7 +349,7 @@ def cpu_baseline(synthetic):
                       f"{t_total:.1f} s; weight quantization excluded (offline)"}
 
 
-def prefill(torch, w4, synthetic, reps=10, group=GROUP):
+def prefill(torch, w4, synthetic, reps=10, group=GROUP, paths=(0,)):
     """The prefill-shaped dense GEMM (M=4096, K=N=8192): quantize once, then `reps`
     back-to-back prepared launches timed with one event pair on the launch stream.
     Group sizes other than 128 are packed by the host packer (the device packer takes 128)."""
@@ -364,21 +367,25 @@ def prefill(torch, w4, synthetic, reps=10, group=GROUP):
     x = torch.from_numpy(synthetic.activations(0, M, K)).to(dev)
     qa, sc = w4.quantize_act(x)
     out_buf = torch.empty((M, N), dtype=torch.float32, device=dev)
-    launch = w4.prepare_gemm(qa, sc, *layer, out_buf, group=group)
-    for _ in range(40):  # about 20 ms of warm-up
-        launch()
-    stream = torch.cuda.current_stream()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    for _ in range(reps):
-        launch()
-    e.record(stream)
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    tops = 2 * M * N * K / (ms * 1e-3) / 1e12
+    res = {}
+    for path in paths:  # (0: the loop w4a8_gemm picks; others force one, for comparisons)
+        launch = w4.prepare_gemm(qa, sc, *layer, out_buf, group=group, path=path)
+        for _ in range(40):  # about 20 ms of warm-up
+            launch()
+        stream = torch.cuda.current_stream()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            launch()
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        tops = 2 * M * N * K / (ms * 1e-3) / 1e12
+        res[path] = {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1),
+                     "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
     del layer, x, qa, sc, out_buf
     torch.cuda.empty_cache()
-    return {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    return res[paths[0]] if len(paths) == 1 else res
 
 
 def quant_variants(torch, w4, synthetic):
@@ -620,7 +627,7 @@ def main():
     if args.only:
         if args.only == "prefill":
             res = {f"prefill_M4096_K8192_N8192_group{args.group}": prefill(torch, w4, synthetic, args.reps,
-                                                                            args.group)}
+                                                                            args.group, tuple(args.path or (0,)))}
         elif args.only == "toy_moe":
             res = toy_moe(torch, w4, synthetic, args.size or (1, 2, 4, 512), args.reps)
         else:

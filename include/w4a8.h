@@ -209,7 +209,8 @@ w4a8_status w4a8_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_t
  * `path` selects the main loop: 0 = the one w4a8_gemm would pick for M,
  * 1 = the small-M streaming loop (M <= 64; for group 64 or 256, the decode loop,
  * M <= 16), 2 = the large-M tiled loop with the tile w4a8_gemm would pick,
- * 3 = tiled with 128x128 workgroup tiles, 4 = tiled with 256x128 workgroup tiles. */
+ * 3 = tiled with 128x128 workgroup tiles, 4 = tiled with 256x128 workgroup tiles,
+ * 5 = tiled with 256x256 workgroup tiles (group 128; 256x128 for 64 and 256). */
 w4a8_status w4a8_gemm_debug_isums(const int8_t *qa, int64_t M, int64_t K,
                                   const uint8_t *packed, const uint16_t *zp, int64_t N,
                                   int32_t group, int32_t path, int32_t *isums, hipStream_t stream);

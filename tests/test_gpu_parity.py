@@ -130,8 +130,8 @@ def test_device_packer_bit_exact(orc, case):
 
 
 # ------------------------------------------------------------------ dense GEMM, small shapes
-ALL = (1, 2, 3, 4)             # streaming; tiled with the default tile, 128x128, 256x128
-TILED = (2, 3, 4)
+ALL = (1, 2, 3, 4, 5)          # streaming; tiled with the default tile, 128x128, 256x128, 256x256
+TILED = (2, 3, 4, 5)
 SHAPES = [  # (M, N, K, paths)
     (4, 128, 256, ALL),         # the small config
     (1, 16, 128, ALL),

@@ -297,11 +297,16 @@ def prepare_quantize_act(x, qa, a_scale) -> Launch:
                                         _stream(x.device)), (x, qa, a_scale))
 
 
-def prepare_gemm(qa, a_scale, packed, scale, zp, out, group: int = GROUP) -> Launch:
-    """Prepared w4a8_gemm writing into a preallocated out float32 [M][N]."""
+def prepare_gemm(qa, a_scale, packed, scale, zp, out, group: int = GROUP, path: int = 0) -> Launch:
+    """Prepared w4a8_gemm (path 0) or w4a8_gemm_path writing into a preallocated out
+    float32 [M][N]."""
     M, K = qa.shape
     N = packed.shape[0]
     assert tuple(out.shape) == (M, N)
+    if path:
+        return Launch("w4a8_gemm_path", (_dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(packed), _dev_ptr(scale),
+                                         _dev_ptr(zp), N, group, path, _dev_ptr(out), _stream(qa.device)),
+                      (qa, a_scale, packed, scale, zp, out))
     return Launch("w4a8_gemm", (_dev_ptr(qa), _dev_ptr(a_scale), M, K, _dev_ptr(packed), _dev_ptr(scale),
                                 _dev_ptr(zp), N, group, _dev_ptr(out), _stream(qa.device)),
                   (qa, a_scale, packed, scale, zp, out))

@@ -331,7 +331,7 @@ static w4a8_status check_gemm(const int8_t *qa, int64_t M, int64_t K, const uint
 static w4a8_status gemm_common(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                                const uint16_t *scale, const uint16_t *zp, int64_t N, int32_t group, int32_t path,
                                float *out, int32_t *isums, hipStream_t stream) {
-    W4A8_REQUIRE(path >= 0 && path <= 4, W4A8_EINVAL, "path=%d must be in [0, 4]", (int)path);
+    W4A8_REQUIRE(path >= 0 && path <= 5, W4A8_EINVAL, "path=%d must be in [0, 5]", (int)path);
     if (group != W4A8_GROUP) {
         // group sizes 64 and 256: the decode loop for M <= 16 (K a multiple of 256), the
         // tiled loop otherwise

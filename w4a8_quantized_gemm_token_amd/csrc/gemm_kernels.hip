@@ -1585,6 +1585,329 @@ __global__ __launch_bounds__(kT3Threads) void gemm_tiled3_kernel(const int8_t *_
                            N, isums, M, ep);
 }
 
+// ------------------------------------------------------------------ tiled loop, 256x256 tiles
+// The same arithmetic as tile3_unit (per-group int32 sums of v_mfma_i32_32x32x32_i8 chains,
+// folded into fp32 in increasing g with one fmaf per element and group) on a 256x256 workgroup
+// tile: eight waves of 128x64 (4x2 chains), two per SIMD, and two LDS stages of 64 KB (the 256
+// activation rows and the 256 unpacked weight columns of one group, in the swizzled layout of
+// t3_sw).  Per output element and group a wave reads 25% fewer fragment bytes from LDS than
+// with 64x64 wave tiles, and the workgroup moves 40% fewer bytes through the vector memory
+// path (one activation tile serves 256 columns).
+// Iteration g computes group g from stage g % 2; at its top the activations of group g + 1 are
+// requested straight into the other stage and the packed weights into registers (one
+// iteration of lead: that stage was last read before the previous barrier); before the
+// barrier that ends it, the weights are unpacked into that stage.  A wave keeps the weight
+// fragments of the group (both 32-column blocks) and loads the activation fragments of one
+// 32-row block at a time, each step's fragment replacing the one the previous block's
+// second chain has just used.
+constexpr int kT4BM = 256, kT4BN = 256;
+constexpr int kT4Threads = 512;
+constexpr int kT4StageA = kT4BM * G128, kT4Stage = kT4StageA + kT4BN * G128;
+constexpr int kT4Lds = 2 * kT4Stage;  // 131072 bytes
+
+template <bool ISUMS, int EPI = kEpiOut>
+__device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restrict__ qa,
+                                           const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
+                                           int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
+                                           const uint16_t *__restrict__ wsc, const uint16_t *__restrict__ wzp,
+                                           int64_t N, int64_t n0, float *__restrict__ out, int64_t ldo,
+                                           int32_t *__restrict__ isums, int64_t M_isums, const T3Epi &ep = T3Epi{}) {
+    static_assert(EPI == kEpiOut || EPI == kEpiSilu, "plain and SiLU epilogues");
+    static_assert(EPI == kEpiOut || !ISUMS, "the debug form stores int32 sums only");
+    constexpr int NT = kT4Threads, LA = 4;  // threads; 1 KB activation loads per wave and group
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t G = K / G128;
+    // weight row of MFMA column c of the tile (-1: past the matrix); kEpiSilu as in tile3_unit
+    // (n0 counts h columns: 128 per tile)
+    auto wrow = [&](int c) -> int64_t {
+        if constexpr (EPI == kEpiSilu) {
+            const int64_t hc = n0 + (c >> 6) * 32 + (c & 31);
+            return hc < ep.half ? ((c & 32) ? ep.half + hc : hc) : -1;
+        } else {
+            return n0 + c < N ? n0 + c : -1;
+        }
+    };
+
+    __shared__ float row_as[kT4BM];
+    __shared__ int8_t row_ok[kT4BM];
+    for (int t = tid; t < kT4BM; t += NT) {
+        int64_t r = -1;
+        if (t < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + t] : rows.slot0 + t;
+        const bool ok = r >= 0 && r < R;
+        row_ok[t] = ok ? 1 : 0;
+        if (!ISUMS) row_as[t] = ok ? a_scale[r] : 0.0f;
+    }
+
+    // ---- activation loads: load j of wave w fills LDS rows 8 (4 w + j) + [0, 8); lane l
+    // brings row 8 (4 w + j) + (l >> 3), chunk (l & 7) of the swizzled layout
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa);
+    uint32_t aoff[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int rl = 8 * (LA * wave + j) + (lane >> 3);
+        int64_t r = -1;
+        if (rl < rows.rows) r = row_index ? (int64_t)row_index[rows.slot0 + rl] : rows.slot0 + rl;
+        if (r < 0 || r >= R) r = 0;
+        aoff[j] = (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 7) ^ ((rl >> 1) & 7)) << 4);
+    }
+    auto a_dma = [&](int st, int64_t g) {
+        uint8_t *dst = lds + st * kT4Stage + 1024 * (LA * wave);
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + 1024 * j), 16, (int)aoff[j],
+                                                     (int)(g * G128), 0, 0);
+    };
+
+    // ---- packed weights: thread t takes column t >> 1 of the tile, bytes 32 (t & 1) + [0, 32)
+    // of a group (codes 64 (t & 1) + [0, 64)), with that column's zero point; and this lane's
+    // two output columns' scales
+    const int bcol = tid >> 1, bpart = tid & 1;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (unused by the debug form)
+    uint32_t boff, zoff;
+    {
+        const int64_t gc = wrow(bcol) >= 0 ? wrow(bcol) : 0;
+        boff = (uint32_t)(gc * (K / 2)) + (uint32_t)(32 * bpart);
+        zoff = (uint32_t)(gc * 2);
+    }
+    int64_t scol[2];
+    uint32_t soff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t wr = wrow(wn * 64 + j * 32 + (lane & 31));
+        scol[j] = wr >= 0 ? wr : N;
+        soff[j] = (uint32_t)((wr >= 0 ? wr : 0) * 2);
+    }
+    struct Slot {
+        v4u rb0, rb1;
+        uint32_t rz, rs0, rs1;
+    };
+    auto b_load = [&](Slot &x, int64_t g) {
+        const int gs = (int)(g * N * 2);
+        x.rb0 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff, (int)(g * (G128 / 2)), 0);
+        x.rb1 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff + 16, (int)(g * (G128 / 2)), 0);
+        x.rz = __builtin_amdgcn_raw_buffer_load_b16(rz, zoff, gs, 0);
+        if constexpr (!ISUMS) {
+            x.rs0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[0], gs, 0);
+            x.rs1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[1], gs, 0);
+        } else {
+            x.rs0 = x.rs1 = 0;
+        }
+    };
+    auto b_store = [&](const Slot &x, int st) {
+        uint8_t *B = lds + st * kT4Stage + kT4StageA;
+        const uint32_t zadd = zp_add_const((uint16_t)x.rz);
+        const uint32_t d8[8] = {x.rb0.x, x.rb0.y, x.rb0.z, x.rb0.w, x.rb1.x, x.rb1.y, x.rb1.z, x.rb1.w};
+        uint32_t w[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) unpack8(d8[k], zadd, w[2 * k], w[2 * k + 1]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<v4u *>(B + t3_sw(bcol, 4 * bpart + q)) = v4u{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+    };
+
+    // ---- compute: lane l feeds A row (l & 31) / B column (l & 31) of a 32x32 tile with the 16
+    // bytes of chunk 2 ks + (l >> 5) and holds accumulator rows 8 (r >> 2) + 4 (l >> 5) + (r & 3);
+    // row block i and column block j are the first block's addresses plus 4096 i / 4096 j
+    // (32 rows of 128 bytes; the swizzle repeats every 16 rows)
+    const int frow = lane & 31, fch = lane >> 5;
+    int aofs[4], bofs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        aofs[ks] = t3_sw(wm * 128 + frow, 2 * ks + fch);
+        bofs[ks] = kT4StageA + t3_sw(wn * 64 + frow, 2 * ks + fch);
+    }
+    float acc[4][2][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    float sc[2] = {0.0f, 0.0f}, scn[2] = {0.0f, 0.0f};
+    // Rolling consumption, as in tile3_unit: chain c = 2 i + j of a group runs while chain c - 1
+    // is folded (or, in the debug form, stored); the last chain of group g is consumed during
+    // the first chain of group g + 1.  Every element still takes its groups in increasing g.
+    v16i prev = {};
+    float prev_sc = 0.0f;  // fmaf(0, 0, acc) == acc before the first group
+    int64_t prev_g = -1;   // (debug form: no chain before the first)
+    auto consume = [&](const v16i &dd, int i, int j, float s_, int64_t g) {
+        if constexpr (ISUMS) {
+            if (g < 0) return;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                if (m < rows.rows && scol[j] < N) isums[(g * M_isums + rows.slot0 + m) * N + scol[j]] = dd[r];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s_, (float)dd[r], acc[i][j][r]);
+        }
+    };
+    // Pins the folded values at the end of a chain's scheduling region: left alone, the
+    // compiler sinks every fold below the last chain and keeps all eight chains' sums live.
+    // (After the region's group barriers: an asm statement ends a scheduling region.)
+    auto pin = [&](int i, int j) {
+        if constexpr (!ISUMS) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) __asm__ volatile("" : "+v"(acc[i][j][r]));
+        }
+    };
+    auto group = [&](int st, int64_t g) {
+        const uint8_t *base = lds + st * kT4Stage;
+        // the group's first fragments in the order the first chain takes them; the last
+        // group's last chain is folded while they arrive
+        v4i b[2][4], a[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            a[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks]);
+            b[0][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b[1][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks] + 4096);
+        consume(prev, 3, 1, prev_sc, prev_g);
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+        pin(3, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        v16i d = {};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int i = c >> 1, j = c & 1;
+            v16i dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[j][0], v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int ks = 1; ks < 4; ++ks) dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ks], b[j][ks], dn, 0, 0, 0);
+            if (j == 1 && i < 3) {
+                // the next row block's fragments, each after the MFMA that last reads its register
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    a[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks] + 4096 * (i + 1));
+            }
+            if (c > 0) consume(d, (c - 1) >> 1, (c - 1) & 1, sc[(c - 1) & 1], g);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (j == 1 && i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+            if (c > 0) pin((c - 1) >> 1, (c - 1) & 1);
+            // (one chain per scheduling region: the chains are independent, and letting them
+            // interleave keeps eight 16-register results live at once)
+            __builtin_amdgcn_sched_barrier(0);
+            d = dn;
+        }
+        prev = d;
+        prev_sc = sc[1];
+        prev_g = g;
+    };
+
+    // ---- prologue: group 0 into stage 0
+    Slot sl;
+    a_dma(0, 0);
+    b_load(sl, 0);
+    __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 15));
+    b_store(sl, 0);
+    scn[0] = half_bits_to_float((uint16_t)sl.rs0);
+    scn[1] = half_bits_to_float((uint16_t)sl.rs1);
+    stage_barrier<0>();
+
+    // ---- main loop, unrolled by two so that the stage index is a constant
+    auto body = [&](auto stc, int64_t g) {
+        constexpr int ST = decltype(stc)::value;
+        const bool more = g + 1 < G;  // (uniform)
+        sc[0] = scn[0];
+        sc[1] = scn[1];
+        __asm__ volatile("" ::: "memory");
+        if (more) {
+            a_dma(ST ^ 1, g + 1);
+            b_load(sl, g + 1);
+        }
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        group(ST, g);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 15));
+            b_store(sl, ST ^ 1);
+            scn[0] = half_bits_to_float((uint16_t)sl.rs0);
+            scn[1] = half_bits_to_float((uint16_t)sl.rs1);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) __asm__ volatile("" : "+v"(scn[h]));
+        stage_barrier<0>();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int64_t g = 0;
+    for (; g + 1 < G; g += 2) {
+        body(I0{}, g);
+        body(I1{}, g + 1);
+    }
+    if (g < G) body(I0{}, g);
+    consume(prev, 3, 1, prev_sc, prev_g);  // the last group's last chain
+
+    if constexpr (!ISUMS && EPI == kEpiOut) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                if (m < rows.rows && row_ok[m]) {
+                    const int64_t slot = rows.slot0 + m;
+                    const float as = row_as[m];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
+                }
+            }
+    } else if constexpr (EPI == kEpiSilu) {
+        const int64_t hc = n0 + wn * 32 + (lane & 31);  // this lane's h column
+        const bool col_ok = hc < ep.half;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+                const bool ok = m < rows.rows && row_ok[m];
+                const float as = row_as[m];
+                const float gate = as * acc[i][0][r], up = as * acc[i][1][r];
+                const float h = silu_mul(gate, up);
+                float hm = (ok && col_ok) ? fabsf(h) : 0.0f;
+                hm = dpp_max<0xB1>(hm);   // quad_perm [1,0,3,2]
+                hm = dpp_max<0x4E>(hm);   // quad_perm [2,3,0,1]
+                hm = dpp_max<0x124>(hm);  // row_ror:4
+                hm = dpp_max<0x128>(hm);  // row_ror:8
+                if (ok) {
+                    float *line = out + (rows.slot0 + m) * ldo;
+                    if (col_ok) line[hc] = h;
+                    if ((lane & 15) == 0) line[ep.half + (n0 + wn * 32 + (lane & 16)) / 16] = hm;
+                }
+            }
+    }
+}
+
+template <bool ISUMS, int EPI = kEpiOut>
+__global__ __launch_bounds__(kT4Threads) void gemm_tiled4_kernel(const int8_t *__restrict__ qa,
+                                                                 const float *__restrict__ a_scale, int64_t M,
+                                                                 int64_t K, const uint8_t *__restrict__ packed,
+                                                                 const uint16_t *__restrict__ scale,
+                                                                 const uint16_t *__restrict__ zp, int64_t N,
+                                                                 float *__restrict__ out,
+                                                                 int32_t *__restrict__ isums) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    const int64_t mt = (M + kT4BM - 1) / kT4BM, nt = (N + kT4BN - 1) / kT4BN;
+    int64_t tm, tn;
+    panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
+    const int64_t m0 = tm * kT4BM;
+    const int rows = (int)((M - m0) < kT4BM ? (M - m0) : kT4BM);
+    tile4_unit<ISUMS, EPI>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT4BN, out,
+                           N, isums, M);
+}
+
 template <int WM, int WN, bool ISUMS, int GS>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const int8_t *__restrict__ qa,
                                                                   const float *__restrict__ a_scale, int64_t M,
@@ -1748,7 +2071,6 @@ __global__ __launch_bounds__(kDecThreads) void grouped_decode_kernel(
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
         return (c > 0 && c <= small_eff) ? ((c + 15) / 16) * ntiles : 0;
     });
-    const int64_t G = K / G128;
     const int64_t lda = K + 16;
     float *red = reinterpret_cast<float *>(dsm + ((dec_lds_bytes(16, K) + 15) / 16) * 16);
     // Contiguous unit ranges of one length, rounded up to whole rounds of the 16 waves
@@ -2090,7 +2412,6 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_tiled_kernel(
         const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
         return (c > cmin && c <= cmax) ? ((c + S::BM - 1) / S::BM) * ntn : 0;
     });
-    const int64_t G = K / G128;
     // Round r hands each XCD (workgroup b runs on XCD b % 8) a contiguous run of units,
     // row tiles fastest: the workgroups of one XCD then share their experts' weight
     // columns and activation rows in that XCD's L2.
@@ -2234,6 +2555,34 @@ hipError_t launch_tiled3(const int8_t *qa, const float *a_scale, int64_t M, int6
     return hipGetLastError();
 }
 
+// 256x256 tiles when they still give every CU a workgroup (else the 256x128 loop, with twice
+// as many tiles).
+bool tiled4_pays(int64_t M, int64_t N) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return ((M + kT4BM - 1) / kT4BM) * ((N + kT4BN - 1) / kT4BN) >= cus;
+}
+
+hipError_t launch_tiled4(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
+                         const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
+                         hipStream_t stream) {
+    const int64_t tiles = ((M + kT4BM - 1) / kT4BM) * ((N + kT4BN - 1) / kT4BN);
+    const dim3 grid((uint32_t)tiles), block(kT4Threads);
+#define W4A8_T4(IS)                                                                                                 \
+    do {                                                                                                            \
+        if (hipFuncSetAttribute((const void *)gemm_tiled4_kernel<IS>, hipFuncAttributeMaxDynamicSharedMemorySize,   \
+                                kT4Lds) != hipSuccess)                                                              \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((gemm_tiled4_kernel<IS>), grid, block, kT4Lds, stream, qa, a_scale, M, K, packed, scale, \
+                           zp, N, out, isums);                                                                      \
+    } while (0)
+    if (isums) W4A8_T4(true);
+    else W4A8_T4(false);
+#undef W4A8_T4
+    return hipGetLastError();
+}
+
 // tm: `packed` is the tile-major array (scale and zp unused; no isums)
 template <int GS = G128>
 hipError_t launch_decode(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
@@ -2358,7 +2707,9 @@ hipError_t launch_gemm(const int8_t *qa, const float *a_scale, int64_t M, int64_
 #undef W4A8_STREAM
 #undef W4A8_STREAM_U
     } else {
-        if (path == 4 || (path == 2 && M > 128)) {
+        if (tiled3_fits(M, K, N) && (path == 5 || (path == 2 && M > 128 && tiled4_pays(M, N))))
+            return launch_tiled4(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
+        if (path >= 4 || (path == 2 && M > 128)) {
             if (tiled3_fits(M, K, N))
                 return launch_tiled3(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
             return launch_tiled<4, 2>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
@@ -2380,7 +2731,7 @@ hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64
             return launch_decode<64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, false, stream);
         return launch_decode<256>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, false, stream);
     }
-    const bool wide = path == 4 || (path == 2 && M > 128);
+    const bool wide = path >= 4 || (path == 2 && M > 128);  // (path 5: the 256x128 loop at these sizes)
     if (group == 64)
         return wide ? launch_tiled<4, 2, 64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream)
                     : launch_tiled<2, 2, 64>(qa, a_scale, M, K, packed, scale, zp, N, out, isums, stream);
