@@ -456,6 +456,37 @@ def test_grouped_gemm_isums_bit_exact(orc, counts, N, K):
         assert not bad.any(), f"expert {e} ({s1 - s0} slots): {int(bad.sum())} sums differ"
 
 
+def test_grouped_gemm_256x256_loop(orc):
+    """Enough slots and columns (2692 slots, N = 13440: 53 column tiles of 256, the last one
+    half full) that the experts above 128 slots run on 256x256 tiles, small and mid-size experts
+    beside them: per-group int32 sums bit-exact and fp32 outputs within tolerance for every slot
+    on three sampled column ranges (the first tile, a middle one, the last one and a half)."""
+    w4 = w4mod()
+    counts = [3, 129, 700, 60, 1500, 300]
+    E, N, K, R = len(counts), 13440, 1024, 311
+    S = sum(counts)
+    rng = np.random.default_rng(13)
+    row_index = rng.integers(0, R, S).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synthetic.activations(13, R, K)
+    qr, sr = orc.quantize_act(x)
+    cols = np.concatenate([np.arange(0, 256), np.arange(6656, 6912), np.arange(N - 384, N)])
+    packed, scale, zp = device_experts(13, synthetic.TAG_W, E, N, K)
+    qa, sc = w4.quantize_act(to_dev(x))
+    assert np.array_equal(to_host(qa), qr)
+    ri, od, cd = to_dev(row_index), to_dev(offsets), to_dev(cols)
+    isums = to_host(w4.moe_grouped_gemm_debug_isums(qa, ri, od, packed, zp, max_slots=S)[:, :, cd])
+    out = to_host(w4.moe_grouped_gemm(qa, sc, ri, od, packed, scale, zp, max_slots=S)[:, cd])
+    for e in range(E):
+        s0, s1 = offsets[e], offsets[e + 1]
+        q, s_, z = oracle_columns(orc, 13, synthetic.TAG_W, e, K, cols)
+        rows = row_index[s0:s1]
+        bad = isums[:, s0:s1] != orc.group_isums(qr[rows], q, z)
+        assert not bad.any(), f"expert {e} ({s1 - s0} slots): {int(bad.sum())} sums differ"
+        ref, mag = orc.gemm(qr[rows], sr[rows], q, s_, z)
+        check_close(out[s0:s1], ref, mag, f"expert {e} ({s1 - s0} slots)")
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 512])
 def test_toy_moe_full_size_sampled(orc, B):
     """8 experts, top-1, K=4096, N=14336: route on the GPU, grouped GEMM, combine; the

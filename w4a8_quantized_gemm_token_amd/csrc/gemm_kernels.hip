@@ -2471,6 +2471,42 @@ __global__ __launch_bounds__(kT3Threads) void grouped_tiled3_kernel(
     }
 }
 
+// The same units in 256x256 tiles (tile4_unit: eight 128x64 wave tiles, two LDS stages): half
+// as many units as the 256x128 loop, each weight column unpacked once per 256 rows.
+// EPI = kEpiSilu: tiles of 128 h columns (256 weight rows: gate and up of each h column).
+template <bool ISUMS, int EPI = kEpiOut>
+__global__ __launch_bounds__(kT4Threads) void grouped_tiled4_kernel(
+    const int8_t *__restrict__ qa, const float *__restrict__ a_scale, int64_t R, const int32_t *__restrict__ row_index,
+    const int32_t *__restrict__ offsets, int32_t E, int64_t K, const uint8_t *__restrict__ packed,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ zp, int64_t N, int64_t max_slots,
+    float *__restrict__ out, int32_t *__restrict__ isums, int64_t cmin, T3Epi ep) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ int64_t pfx[kMaxExperts + 1];
+    constexpr int TBN = EPI == kEpiSilu ? kT4BN / 2 : kT4BN;  // output columns per tile
+    const int64_t ntn = ((EPI == kEpiSilu ? ep.half : N) + TBN - 1) / TBN;
+    const int64_t total = expert_prefix(E, pfx, kT4Threads, [&](int e) -> int64_t {
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        return c > cmin ? ((c + kT4BM - 1) / kT4BM) * ntn : 0;
+    });
+    const int64_t G = K / G128;
+    const int64_t nb = gridDim.x;
+    const bool by_xcd = nb % 8 == 0;
+    const int64_t lane_u = by_xcd ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    for (int64_t u = lane_u; u < total; u += nb) {
+        const int e = find_expert(pfx, E, u);
+        const int64_t c = clamp_slots(offsets[e + 1], max_slots) - clamp_slots(offsets[e], max_slots);
+        const int64_t mt = (c + kT4BM - 1) / kT4BM;
+        const int64_t local = u - pfx[e];
+        const int64_t tm = local % mt, tn = local / mt;
+        const int64_t s0 = clamp_slots(offsets[e], max_slots) + tm * kT4BM;
+        const int rows = (int)((c - tm * kT4BM) < kT4BM ? (c - tm * kT4BM) : kT4BM);
+        tile4_unit<ISUMS, EPI>(dsm, qa, a_scale, row_index, R, TileRows{s0, rows}, K,
+                               packed + (int64_t)e * N * (K / 2), (ISUMS ? nullptr : scale + (int64_t)e * G * N),
+                               zp + (int64_t)e * G * N, N, tn * TBN, out, N, isums, max_slots, ep);
+        __syncthreads();  // the next unit reuses the LDS stages and row tables
+    }
+}
+
 template <int MT, int U, int SPLIT>
 hipError_t launch_stream2_t(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *packed,
                             const uint16_t *scale, const uint16_t *zp, int64_t N, float *out, int32_t *isums,
@@ -2845,6 +2881,13 @@ static hipError_t launch_grouped_tiled_s(const int8_t *qa, const float *a_scale,
 #undef W4A8_GTS
 }
 
+// The expert loop over 256x256 tiles when the slots could fill every CU with such tiles at
+// least twice over (an estimate from the slot count: the device-side offsets are not read
+// here); else the 256x128 loop, with twice as many units.
+static bool grouped_tiled4_pays(int64_t max_slots, int64_t N, int cus) {
+    return (max_slots / kT4BM) * ((N + kT4BN - 1) / kT4BN) >= 2 * (int64_t)cus;
+}
+
 // experts with more than cmin slots
 static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, int64_t R, const int32_t *row_index,
                                        const int32_t *expert_offsets, int32_t E, int64_t K, const uint8_t *packed,
@@ -2856,6 +2899,27 @@ static hipError_t launch_grouped_tiled(const int8_t *qa, const float *a_scale, i
         hipError_t err = launch_grouped_tiled_s<2, 2>(qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale,
                                                       zp, N, max_slots, out, isums, cmin, 128, cus, gs, stream);
         if (err != hipSuccess || max_slots <= 128) return err;
+    }
+    if (gs == G128 && tiled3_fits(R, K, N) && grouped_tiled4_pays(max_slots, N, cus)) {
+#define W4A8_GT4(IS, EP, EPA)                                                                                       \
+    do {                                                                                                            \
+        if (hipFuncSetAttribute((const void *)grouped_tiled4_kernel<IS, EP>,                                        \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kT4Lds) != hipSuccess)                  \
+            return hipGetLastError();                                                                               \
+        hipLaunchKernelGGL((grouped_tiled4_kernel<IS, EP>), dim3((uint32_t)cus), dim3(kT4Threads), kT4Lds, stream,  \
+                           qa, a_scale, R, row_index, expert_offsets, E, K, packed, scale, zp, N, max_slots, out,   \
+                           isums, (int64_t)128, EPA);                                                               \
+    } while (0)
+        if (isums) {
+            W4A8_GT4(true, kEpiOut, T3Epi{});
+        } else if (silu) {  // the >128-slot experts with SiLU * up folded into the epilogue
+            W4A8_GT4(false, kEpiSilu, *silu);
+            if (fused_min) *fused_min = 128;
+        } else {
+            W4A8_GT4(false, kEpiOut, T3Epi{});
+        }
+#undef W4A8_GT4
+        return hipGetLastError();
     }
     if (gs == G128 && tiled3_fits(R, K, N)) {
 #define W4A8_GT3(IS)                                                                                                \
