@@ -306,8 +306,12 @@ def run_decode(torch, w4, prep, n_layers, xs, steps, warmup, warmup_s=0.0):
 
     per_m, launch_ms = {}, []
     for M in M_DEC:
-        for i in range(n_layers):            # GPU busy when the start event is reached
-            gemms[M][i]()
+        # a few milliseconds of the same launches first: after the host's synchronize above the
+        # GPU idles briefly, and the first launches after an idle gap run at a lower clock (the
+        # M timed first measured 1-3 us slower than the same M timed later); the GPU is also
+        # still busy when the start event is reached
+        for i in range(max(n_layers, 200)):
+            gemms[M][i % n_layers]()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record(stream)
@@ -461,8 +465,8 @@ def decode_group_sizes(torch, w4, synthetic, copies, reps=50):
             qa, sc = w4.quantize_act(x[:M].contiguous())
             o = torch.empty((M, N_DEC), dtype=torch.float32, device=dev)
             launches = [w4.prepare_gemm(qa, sc, *layers[i], o, group=group) for i in range(copies)]
-            for launch in launches * 4:
-                launch()
+            for i in range(200):   # steady clock before the start event (as in run_decode)
+                launches[i % copies]()
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record(stream)
