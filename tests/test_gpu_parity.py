@@ -487,6 +487,39 @@ def test_grouped_gemm_256x256_loop(orc):
         check_close(out[s0:s1], ref, mag, f"expert {e} ({s1 - s0} slots)")
 
 
+def test_grouped_gemm_rows_past_32bit_offsets(orc):
+    """R * K above 2^32 (1,052,672 activation rows of K = 4096, 4.3 GB): the loops that address
+    rows with 32-bit offsets are not launched, and the streaming and 128-row tiled loops that
+    take every slot class (5, 40, 100 and 200 slots) gather rows on both sides of the 4 GiB
+    boundary; int32 sums bit-exact and fp32 outputs within tolerance for every slot."""
+    w4 = w4mod()
+    K, N = 4096, 256
+    R = (1 << 20) + 4096
+    assert R * K > (1 << 32)
+    counts = [5, 40, 100, 200]
+    E, S = len(counts), sum(counts)
+    rng = np.random.default_rng(17)
+    row_index = rng.integers((1 << 20) - 2048, R, S).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    gen = torch.Generator(device=cuda()).manual_seed(17)
+    qa = torch.randint(-127, 128, (R, K), dtype=torch.int8, device=cuda(), generator=gen)
+    sc = torch.rand((R,), dtype=torch.float32, device=cuda(), generator=gen) * 0.01 + 1e-3
+    ri = to_dev(row_index)
+    qrows, srows = to_host(qa[ri.long()]), to_host(sc[ri.long()])
+    packed, scale, zp = device_experts(17, synthetic.TAG_W, E, N, K)
+    od = to_dev(offsets)
+    isums = to_host(w4.moe_grouped_gemm_debug_isums(qa, ri, od, packed, zp, max_slots=S))
+    out = to_host(w4.moe_grouped_gemm(qa, sc, ri, od, packed, scale, zp, max_slots=S))
+    del qa
+    for e in range(E):
+        s0, s1 = offsets[e], offsets[e + 1]
+        q, s_, z = oracle_columns(orc, 17, synthetic.TAG_W, e, K, np.arange(N))
+        bad = isums[:, s0:s1] != orc.group_isums(qrows[s0:s1], q, z)
+        assert not bad.any(), f"expert {e} ({s1 - s0} slots): {int(bad.sum())} sums differ"
+        ref, mag = orc.gemm(qrows[s0:s1], srows[s0:s1], q, s_, z)
+        check_close(out[s0:s1], ref, mag, f"expert {e} ({s1 - s0} slots)")
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 512])
 def test_toy_moe_full_size_sampled(orc, B):
     """8 experts, top-1, K=4096, N=14336: route on the GPU, grouped GEMM, combine; the
