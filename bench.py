@@ -353,6 +353,28 @@ def cpu_baseline(synthetic):
                       f"{t_total:.1f} s; weight quantization excluded (offline)"}
 
 
+def cpu_prefill_context(synthetic, rows=32):
+    """The oracle on a row sample of the prefill GEMM (the first `rows` of M=4096; all of K=N=8192),
+    repeated for about 4 s; host threads.  Context for the GPU prefill figure, not a baseline of
+    the headline workload."""
+    import oracle
+    orc = oracle.default()
+    W = synthetic.fill_weights_host(0, synthetic.TAG_W, 0, 8192, 0, 8192, "offset")
+    q, s, z = orc.quantize_weights(W)   # offline weight conversion, not timed
+    del W
+    x = synthetic.activations(0, rows, 8192)
+    reps, t_total = 0, 0.0
+    while t_total < 4.0 and reps < 100:
+        t0 = time.perf_counter()
+        qa, sc = orc.quantize_act(x)
+        orc.gemm(qa, sc, q, s, z)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"TOPS": round(2.0 * rows * 8192 * 8192 * reps / t_total / 1e12, 4), "cores": orc.num_threads(),
+            "kind": "oracle", "sample": f"rows 0..{rows - 1} of the M=4096 prefill GEMM (K=N=8192), {reps} "
+                                       f"repetitions, {t_total:.1f} s; weight quantization excluded"}
+
+
 def prefill(torch, w4, synthetic, reps=10, group=GROUP, paths=(0,)):
     """The prefill-shaped dense GEMM (M=4096, K=N=8192): quantize once, then `reps`
     back-to-back prepared launches timed with one event pair on the launch stream.
@@ -684,6 +706,8 @@ def main():
                                **secondary(torch, w4, synthetic, args.copies)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synthetic)
+        if "secondary" in result:
+            result["secondary"]["cpu_oracle_prefill"] = cpu_prefill_context(synthetic)
     print(json.dumps(result), flush=True)
 
 
