@@ -267,8 +267,8 @@ def run_decode(torch, w4, prep, n_layers, xs, steps, warmup, warmup_s=0.0):
     (pointers marshalled), so the host stays ahead of the GPU and kernels run back to back.
     HIP event records are themselves queue packets that cost a few microseconds each, so none
     sits between the kernels of a step; the GEMM's launch duration is taken from one event pair
-    around `steps` back-to-back GEMM launches per M (rotating weight copies, activations from
-    the step) on the same stream."""
+    around max(`steps`, 200) back-to-back GEMM launches per M (rotating weight copies,
+    activations from the step) on the same stream."""
     dev = torch.device("cuda:0")
     quant, gemms = {}, {}
     for M in M_DEC:
@@ -312,14 +312,17 @@ def run_decode(torch, w4, prep, n_layers, xs, steps, warmup, warmup_s=0.0):
         # still busy when the start event is reached
         for i in range(max(n_layers, 200)):
             gemms[M][i % n_layers]()
+        # at least 200 launches between the events: an event record costs a few microseconds,
+        # which over 20 launches would add about 1% to each
+        n_timed = max(steps, 200)
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record(stream)
-        for i in range(steps):
+        for i in range(n_timed):
             gemms[M][i % n_layers]()
         e.record(stream)
         e.synchronize()
-        ms = s.elapsed_time(e) / steps
+        ms = s.elapsed_time(e) / n_timed
         launch_ms.append(ms)
         per_m[str(M)] = {"gemm_us": round(ms * 1e3, 2),
                          "GB/s": round(dense_bytes(M, N_DEC, K_DEC) / (ms * 1e-3) / 1e9, 1),
@@ -467,7 +470,7 @@ def quant_variants(torch, w4, synthetic):
     return res
 
 
-def decode_group_sizes(torch, w4, synthetic, copies, reps=50):
+def decode_group_sizes(torch, w4, synthetic, copies, reps=200):
     """The decode GEMM (K=8192, N=28672, M = 1, 8, 16, standard layout) at group 64 and 256:
     per M, one event pair around `reps` back-to-back prepared launches that rotate `copies`
     weight copies (device packer, outlier weights)."""
