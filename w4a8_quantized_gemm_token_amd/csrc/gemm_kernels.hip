@@ -1586,25 +1586,31 @@ __global__ __launch_bounds__(kT3Threads) void gemm_tiled3_kernel(const int8_t *_
 }
 
 // ------------------------------------------------------------------ tiled loop, 256x256 tiles
-// The same arithmetic as tile3_unit (per-group int32 sums of v_mfma_i32_32x32x32_i8 chains,
-// folded into fp32 in increasing g with one fmaf per element and group) on a 256x256 workgroup
-// tile: eight waves of 128x64 (4x2 chains), two per SIMD, and two LDS stages of 64 KB (the 256
-// activation rows and the 256 unpacked weight columns of one group, in the swizzled layout of
-// t3_sw).  Per output element and group a wave reads 25% fewer fragment bytes from LDS than
-// with 64x64 wave tiles, and the workgroup moves 40% fewer bytes through the vector memory
-// path (one activation tile serves 256 columns).
+// The same arithmetic as tile3_unit (per-group int32 sums, folded into fp32 in increasing g with
+// one fmaf per element and group) on a 256x256 workgroup tile: eight waves of 128x64, two per
+// SIMD, and two LDS stages of 64 KB (the 256 activation rows and the 256 unpacked weight columns
+// of one group, in the swizzled layout of t3_sw).  Per output element and group a wave reads 25%
+// fewer fragment bytes from LDS than with 64x64 wave tiles, and the workgroup moves 40% fewer
+// bytes through the vector memory path than with 256x128 tiles (one activation tile serves 256
+// columns).
 // Iteration g computes group g from stage g % 2; at its top the activations of group g + 1 are
-// requested straight into the other stage and the packed weights into registers (one
-// iteration of lead: that stage was last read before the previous barrier); before the
-// barrier that ends it, the weights are unpacked into that stage.  A wave keeps the weight
-// fragments of the group (both 32-column blocks) and loads the activation fragments of one
-// 32-row block at a time, each step's fragment replacing the one the previous block's
-// second chain has just used.
+// requested straight into the other stage (that stage was last read before the previous
+// barrier).  The packed weights come through registers with two groups of lead: those of group
+// g + 1, requested during iteration g - 1, are unpacked into the other stage a quarter at a time
+// between the MFMA chains of the second half of iteration g, and group g + 2's are requested
+// after them, so that no unpack work or LDS store waits in front of the barrier.
 constexpr int kT4BM = 256, kT4BN = 256;
 constexpr int kT4Threads = 512;
 constexpr int kT4StageA = kT4BM * G128, kT4Stage = kT4StageA + kT4BN * G128;
 constexpr int kT4Lds = 2 * kT4Stage;  // 131072 bytes
 
+// Chains of v_mfma_i32_16x16x64_i8: a wave's 128x64 block is 8 x 4 chains of 16x16 outputs, two
+// MFMAs (k steps of 64) per chain and group, so a chain's int32 sums take 4 registers (the
+// 32x32x32 form needs 16 per chain, and then the packed weights do not fit beside them).
+// During chains 16-31 a quarter of the next group's weights is unpacked every four chains.
+// Step ks of a group: lane quarter qd = l >> 4 supplies codes 16 (4 ks + qd) + [0, 16) of its row
+// (A: row (l & 15) of the row block) and of its column (B: column (l & 15) of the column block);
+// accumulator register r of a chain holds row 4 qd + r, column l & 15.
 template <bool ISUMS, int EPI = kEpiOut>
 __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restrict__ qa,
                                            const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
@@ -1614,13 +1620,12 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
                                            int32_t *__restrict__ isums, int64_t M_isums, const T3Epi &ep = T3Epi{}) {
     static_assert(EPI == kEpiOut || EPI == kEpiSilu, "plain and SiLU epilogues");
     static_assert(EPI == kEpiOut || !ISUMS, "the debug form stores int32 sums only");
-    constexpr int NT = kT4Threads, LA = 4;  // threads; 1 KB activation loads per wave and group
+    constexpr int NT = kT4Threads, LA = 4;
+    constexpr int NBL = ISUMS ? 3 : 7;  // weight loads per thread and group (codes 2, zp 1, scales 4)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int64_t G = K / G128;
-    // weight row of MFMA column c of the tile (-1: past the matrix); kEpiSilu as in tile3_unit
-    // (n0 counts h columns: 128 per tile)
     auto wrow = [&](int c) -> int64_t {
         if constexpr (EPI == kEpiSilu) {
             const int64_t hc = n0 + (c >> 6) * 32 + (c & 31);
@@ -1640,8 +1645,7 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
         if (!ISUMS) row_as[t] = ok ? a_scale[r] : 0.0f;
     }
 
-    // ---- activation loads: load j of wave w fills LDS rows 8 (4 w + j) + [0, 8); lane l
-    // brings row 8 (4 w + j) + (l >> 3), chunk (l & 7) of the swizzled layout
+    // ---- activation loads (as tile4_unit)
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa);
     uint32_t aoff[LA];
 #pragma unroll
@@ -1660,30 +1664,28 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
                                                      (int)(g * G128), 0, 0);
     };
 
-    // ---- packed weights: thread t takes column t >> 1 of the tile, bytes 32 (t & 1) + [0, 32)
-    // of a group (codes 64 (t & 1) + [0, 64)), with that column's zero point; and this lane's
-    // two output columns' scales
+    // ---- packed weights (as tile4_unit: thread t unpacks column t >> 1, codes 64 (t & 1) + [0, 64));
+    // this lane's four output columns' scales
     const int bcol = tid >> 1, bpart = tid & 1;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);  // (unused by the debug form)
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);
     uint32_t boff, zoff;
     {
         const int64_t gc = wrow(bcol) >= 0 ? wrow(bcol) : 0;
         boff = (uint32_t)(gc * (K / 2)) + (uint32_t)(32 * bpart);
         zoff = (uint32_t)(gc * 2);
     }
-    int64_t scol[2];
-    uint32_t soff[2];
+    const int frow = lane & 15, qd = lane >> 4;
+    uint32_t soff[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t wr = wrow(wn * 64 + j * 32 + (lane & 31));
-        scol[j] = wr >= 0 ? wr : N;
-        soff[j] = (uint32_t)((wr >= 0 ? wr : 0) * 2);
+    for (int cb = 0; cb < 4; ++cb) {
+        const int64_t wr = wrow(wn * 64 + 16 * cb + frow);
+        soff[cb] = (uint32_t)((wr >= 0 ? wr : 0) * 2);
     }
     struct Slot {
         v4u rb0, rb1;
-        uint32_t rz, rs0, rs1;
+        uint32_t rz, rs[4];
     };
     auto b_load = [&](Slot &x, int64_t g) {
         const int gs = (int)(g * N * 2);
@@ -1691,154 +1693,167 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
         x.rb1 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff + 16, (int)(g * (G128 / 2)), 0);
         x.rz = __builtin_amdgcn_raw_buffer_load_b16(rz, zoff, gs, 0);
         if constexpr (!ISUMS) {
-            x.rs0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[0], gs, 0);
-            x.rs1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[1], gs, 0);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) x.rs[cb] = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[cb], gs, 0);
         } else {
-            x.rs0 = x.rs1 = 0;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) x.rs[cb] = 0;
         }
     };
-    auto b_store = [&](const Slot &x, int st) {
+    // quarter q of the unpack: codes 16 q + [0, 16) of this thread's 64 into chunk 4 bpart + q
+    auto b_part = [&](const Slot &x, int st, int q, uint32_t zadd) {
         uint8_t *B = lds + st * kT4Stage + kT4StageA;
-        const uint32_t zadd = zp_add_const((uint16_t)x.rz);
-        const uint32_t d8[8] = {x.rb0.x, x.rb0.y, x.rb0.z, x.rb0.w, x.rb1.x, x.rb1.y, x.rb1.z, x.rb1.w};
-        uint32_t w[16];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) unpack8(d8[k], zadd, w[2 * k], w[2 * k + 1]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<v4u *>(B + t3_sw(bcol, 4 * bpart + q)) = v4u{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+        const uint32_t d0 = q == 0 ? x.rb0.x : (q == 1 ? x.rb0.z : (q == 2 ? x.rb1.x : x.rb1.z));
+        const uint32_t d1 = q == 0 ? x.rb0.y : (q == 1 ? x.rb0.w : (q == 2 ? x.rb1.y : x.rb1.w));
+        uint32_t w0, w1, w2, w3;
+        unpack8(d0, zadd, w0, w1);
+        unpack8(d1, zadd, w2, w3);
+        *reinterpret_cast<v4u *>(B + t3_sw(bcol, 4 * bpart + q)) = v4u{w0, w1, w2, w3};
     };
 
-    // ---- compute: lane l feeds A row (l & 31) / B column (l & 31) of a 32x32 tile with the 16
-    // bytes of chunk 2 ks + (l >> 5) and holds accumulator rows 8 (r >> 2) + 4 (l >> 5) + (r & 3);
-    // row block i and column block j are the first block's addresses plus 4096 i / 4096 j
-    // (32 rows of 128 bytes; the swizzle repeats every 16 rows)
-    const int frow = lane & 31, fch = lane >> 5;
-    int aofs[4], bofs[4];
+    // ---- fragments: row block rb (16 rows) and column block cb (16 columns) are the first
+    // block's addresses plus 2048 rb / 2048 cb (the swizzle repeats every 16 rows)
+    int aofs[2], bofs[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        aofs[ks] = t3_sw(wm * 128 + frow, 2 * ks + fch);
-        bofs[ks] = kT4StageA + t3_sw(wn * 64 + frow, 2 * ks + fch);
+    for (int ks = 0; ks < 2; ++ks) {
+        aofs[ks] = t3_sw(wm * 128 + frow, 4 * ks + qd);
+        bofs[ks] = kT4StageA + t3_sw(wn * 64 + frow, 4 * ks + qd);
     }
-    float acc[4][2][16];
+    auto scol = [&](int cb) -> int64_t {
+        const int64_t wr = wrow(wn * 64 + 16 * cb + frow);
+        return wr >= 0 ? wr : N;
+    };
+    float acc[8][4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
-    float sc[2] = {0.0f, 0.0f}, scn[2] = {0.0f, 0.0f};
-    // Rolling consumption, as in tile3_unit: chain c = 2 i + j of a group runs while chain c - 1
-    // is folded (or, in the debug form, stored); the last chain of group g is consumed during
-    // the first chain of group g + 1.  Every element still takes its groups in increasing g.
-    v16i prev = {};
-    float prev_sc = 0.0f;  // fmaf(0, 0, acc) == acc before the first group
-    int64_t prev_g = -1;   // (debug form: no chain before the first)
-    auto consume = [&](const v16i &dd, int i, int j, float s_, int64_t g) {
+    // Rolling consumption: chain c = 4 rb + cb runs while chain c - 1 is folded; the last chain of
+    // a group is folded during the first chain of the next (every element takes its groups in
+    // increasing g)
+    v4i prev = {};
+    float prev_sc = 0.0f;
+    int64_t prev_g = -1;
+    auto consume = [&](const v4i &dd, int rb, int cb, float s_, int64_t g) {
         if constexpr (ISUMS) {
             if (g < 0) return;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
-                if (m < rows.rows && scol[j] < N) isums[(g * M_isums + rows.slot0 + m) * N + scol[j]] = dd[r];
+            for (int r = 0; r < 4; ++r) {
+                const int m = wm * 128 + 16 * rb + 4 * qd + r;
+                if (m < rows.rows && scol(cb) < N) isums[(g * M_isums + rows.slot0 + m) * N + scol(cb)] = dd[r];
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s_, (float)dd[r], acc[i][j][r]);
+            for (int r = 0; r < 4; ++r) acc[rb][cb][r] = fmaf(s_, (float)dd[r], acc[rb][cb][r]);
         }
     };
-    // Pins the folded values at the end of a chain's scheduling region: left alone, the
-    // compiler sinks every fold below the last chain and keeps all eight chains' sums live.
-    // (After the region's group barriers: an asm statement ends a scheduling region.)
-    auto pin = [&](int i, int j) {
+    auto pin = [&](int rb, int cb) {
         if constexpr (!ISUMS) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) __asm__ volatile("" : "+v"(acc[i][j][r]));
+            for (int r = 0; r < 4; ++r) __asm__ volatile("" : "+v"(acc[rb][cb][r]));
         }
     };
-    auto group = [&](int st, int64_t g) {
+
+    float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, scn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    Slot sl;
+    uint32_t zadd = 0;
+    // group g from stage st; during chains 16-31 the next group's weights (in sl) are unpacked into
+    // stage st ^ 1 and group g2's requested
+    auto group = [&](int st, int64_t g, int64_t g2) {
         const uint8_t *base = lds + st * kT4Stage;
-        // the group's first fragments in the order the first chain takes them; the last
-        // group's last chain is folded while they arrive
-        v4i b[2][4], a[4];
+        v4i b[4][2], a[2], an[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            a[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks]);
-            b[0][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks]);
-        }
+        for (int ks = 0; ks < 2; ++ks) a[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) b[1][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks] + 4096);
-        consume(prev, 3, 1, prev_sc, prev_g);
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
-        pin(3, 1);
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) b[cb][ks] = *reinterpret_cast<const v4i *>(base + bofs[ks] + 2048 * cb);
+        consume(prev, 7, 3, prev_sc, prev_g);
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        pin(7, 3);
         __builtin_amdgcn_sched_barrier(0);
-        v16i d = {};
+        v4i d = {};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = c >> 1, j = c & 1;
-            v16i dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[j][0], v16i{}, 0, 0, 0);
+        for (int c = 0; c < 32; ++c) {
+            const int rb = c >> 2, cb = c & 3;
+            v4i dn = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], b[cb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+            dn = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[1], b[cb][1], dn, 0, 0, 0);
+            if (cb == 0 && rb < 7) {  // the next row block's fragments
 #pragma unroll
-            for (int ks = 1; ks < 4; ++ks) dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ks], b[j][ks], dn, 0, 0, 0);
-            if (j == 1 && i < 3) {
-                // the next row block's fragments, each after the MFMA that last reads its register
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    a[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks] + 4096 * (i + 1));
+                for (int ks = 0; ks < 2; ++ks) an[ks] = *reinterpret_cast<const v4i *>(base + aofs[ks] + 2048 * (rb + 1));
             }
-            if (c > 0) consume(d, (c - 1) >> 1, (c - 1) & 1, sc[(c - 1) & 1], g);
+            if (c > 0) consume(d, (c - 1) >> 2, (c - 1) & 3, sc[(c - 1) & 3], g);
+            const bool piece = c >= 16 && (c & 3) == 0;
+            if (piece) {
+                const int q = (c - 16) >> 2;
+                if (q == 0) zadd = zp_add_const((uint16_t)sl.rz);
+                b_part(sl, st ^ 1, q, zadd);
+                if (q == 3) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (j == 1 && i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    for (int j = 0; j < 4; ++j) scn[j] = half_bits_to_float((uint16_t)sl.rs[j]);
+                    b_load(sl, g2);
+                }
             }
-            if (c > 0) pin((c - 1) >> 1, (c - 1) & 1);
-            // (one chain per scheduling region: the chains are independent, and letting them
-            // interleave keeps eight 16-register results live at once)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (cb == 0 && rb < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            if (piece) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (c == 28) {
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, NBL, 0);
+                }
+            }
+            if (c > 0) pin((c - 1) >> 2, (c - 1) & 3);
             __builtin_amdgcn_sched_barrier(0);
             d = dn;
+            if (cb == 3 && rb < 7) {
+                a[0] = an[0];
+                a[1] = an[1];
+            }
         }
         prev = d;
-        prev_sc = sc[1];
+        prev_sc = sc[3];
         prev_g = g;
     };
 
-    // ---- prologue: group 0 into stage 0
-    Slot sl;
+    // ---- prologue: group 0 into stage 0; group 1's weights requested
     a_dma(0, 0);
     b_load(sl, 0);
     __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 15));
-    b_store(sl, 0);
-    scn[0] = half_bits_to_float((uint16_t)sl.rs0);
-    scn[1] = half_bits_to_float((uint16_t)sl.rs1);
-    stage_barrier<0>();
+    {
+        const uint32_t z0 = zp_add_const((uint16_t)sl.rz);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b_part(sl, 0, q, z0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scn[j] = half_bits_to_float((uint16_t)sl.rs[j]);
+    b_load(sl, G > 1 ? 1 : 0);
+    stage_barrier<NBL>();
 
-    // ---- main loop, unrolled by two so that the stage index is a constant
+    // ---- main loop, unrolled by two so that the stage index is a constant; past the last group
+    // the loads repeat group G - 1 into a stage no longer read (the waits stay the same)
     auto body = [&](auto stc, int64_t g) {
         constexpr int ST = decltype(stc)::value;
-        const bool more = g + 1 < G;  // (uniform)
-        sc[0] = scn[0];
-        sc[1] = scn[1];
-        __asm__ volatile("" ::: "memory");
-        if (more) {
-            a_dma(ST ^ 1, g + 1);
-            b_load(sl, g + 1);
-        }
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        group(ST, g);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 15));
-            b_store(sl, ST ^ 1);
-            scn[0] = half_bits_to_float((uint16_t)sl.rs0);
-            scn[1] = half_bits_to_float((uint16_t)sl.rs1);
-        }
+        const int64_t g1 = g + 1 < G ? g + 1 : G - 1, g2 = g + 2 < G ? g + 2 : G - 1;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) __asm__ volatile("" : "+v"(scn[h]));
-        stage_barrier<0>();
+        for (int j = 0; j < 4; ++j) sc[j] = scn[j];
+        __asm__ volatile("" ::: "memory");
+        a_dma(ST ^ 1, g1);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        group(ST, g, g2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(scn[j]));
+        stage_barrier<NBL>();  // group g + 1 is in its stage; g + 2's weights may still be in flight
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -1848,45 +1863,49 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
         body(I1{}, g + 1);
     }
     if (g < G) body(I0{}, g);
-    consume(prev, 3, 1, prev_sc, prev_g);  // the last group's last chain
+    __builtin_amdgcn_s_waitcnt(0);  // the last (unused) weight loads
+    consume(prev, 7, 3, prev_sc, prev_g);
 
     if constexpr (!ISUMS && EPI == kEpiOut) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int rbk = 0; rbk < 8; ++rbk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
+            for (int r = 0; r < 4; ++r) {
+                const int m = wm * 128 + 16 * rbk + 4 * qd + r;
                 if (m < rows.rows && row_ok[m]) {
                     const int64_t slot = rows.slot0 + m;
                     const float as = row_as[m];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        if (scol[j] < N) out[slot * ldo + scol[j]] = as * acc[i][j][r];
+                    for (int cb = 0; cb < 4; ++cb)
+                        if (scol(cb) < N) out[slot * ldo + scol(cb)] = as * acc[rbk][cb][r];
                 }
             }
     } else if constexpr (EPI == kEpiSilu) {
-        const int64_t hc = n0 + wn * 32 + (lane & 31);  // this lane's h column
-        const bool col_ok = hc < ep.half;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int hb = 0; hb < 2; ++hb) {
+            const int64_t hc = n0 + wn * 32 + 16 * hb + frow;  // this lane's h column
+            const bool col_ok = hc < ep.half;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fch + (r & 3);
-                const bool ok = m < rows.rows && row_ok[m];
-                const float as = row_as[m];
-                const float gate = as * acc[i][0][r], up = as * acc[i][1][r];
-                const float h = silu_mul(gate, up);
-                float hm = (ok && col_ok) ? fabsf(h) : 0.0f;
-                hm = dpp_max<0xB1>(hm);   // quad_perm [1,0,3,2]
-                hm = dpp_max<0x4E>(hm);   // quad_perm [2,3,0,1]
-                hm = dpp_max<0x124>(hm);  // row_ror:4
-                hm = dpp_max<0x128>(hm);  // row_ror:8
-                if (ok) {
-                    float *line = out + (rows.slot0 + m) * ldo;
-                    if (col_ok) line[hc] = h;
-                    if ((lane & 15) == 0) line[ep.half + (n0 + wn * 32 + (lane & 16)) / 16] = hm;
+            for (int rbk = 0; rbk < 8; ++rbk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = wm * 128 + 16 * rbk + 4 * qd + r;
+                    const bool ok = m < rows.rows && row_ok[m];
+                    const float as = row_as[m];
+                    const float gate = as * acc[rbk][hb][r], up = as * acc[rbk][hb + 2][r];
+                    const float hv = silu_mul(gate, up);
+                    float hm = (ok && col_ok) ? fabsf(hv) : 0.0f;
+                    hm = dpp_max<0xB1>(hm);   // quad_perm [1,0,3,2]
+                    hm = dpp_max<0x4E>(hm);   // quad_perm [2,3,0,1]
+                    hm = dpp_max<0x124>(hm);  // row_ror:4
+                    hm = dpp_max<0x128>(hm);  // row_ror:8
+                    if (ok) {
+                        float *line = out + (rows.slot0 + m) * ldo;
+                        if (col_ok) line[hc] = hv;
+                        if (frow == 0) line[ep.half + (n0 + wn * 32 + 16 * hb) / 16] = hm;
+                    }
                 }
-            }
+        }
     }
 }
 
