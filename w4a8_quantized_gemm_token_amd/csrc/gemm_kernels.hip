@@ -1798,11 +1798,11 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
                     b_load(sl, g2);
                 }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            // both MFMAs of the chain first, then the previous chain's fold (measured 3-4% faster
+            // than one MFMA, four fold instructions, the other MFMA, the other four)
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (cb == 0 && rb < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            if (c > 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
             if (piece) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
                 __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
