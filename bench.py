@@ -378,7 +378,7 @@ def cpu_prefill_context(synthetic, rows=32):
                                        f"repetitions, {t_total:.1f} s; weight quantization excluded"}
 
 
-def prefill(torch, w4, synthetic, reps=10, group=GROUP, paths=(0,)):
+def prefill(torch, w4, synthetic, reps=20, group=GROUP, paths=(0,)):
     """The prefill-shaped dense GEMM (M=4096, K=N=8192): quantize once, then `reps`
     back-to-back prepared launches timed with one event pair on the launch stream.
     Group sizes other than 128 are packed by the host packer (the device packer takes 128)."""
@@ -399,8 +399,7 @@ def prefill(torch, w4, synthetic, reps=10, group=GROUP, paths=(0,)):
     res = {}
     for path in paths:  # (0: the loop w4a8_gemm picks; others force one, for comparisons)
         launch = w4.prepare_gemm(qa, sc, *layer, out_buf, group=group, path=path)
-        for _ in range(40):  # about 20 ms of warm-up
-            launch()
+        _warm(torch, [launch])
         stream = torch.cuda.current_stream()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
@@ -490,8 +489,7 @@ def decode_group_sizes(torch, w4, synthetic, copies, reps=200):
             qa, sc = w4.quantize_act(x[:M].contiguous())
             o = torch.empty((M, N_DEC), dtype=torch.float32, device=dev)
             launches = [w4.prepare_gemm(qa, sc, *layers[i], o, group=group) for i in range(copies)]
-            for i in range(200):   # steady clock before the start event (as in run_decode)
-                launches[i % copies]()
+            _warm(torch, launches)   # steady clock before the start event
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record(stream)
@@ -529,10 +527,21 @@ def _device_experts(torch, w4, synthetic, seed, tag, E, N, K):
         E, N, K, lambda e, W: synthetic.fill_weights_device(W, seed, tag, e, K, 0, "plain"), dev)
 
 
+def _warm(torch, fns, seconds=0.3):
+    """Runs the launches for at least `seconds` (in batches, synchronized): the clock of a GPU that
+    was idle or on lighter work takes longer than a few launches to settle."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fns[i % len(fns)]()
+            i += 1
+        torch.cuda.synchronize()
+
+
 def _timed(torch, fns, reps):
     stream = torch.cuda.current_stream()
-    for i in range(20):
-        fns[i % len(fns)]()
+    _warm(torch, fns)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
     for i in range(reps):
