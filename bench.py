@@ -508,9 +508,10 @@ def decode_group_sizes(torch, w4, synthetic, copies, reps=200):
 
 
 def secondary(torch, w4, synthetic, copies):
-    """Prefill (M=4096, K=N=8192) TOPS, decode at group 64 and 256, MoE layer times and the
-    smoothing figures; context."""
-    out = {**decode_group_sizes(torch, w4, synthetic, copies),
+    """torch's own streaming kernels on this machine, prefill (M=4096, K=N=8192) TOPS, decode at group 64 and
+    256, MoE layer times and the smoothing figures; context."""
+    out = {"torch_streaming_1GiB": torch_streaming(torch),
+           **decode_group_sizes(torch, w4, synthetic, copies),
            "prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
            "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
            "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
@@ -549,6 +550,22 @@ def _timed(torch, fns, reps):
     e.record(stream)
     torch.cuda.synchronize()
     return s.elapsed_time(e) / reps
+
+
+def torch_streaming(torch, nbytes=1 << 30, reps=20):
+    """A plain read (sum) and a copy of 1 GiB with torch's own kernels (larger than the 256 MB
+    MALL): the HBM bandwidth an ordinary streaming kernel gets on this machine.  Context for the
+    roofline fractions, which stay against the 8 TB/s datasheet peak."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    red = torch.empty((), dtype=torch.float32, device="cuda:0")
+    read_ms = _timed(torch, [lambda: torch.sum(a, dim=0, out=red)], reps)
+    copy_ms = _timed(torch, [lambda: b.copy_(a)], reps)
+    del a, b, red
+    torch.cuda.empty_cache()
+    return {"read_GB/s": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+            "copy_GB/s": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
+            "kernels": "torch.sum over 1 GiB of fp32 (read bytes); torch copy_ of 1 GiB (read + write bytes)"}
 
 
 def toy_moe(torch, w4, synthetic, batches, reps=60):
