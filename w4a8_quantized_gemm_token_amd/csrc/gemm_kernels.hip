@@ -449,23 +449,12 @@ __device__ __forceinline__ void stage_rows_dma(uint8_t *lds, int64_t lda, const 
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(qa);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int bpr = (int)((K + 1023) / 1024);  // 1 KB blocks per row
-    // 32-bit arithmetic throughout (K and the offsets are below 2^32), each product kept apart
-    // from its add: a multiply feeding an add becomes v_mad_u64_u32, whose unused high addend
-    // half the compiler has paired with a register that a weight load was still filling, so the
-    // staging (issued after the first weight windows in the expert loop) waited for the weights
-    const int k32 = (int)K;
     for (int i = wave; i < nrows * bpr; i += nwaves) {
         const int r = i / bpr;
-        int rb = r * bpr;
-        __asm__("" : "+v"(rb));
-        const int b = i - rb;
-        int cb = b * 1024;
-        __asm__("" : "+v"(cb));
-        if (cb + lane * 16 < k32) {
-            uint32_t p = (uint32_t)src_row(r) * (uint32_t)k32;
-            __asm__("" : "+v"(p));
-            const uint32_t off = p + (uint32_t)(cb + lane * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + r * lda + cb), 16, (int)off, 0, 0, 0);
+        const int b = i - r * bpr;
+        if (b * 1024 + lane * 16 < K) {
+            const uint32_t off = (uint32_t)(src_row(r) * K + b * 1024 + lane * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + r * lda + b * 1024), 16, (int)off, 0, 0, 0);
         }
     }
 }
