@@ -292,6 +292,28 @@ def test_route_bit_exact(orc, T, E, k, kind, seed):
     assert np.array_equal(rows, perm_r // k)
 
 
+@pytest.mark.parametrize("T,E,k,kind,shared", [(16, 384, 8, "skewed", True), (13, 1024, 8, "iid", False),
+                                               (16, 40, 3, "iid", True), (5, 8, 2, "iid", False)])
+def test_route_small_batch_one_launch(orc, T, E, k, kind, shared):
+    """Batches of at most 16 tokens are routed and bucketed by one workgroup (one launch); the
+    tables are the oracle's bit for bit, with the shared expert's slots appended when asked."""
+    w4 = w4mod()
+    logits = (synthetic.router_logits_iid(11, T, E) if kind == "iid" else synthetic.router_logits_skewed(1, T, E))
+    ids, w, off, perm, rows, sop = (to_host(t) for t in w4.moe_route(to_dev(logits).reshape(T, E), k, shared))
+    ids_r, w_r = orc.route_topk(logits.reshape(T, E), k)
+    off_r, perm_r = orc.bucket(ids_r, E)
+    assert np.array_equal(ids, ids_r)
+    assert np.allclose(w, w_r, rtol=2e-6, atol=1e-7)
+    assert np.array_equal(off[:E + 1], off_r) and np.array_equal(perm, perm_r)
+    inv = np.empty_like(perm_r)
+    inv[perm_r] = np.arange(len(perm_r), dtype=np.int32)
+    assert np.array_equal(sop, inv)
+    assert np.array_equal(rows[:T * k], perm_r // k)
+    if shared:
+        assert off[E + 1] == T * k + T
+        assert np.array_equal(rows[T * k:], np.arange(T, dtype=np.int32))
+
+
 def test_route_ties_go_to_lower_expert():
     w4 = w4mod()
     logits = np.zeros((3, 16), np.float32)

@@ -53,12 +53,9 @@ __device__ __forceinline__ void argmax_step(float &bv, int &bi) {
 // as scalars -- no LDS round trips, no branches.  Every lane ends up with all k picks;
 // lane j writes pick j.
 template <int PER>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
-                                                                   int32_t E, int32_t k, int32_t *__restrict__ ids,
-                                                                   float *__restrict__ w) {
+__device__ __forceinline__ void route_token(const float *__restrict__ logits, int64_t t, int32_t E, int32_t k,
+                                            int32_t *__restrict__ ids, float *__restrict__ w) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x >> 6);
-    if (t >= T) return;  // whole waves
     const float *row = logits + t * E;
     float v[PER];
     uint32_t taken = 0;  // bit i: logit i * 64 + lane already picked (or past E)
@@ -118,6 +115,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
     }
 }
 
+template <int PER>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
+                                                                   int32_t E, int32_t k, int32_t *__restrict__ ids,
+                                                                   float *__restrict__ w) {
+    const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole waves
+    route_token<PER>(logits, t, E, k, ids, w);
+}
+
 constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / kWave;
 
@@ -137,12 +143,10 @@ constexpr int kBucketWaves = kBucketThreads / kWave;
 // atomics on positions; four barriers in all.
 // kBatch 64-pair chunks have their expert ids loaded together (their latencies overlap).
 template <int kBatch>
-__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *__restrict__ ids, int64_t P, int32_t E,
-                                                                int32_t k, int64_t shared_T,
-                                                                int32_t *__restrict__ offsets,
-                                                                int32_t *__restrict__ perm,
-                                                                int32_t *__restrict__ slot_row,
-                                                                int32_t *__restrict__ slot_of_pair) {
+__device__ __forceinline__ void bucket_pairs(const int32_t *__restrict__ ids, int64_t P, int32_t E, int32_t k,
+                                             int64_t shared_T, int32_t *__restrict__ offsets,
+                                             int32_t *__restrict__ perm, int32_t *__restrict__ slot_row,
+                                             int32_t *__restrict__ slot_of_pair) {
     __shared__ int32_t hist[kBucketWaves][kMaxE];  // counts, then each wave's running slot
     __shared__ int32_t wave_sum[kBucketWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -230,6 +234,35 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *_
         for (int64_t t = tid; t < shared_T; t += kBucketThreads) slot_row[P + t] = (int32_t)t;
 }
 
+template <int kBatch>
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t *__restrict__ ids, int64_t P, int32_t E,
+                                                                int32_t k, int64_t shared_T,
+                                                                int32_t *__restrict__ offsets,
+                                                                int32_t *__restrict__ perm,
+                                                                int32_t *__restrict__ slot_row,
+                                                                int32_t *__restrict__ slot_of_pair) {
+    bucket_pairs<kBatch>(ids, P, E, k, shared_T, offsets, perm, slot_row, slot_of_pair);
+}
+
+// Routing and bucketing of a small batch (T <= kFusedRouteT, at most one token per wave) in
+// one workgroup: wave w routes token w, and after a barrier -- which also makes the waves'
+// writes of ids visible to the whole workgroup -- the same workgroup buckets the pairs.  One
+// launch instead of two; the tables are the same bits.  (With four tokens per wave, at T = 64,
+// the one CU's serial routing cost more than the launch it saves.)
+constexpr int64_t kFusedRouteT = 16;
+template <int PER>
+__global__ __launch_bounds__(kBucketThreads) void route_bucket_kernel(const float *__restrict__ logits, int64_t T,
+                                                                      int32_t E, int32_t k, int32_t *__restrict__ ids,
+                                                                      float *__restrict__ w, int64_t shared_T,
+                                                                      int32_t *__restrict__ offsets,
+                                                                      int32_t *__restrict__ perm,
+                                                                      int32_t *__restrict__ slot_row,
+                                                                      int32_t *__restrict__ slot_of_pair) {
+    for (int64_t t = threadIdx.x >> 6; t < T; t += kBucketWaves) route_token<PER>(logits, t, E, k, ids, w);
+    __syncthreads();
+    bucket_pairs<1>(ids, T * k, E, k, shared_T, offsets, perm, slot_row, slot_of_pair);
+}
+
 constexpr int kCombineThreads = 256;
 // grid: (T, ceil(H/4 / 256)); each thread one float4 of one token row
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ y,
@@ -279,6 +312,20 @@ namespace w4a8 {
 hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk, int32_t with_shared, int32_t *ids,
                             float *w, int32_t *offsets, int32_t *perm, int32_t *slot_row, int32_t *slot_of_pair,
                             hipStream_t stream) {
+    const int64_t shared_f = with_shared ? T : (int64_t)0;
+    if (T > 0 && T <= kFusedRouteT && T * topk <= (int64_t)kBucketThreads) {
+        const int per = (E + kWave - 1) / kWave;
+#define W4A8_RB(PP)                                                                                                 \
+    hipLaunchKernelGGL(route_bucket_kernel<PP>, dim3(1), dim3(kBucketThreads), 0, stream, logits, T, E, topk, ids, w, \
+                       shared_f, offsets, perm, slot_row, slot_of_pair)
+        if (per <= 1) W4A8_RB(1);
+        else if (per <= 2) W4A8_RB(2);
+        else if (per <= 4) W4A8_RB(4);
+        else if (per <= 8) W4A8_RB(8);
+        else W4A8_RB(kPerLane);
+#undef W4A8_RB
+        return hipGetLastError();
+    }
     if (T > 0) {
         const dim3 grid((uint32_t)((T + kRouteThreads / kWave - 1) / (kRouteThreads / kWave))), block(kRouteThreads);
         const int per = (E + kWave - 1) / kWave;  // logits per lane, rounded up to a power of two
