@@ -18,6 +18,8 @@
 //    own pairs in increasing pair index (ballots over the expert id bits rank
 //    lanes with the same expert) -- stable, deterministic, no atomics on
 //    positions.
+//  * route_bucket: both in one launch for batches of at most 16 tokens (the bucketing
+//    workgroup's waves route one token each first).
 //  * combine: out[t] = sum_j w[t][j] * y[slot(t, j)] + y_shared[t], float4 wide.
 #include "w4a8_internal.hpp"
 
