@@ -240,6 +240,8 @@ def parse():
     p.add_argument("--path", type=int, action="append",
                    help="main loop of --only prefill (as w4a8_gemm_path; default: the one w4a8_gemm picks); "
                         "repeatable, each timed in turn")
+    p.add_argument("--tile-major", action="store_true",
+                   help="--only prefill on the tile-major weight array (w4a8_gemm_tm; group 128)")
     return p.parse_args()
 
 
@@ -378,10 +380,11 @@ def cpu_prefill_context(synthetic, rows=32):
                                        f"repetitions, {t_total:.1f} s; weight quantization excluded"}
 
 
-def prefill(torch, w4, synthetic, reps=20, group=GROUP, paths=(0,)):
+def prefill(torch, w4, synthetic, reps=20, group=GROUP, paths=(0,), tile_major=False):
     """The prefill-shaped dense GEMM (M=4096, K=N=8192): quantize once, then `reps`
     back-to-back prepared launches timed with one event pair on the launch stream.
-    Group sizes other than 128 are packed by the host packer (the device packer takes 128)."""
+    Group sizes other than 128 are packed by the host packer (the device packer takes 128).
+    tile_major: the same weights converted to the tile-major array, run by w4a8_gemm_tm."""
     dev = torch.device("cuda:0")
     M, N, K = 4096, 8192, 8192
     W = torch.empty((N, K), dtype=torch.float32, device=dev)
@@ -397,8 +400,14 @@ def prefill(torch, w4, synthetic, reps=20, group=GROUP, paths=(0,)):
     qa, sc = w4.quantize_act(x)
     out_buf = torch.empty((M, N), dtype=torch.float32, device=dev)
     res = {}
+    if tile_major:
+        layer = (w4.weights_to_tm(*layer),)
+        paths = ("tm",)
     for path in paths:  # (0: the loop w4a8_gemm picks; others force one, for comparisons)
-        launch = w4.prepare_gemm(qa, sc, *layer, out_buf, group=group, path=path)
+        if tile_major:
+            launch = w4.prepare_gemm_tm(qa, sc, layer[0], out_buf)
+        else:
+            launch = w4.prepare_gemm(qa, sc, *layer, out_buf, group=group, path=path)
         _warm(torch, [launch])
         stream = torch.cuda.current_stream()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -513,6 +522,7 @@ def secondary(torch, w4, synthetic, copies):
     out = {"torch_streaming_1GiB": torch_streaming(torch),
            **decode_group_sizes(torch, w4, synthetic, copies),
            "prefill_M4096_K8192_N8192": prefill(torch, w4, synthetic),
+           "prefill_M4096_K8192_N8192_tile_major": prefill(torch, w4, synthetic, tile_major=True),
            "prefill_M4096_K8192_N8192_group64": prefill(torch, w4, synthetic, group=64),
            "prefill_M4096_K8192_N8192_group256": prefill(torch, w4, synthetic, group=256),
            "quant_variants_K8192_N4096_M16": quant_variants(torch, w4, synthetic)}
@@ -681,8 +691,12 @@ def main():
     w4.load()
     if args.only:
         if args.only == "prefill":
-            res = {f"prefill_M4096_K8192_N8192_group{args.group}": prefill(torch, w4, synthetic, args.reps,
-                                                                            args.group, tuple(args.path or (0,)))}
+            if args.tile_major and args.group != GROUP:
+                print("bench.py: --tile-major takes group 128", file=sys.stderr)
+                return 2
+            key = "prefill_M4096_K8192_N8192_" + ("tile_major" if args.tile_major else f"group{args.group}")
+            res = {key: prefill(torch, w4, synthetic, args.reps, args.group, tuple(args.path or (0,)),
+                                tile_major=args.tile_major)}
         elif args.only == "toy_moe":
             res = toy_moe(torch, w4, synthetic, args.size or (1, 2, 4, 512), args.reps)
         else:

@@ -250,12 +250,14 @@ w4a8_status w4a8_weights_to_tm(const uint8_t *packed, const uint16_t *scale, con
                                int64_t N, int64_t K, int32_t group, uint8_t *tm,
                                hipStream_t stream);
 
-/* Device.  out[M][N] as w4a8_gemm, with the weights in the tile-major array, for
- * the decode sizes 1 <= M <= 16.  Output bytes are identical to w4a8_gemm's for
- * the same weights.  Besides w4a8_gemm's conditions it needs K % 256 == 0,
- * M * (K + 16) <= 143360 (the staged activation rows) and a tile-major array
- * below 4 GiB; anything else is W4A8_EINVAL (use w4a8_gemm for larger M).
- * M == 0 is a no-op. */
+/* Device.  out[M][N] as w4a8_gemm, with the weights in the tile-major array.
+ * M <= 16 runs the decode loop: output bytes identical to w4a8_gemm's for the same
+ * weights.  M > 16 runs the 256x256 tiled loop, where the tile-major nibble order
+ * spares the unpack its byte permutes: output bytes identical to w4a8_gemm_path's
+ * path 5 (the same loop over the standard layout).  Besides w4a8_gemm's conditions
+ * it needs K % 256 == 0, a tile-major array below 4 GiB, and M * (K + 16) <= 143360
+ * (the staged activation rows) for M <= 16 or M * K < 2^32 above; anything else
+ * is W4A8_EINVAL.  M == 0 is a no-op. */
 w4a8_status w4a8_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K,
                          const uint8_t *tm, int64_t N, int32_t group, float *out,
                          hipStream_t stream);

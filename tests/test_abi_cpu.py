@@ -102,8 +102,9 @@ def test_validation_rejects_before_launch():
     assert lib.w4a8_weights_to_tm(f, f, f, 120, 256, 128, f, None) == EINVAL
     assert lib.w4a8_weights_to_tm(f, f, f, 128, 256, 64, f, None) == EUNSUPPORTED
     assert lib.w4a8_weights_to_tm(f, f, f, 128, 256, 128, _fake(4104), None) == EINVAL
-    assert lib.w4a8_gemm_tm(f, f, 17, 256, f, 128, 128, f, None) == EINVAL
-    assert b"1 <= M <= 16" in lib.w4a8_last_error()
+    assert lib.w4a8_gemm_tm(f, f, 1 << 20, 4096, f, 128, 128, f, None) == EINVAL  # M*K = 2^32 (tiled loop)
+    assert lib.w4a8_gemm_tm(f, f, 64, 8192, f, 1 << 20, 128, f, None) == EINVAL  # tile-major array >= 4 GiB
+    assert b"4 GiB" in lib.w4a8_last_error()
     assert lib.w4a8_gemm_tm(f, f, 4, 384, f, 128, 128, f, None) == EINVAL
     assert lib.w4a8_gemm_tm(f, f, 16, 9216, f, 128, 128, f, None) == EINVAL  # staged rows past the LDS
     assert lib.w4a8_gemm_tm(f, f, 4, 256, f, 120, 128, f, None) == EINVAL

@@ -5,7 +5,8 @@ defines, built here in plain numpy from the oracle's own codes, scales and zero
 points.  The GEMM over tile-major weights must match the oracle within the fp32
 bound (1e-5 * sum_g |a_scale * w_scale * isum_g| + 1e-6) and, since it runs the
 same arithmetic in the same order as the decode loop over the standard layout,
-give exactly the bytes w4a8_gemm gives.
+give exactly the bytes w4a8_gemm gives.  Above 16 rows it runs the 256x256 tiled loop and must
+give exactly the bytes of that loop over the standard layout (w4a8_gemm_path, path 5).
 """
 from __future__ import annotations
 
@@ -110,6 +111,61 @@ def test_gemm_tm_matches_oracle_and_standard_layout(orc, M, N, K):
     assert np.array_equal(out.view(np.uint32), std.view(np.uint32))
 
 
+# (M, N, K) above 16 rows: the 256x256 tiled loop over tile-major weights; ragged row and column
+# tiles (17, 257, 513 rows; 272, 528, 1040 columns), one window of two groups (K=256), an odd
+# number of windows (K=768)
+TM_TILED_SHAPES = [
+    (17, 272, 1024),
+    (64, 528, 768),
+    (257, 256, 256),
+    (260, 1040, 2048),
+    (513, 528, 512),
+]
+
+
+@pytest.mark.parametrize("M,N,K", TM_TILED_SHAPES)
+def test_gemm_tm_tiled_matches_oracle_and_path5(orc, M, N, K):
+    w4 = w4mod()
+    seed = 5 * M + N
+    W = synthetic.weights(seed, synthetic.TAG_W, 0, N, K)
+    W += synthetic.column_means(seed, N)[:, None] * 3
+    x = synthetic.activations(seed, M, K)
+    q, s, z = orc.quantize_weights(W)
+    qr, sr = orc.quantize_act(x)
+    ref, mag = orc.gemm(qr, sr, q, s, z)
+    packed, scale, zp = to_dev(orc.pack_nibbles(q)), to_dev(s.view(np.int16)), to_dev(z.view(np.int16))
+    tm = w4.weights_to_tm(packed, scale, zp)
+    qa, sc = w4.quantize_act(to_dev(x))
+    out = to_host(w4.gemm_tm(qa, sc, tm))
+    check_close(out, ref, mag, f"tile-major tiled M={M} N={N} K={K}")
+    std = to_host(w4.gemm(qa, sc, packed, scale, zp, path=5))
+    assert np.array_equal(out.view(np.uint32), std.view(np.uint32))
+
+
+def test_gemm_tm_prefill_full_size_sampled(orc):
+    """Prefill layer M=4096, K=N=8192 (per-column mean offsets) on tile-major weights, in the launch
+    configuration the benchmark times: sampled outputs against the oracle, every output byte against
+    the 256x256 loop over the standard layout."""
+    w4 = w4mod()
+    M, N, K = 4096, 8192, 8192
+    packed, scale, zp = device_layer(0, synthetic.TAG_W, 0, N, K, mode="offset")
+    tm = w4.weights_to_tm(packed, scale, zp)
+    rng = np.random.default_rng(17)
+    cols = np.unique(np.concatenate([[0, 15, 16, 255, 256, N - 1], rng.choice(N, 40, replace=False)]))
+    q, s, z = oracle_columns(orc, 0, synthetic.TAG_W, 0, K, cols, mode="offset")
+    x = synthetic.activations(0, M, K)
+    qr, sr = orc.quantize_act(x)
+    qa, sc = w4.quantize_act(to_dev(x))
+    out = to_host(w4.gemm_tm(qa, sc, tm))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, 150, replace=False)]))
+    ms, ns = np.meshgrid(rows, np.arange(len(cols)), indexing="ij")
+    ref, mag = orc.gemm_at(qr, sr, q, s, z, ms.ravel(), ns.ravel())
+    check_close(out[rows][:, cols].ravel(), ref, mag, "tile-major prefill")
+    del tm
+    std = to_host(w4.gemm(qa, sc, packed, scale, zp, path=5))
+    assert np.array_equal(out.view(np.uint32), std.view(np.uint32))
+
+
 def test_gemm_tm_zero_row_and_rejects():
     w4 = w4mod()
     M, N, K = 6, 64, 512
@@ -121,9 +177,15 @@ def test_gemm_tm_zero_row_and_rejects():
     qa, sc = w4.quantize_act(to_dev(x))
     out = to_host(w4.gemm_tm(qa, sc, tm))
     assert not out[2].any() and out[0].any()
-    big = torch.zeros((17, K), dtype=torch.int8, device=cuda())
+    x[3] = 0.0  # the same in the tiled loop (M > 16)
+    xt = np.concatenate([x, synthetic.activations(5, 14, K)])
+    xt[17] = 0.0
+    qa, sc = w4.quantize_act(to_dev(xt))
+    out = to_host(w4.gemm_tm(qa, sc, tm))
+    assert not out[17].any() and out[18].any()
+    odd = torch.zeros((20, 384), dtype=torch.int8, device=cuda())  # K % 256 != 0
     with pytest.raises(w4.W4A8Error) as e:
-        w4.gemm_tm(big, torch.zeros(17, device=cuda()), tm)
+        w4.gemm_tm(odd, torch.zeros(20, device=cuda()), tm)
     assert e.value.status == 1
 
 

@@ -345,7 +345,8 @@ def _tm_n(tm) -> int:
 
 
 def gemm_tm(qa, a_scale, tm, out=None, group: int = GROUP):
-    """out float32 [M][N] (M <= 16) from tile-major weights; the same bytes as gemm()."""
+    """out float32 [M][N] from tile-major weights: the same bytes as gemm() for M <= 16 (decode
+    loop) and as gemm(..., path=5) above (the 256x256 tiled loop)."""
     torch = _torch()
     M, K = qa.shape
     N = _tm_n(tm)

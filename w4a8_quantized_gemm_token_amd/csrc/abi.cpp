@@ -401,8 +401,8 @@ w4a8_status w4a8_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int6
                  "qa, tm and out must be 16-byte aligned");
     if (M == 0) return W4A8_OK;
     W4A8_REQUIRE(gemm_tm_supported(M, K, N), W4A8_EINVAL,
-                 "the tile-major GEMM takes 1 <= M <= 16, K %% 256 == 0, M*(K+16) <= 143360 and a tile-major "
-                 "array below 4 GiB (M=%lld K=%lld N=%lld)",
+                 "the tile-major GEMM takes K %% 256 == 0, a tile-major array below 4 GiB, and "
+                 "M*(K+16) <= 143360 for M <= 16 or M*K < 2^32 above (M=%lld K=%lld N=%lld)",
                  (long long)M, (long long)K, (long long)N);
     return hip_status(launch_gemm_tm(qa, a_scale, M, K, tm, N, out, stream), "gemm_tm launch");
 }

@@ -62,6 +62,12 @@ __device__ __forceinline__ uint32_t zp_add_const(uint16_t zp_bits) {
     return 0x80808080u - z * 0x01010101u;
 }
 
+// the same constant from the tile-major array's -zp byte (two's complement)
+__device__ __forceinline__ uint32_t zp_add_const_neg(uint32_t neg_zp_byte) {
+    const uint32_t z = (0u - neg_zp_byte) & 0xFFu;
+    return 0x80808080u - __builtin_amdgcn_perm(0u, z, 0u);  // z in every byte
+}
+
 // Bijective XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
 // contiguous range of tiles so that neighbouring tiles share that XCD's L2.
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles) {
@@ -1611,7 +1617,10 @@ constexpr int kT4Lds = 2 * kT4Stage;  // 131072 bytes
 // Step ks of a group: lane quarter qd = l >> 4 supplies codes 16 (4 ks + qd) + [0, 16) of its row
 // (A: row (l & 15) of the row block) and of its column (B: column (l & 15) of the column block);
 // accumulator register r of a chain holds row 4 qd + r, column l & 15.
-template <bool ISUMS, int EPI = kEpiOut>
+// TM: the weights are the tile-major array (wpk; wsc and wzp unused): the same codes with each
+// dword's nibbles already in code order (no byte permutes in the unpack), and each column's
+// scales and -zp bytes of a group pair in the tile's 8-byte word.
+template <bool ISUMS, int EPI = kEpiOut, bool TM = false>
 __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restrict__ qa,
                                            const float *__restrict__ a_scale, const int32_t *__restrict__ row_index,
                                            int64_t R, TileRows rows, int64_t K, const uint8_t *__restrict__ wpk,
@@ -1620,6 +1629,7 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
                                            int32_t *__restrict__ isums, int64_t M_isums, const T3Epi &ep = T3Epi{}) {
     static_assert(EPI == kEpiOut || EPI == kEpiSilu, "plain and SiLU epilogues");
     static_assert(EPI == kEpiOut || !ISUMS, "the debug form stores int32 sums only");
+    static_assert(!TM || (EPI == kEpiOut && !ISUMS), "tile-major weights: plain epilogue");
     constexpr int NT = kT4Threads, LA = 4;
     constexpr int NBL = ISUMS ? 3 : 7;  // weight loads per thread and group (codes 2, zp 1, scales 4)
     const int tid = threadIdx.x;
@@ -1668,26 +1678,43 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
     // this lane's four output columns' scales
     const int bcol = tid >> 1, bpart = tid & 1;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(wpk);
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(wzp);
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(ISUMS ? wzp : wsc);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(TM ? (const void *)wpk : (const void *)wzp);
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(TM ? (const void *)wpk : (const void *)(ISUMS ? wzp : wsc));
+    // TM: the first block of column c's 16-column tile, tile-major offsets below 2^32
+    auto tm_tile = [&](int64_t c) -> uint32_t { return (uint32_t)(c >> 4) * (uint32_t)(G / 2) * (uint32_t)kTmBlock; };
     uint32_t boff, zoff;
     {
         const int64_t gc = wrow(bcol) >= 0 ? wrow(bcol) : 0;
-        boff = (uint32_t)(gc * (K / 2)) + (uint32_t)(32 * bpart);
-        zoff = (uint32_t)(gc * 2);
+        if constexpr (TM) {
+            boff = tm_tile(gc) + 16u * (uint32_t)(gc & 15) + 512u * (uint32_t)bpart;
+            zoff = tm_tile(gc) + 2048u + 8u * (uint32_t)(gc & 15) + 4u;
+        } else {
+            boff = (uint32_t)(gc * (K / 2)) + (uint32_t)(32 * bpart);
+            zoff = (uint32_t)(gc * 2);
+        }
     }
     const int frow = lane & 15, qd = lane >> 4;
     uint32_t soff[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const int64_t wr = wrow(wn * 64 + 16 * cb + frow);
-        soff[cb] = (uint32_t)((wr >= 0 ? wr : 0) * 2);
+        const int64_t wc = wr >= 0 ? wr : 0;
+        soff[cb] = TM ? tm_tile(wc) + 2048u + 8u * (uint32_t)(wc & 15) : (uint32_t)(wc * 2);
     }
     struct Slot {
         v4u rb0, rb1;
         uint32_t rz, rs[4];
     };
     auto b_load = [&](Slot &x, int64_t g) {
+        if constexpr (TM) {  // window g / 2 of the tile, group g % 2 in it
+            const int gw = (int)((g >> 1) * kTmBlock), h = (int)(g & 1);
+            x.rb0 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff, gw + 1024 * h, 0);
+            x.rb1 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff + 256, gw + 1024 * h, 0);
+            x.rz = __builtin_amdgcn_raw_buffer_load_b8(rz, zoff, gw + h, 0);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) x.rs[cb] = __builtin_amdgcn_raw_buffer_load_b16(rsc, soff[cb], gw + 2 * h, 0);
+            return;
+        }
         const int gs = (int)(g * N * 2);
         x.rb0 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff, (int)(g * (G128 / 2)), 0);
         x.rb1 = __builtin_amdgcn_raw_buffer_load_b128(rb, boff + 16, (int)(g * (G128 / 2)), 0);
@@ -1706,8 +1733,15 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
         const uint32_t d0 = q == 0 ? x.rb0.x : (q == 1 ? x.rb0.z : (q == 2 ? x.rb1.x : x.rb1.z));
         const uint32_t d1 = q == 0 ? x.rb0.y : (q == 1 ? x.rb0.w : (q == 2 ? x.rb1.y : x.rb1.w));
         uint32_t w0, w1, w2, w3;
-        unpack8(d0, zadd, w0, w1);
-        unpack8(d1, zadd, w2, w3);
+        if constexpr (TM) {  // nibbles already in code order: codes 0-3 low, 4-7 high
+            w0 = ((d0 & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u;
+            w1 = (((d0 >> 4) & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u;
+            w2 = ((d1 & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u;
+            w3 = (((d1 >> 4) & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u;
+        } else {
+            unpack8(d0, zadd, w0, w1);
+            unpack8(d1, zadd, w2, w3);
+        }
         *reinterpret_cast<v4u *>(B + t3_sw(bcol, 4 * bpart + q)) = v4u{w0, w1, w2, w3};
     };
 
@@ -1790,7 +1824,7 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
             const bool piece = c >= 16 && (c & 3) == 0;
             if (piece) {
                 const int q = (c - 16) >> 2;
-                if (q == 0) zadd = zp_add_const((uint16_t)sl.rz);
+                if (q == 0) zadd = TM ? zp_add_const_neg(sl.rz) : zp_add_const((uint16_t)sl.rz);
                 b_part(sl, st ^ 1, q, zadd);
                 if (q == 3) {
 #pragma unroll
@@ -1829,7 +1863,7 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
     b_load(sl, 0);
     __builtin_amdgcn_s_waitcnt(t3_waitcnt(0, 15));
     {
-        const uint32_t z0 = zp_add_const((uint16_t)sl.rz);
+        const uint32_t z0 = TM ? zp_add_const_neg(sl.rz) : zp_add_const((uint16_t)sl.rz);
 #pragma unroll
         for (int q = 0; q < 4; ++q) b_part(sl, 0, q, z0);
     }
@@ -1909,7 +1943,7 @@ __device__ __forceinline__ void tile4_unit(uint8_t *lds, const int8_t *__restric
     }
 }
 
-template <bool ISUMS, int EPI = kEpiOut>
+template <bool ISUMS, int EPI = kEpiOut, bool TM = false>
 __global__ __launch_bounds__(kT4Threads) void gemm_tiled4_kernel(const int8_t *__restrict__ qa,
                                                                  const float *__restrict__ a_scale, int64_t M,
                                                                  int64_t K, const uint8_t *__restrict__ packed,
@@ -1923,8 +1957,8 @@ __global__ __launch_bounds__(kT4Threads) void gemm_tiled4_kernel(const int8_t *_
     panel_tile<4>(xcd_tile(blockIdx.x, mt * nt), mt, nt, tm, tn);
     const int64_t m0 = tm * kT4BM;
     const int rows = (int)((M - m0) < kT4BM ? (M - m0) : kT4BM);
-    tile4_unit<ISUMS, EPI>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT4BN, out,
-                           N, isums, M);
+    tile4_unit<ISUMS, EPI, TM>(dsm, qa, a_scale, nullptr, M, TileRows{m0, rows}, K, packed, scale, zp, N, tn * kT4BN,
+                               out, N, isums, M);
 }
 
 template <int WM, int WN, bool ISUMS, int GS>
@@ -2800,14 +2834,24 @@ hipError_t launch_gemm_tiled_group(const int8_t *qa, const float *a_scale, int64
 
 int64_t tm_bytes(int64_t N, int64_t K) { return (N / 16) * (K / G128 / 2) * kTmBlock; }
 
+// M <= 16: the decode loop (rows staged in LDS); above: the 256x256 tiled loop (activation
+// offsets below 2^32).  Either way the tile-major array must stay below 4 GiB.
 bool gemm_tm_supported(int64_t M, int64_t K, int64_t N) {
-    return M >= 1 && M <= 16 && K % (2 * G128) == 0 && N % 16 == 0 && dec_lds_bytes(M, K) <= kDecLdsMax &&
-           tm_bytes(N, K) < kDecCodesMax;
+    if (M < 1 || K % (2 * G128) != 0 || N % 16 != 0 || tm_bytes(N, K) >= kDecCodesMax) return false;
+    return M <= 16 ? dec_lds_bytes(M, K) <= kDecLdsMax : M * K < (1ll << 32);
 }
 
 hipError_t launch_gemm_tm(const int8_t *qa, const float *a_scale, int64_t M, int64_t K, const uint8_t *tm, int64_t N,
                           float *out, hipStream_t stream) {
-    return launch_decode(qa, a_scale, M, K, tm, nullptr, nullptr, N, out, nullptr, true, stream);
+    if (M <= 16) return launch_decode(qa, a_scale, M, K, tm, nullptr, nullptr, N, out, nullptr, true, stream);
+    const int64_t tiles = ((M + kT4BM - 1) / kT4BM) * ((N + kT4BN - 1) / kT4BN);
+    if (hipFuncSetAttribute((const void *)gemm_tiled4_kernel<false, kEpiOut, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kT4Lds) != hipSuccess)
+        return hipGetLastError();
+    hipLaunchKernelGGL((gemm_tiled4_kernel<false, kEpiOut, true>), dim3((uint32_t)tiles), dim3(kT4Threads), kT4Lds,
+                       stream, qa, a_scale, M, K, tm, (const uint16_t *)nullptr, (const uint16_t *)nullptr, N, out,
+                       (int32_t *)nullptr);
+    return hipGetLastError();
 }
 
 // Standard layout -> tile-major: thread i of workgroup b (b = t * G/2 + w) writes the
