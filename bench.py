@@ -683,6 +683,10 @@ def main():
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               "(sharding the layer over several GPUs is designed but not implemented)", file=sys.stderr)
         sys.exit(2)
+    if args.tile_major and (args.only != "prefill" or args.group != GROUP or args.path):
+        print("bench.py: --tile-major goes with --only prefill at group 128 and takes no --path",
+              file=sys.stderr)
+        sys.exit(2)
     import torch
 
     import synthetic
@@ -691,9 +695,6 @@ def main():
     w4.load()
     if args.only:
         if args.only == "prefill":
-            if args.tile_major and args.group != GROUP:
-                print("bench.py: --tile-major takes group 128", file=sys.stderr)
-                return 2
             key = "prefill_M4096_K8192_N8192_" + ("tile_major" if args.tile_major else f"group{args.group}")
             res = {key: prefill(torch, w4, synthetic, args.reps, args.group, tuple(args.path or (0,)),
                                 tile_major=args.tile_major)}

@@ -94,3 +94,12 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("extra", [["--group", "64"], ["--path", "5"], []])
+def test_tile_major_option_is_checked_before_any_gpu_work(extra):
+    only = ["--only", "toy_moe"] if not extra else ["--only", "prefill"]
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), *only, "--tile-major", *extra],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--tile-major" in r.stderr
